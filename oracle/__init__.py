@@ -1,0 +1,46 @@
+"""CPU oracle for the DFlash 2 draft-path selector.  TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct numpy (fp64) statement of what the selector
+computes, used to check the HIP library.  Only the tests, the smoke check and
+the benchmark's CPU-baseline leg may import it; the product path never does,
+and this package shares no code with the HIP library.
+
+Source: the blog post "DFlash 2: Keep Drafting Parallel" (Inco AI, 2026) and
+its translations; see each function for the passage it follows.
+
+Pinning status (what each function is checked against, in tests/):
+  top16          full stable sort == heapq.nlargest; sorted rows; ties; -inf; +-0
+  gate           W_h = 0 -> 0.5; one-hot h; scipy.special.expit(h @ W); odd symmetry
+  pair_scores    scalar triple loop with math.fsum; zero bilinear -> U; closed forms
+  walk (greedy)  zero bilinear -> per-position top-1; planted chain; lexicographic
+                 brute force over all 16^L paths for L <= 4
+  walk (gumbel)  Gumbel-max frequencies vs softmax (chi-square); T -> 0 == greedy
+  philox4x32_10  rocRAND's header-only Philox4x32-10 compiled for the host
+"""
+from .philox import gumbel, philox4x32_10, uniform_from_word
+from .selector import (
+    SequenceResult,
+    gate,
+    pair_scores,
+    select,
+    select_sequence,
+    top16,
+    top16_rows,
+    walk,
+    widen,
+)
+
+__all__ = [
+    "SequenceResult",
+    "gate",
+    "gumbel",
+    "pair_scores",
+    "philox4x32_10",
+    "select",
+    "select_sequence",
+    "top16",
+    "top16_rows",
+    "uniform_from_word",
+    "walk",
+    "widen",
+]

@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks one oracle function against a textbook or library routine, a
+closed form, an invariant the pages fix, or brute force on tiny inputs, chosen
+so that a plausible slip (dropped term, wrong sign or index, transposed
+operand, swapped embedding roles) fails at least one of them.
+"""
+import heapq
+import itertools
+import math
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+from oracle import philox as ophilox
+
+RNG = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- top-16
+
+
+def _nlargest_ref(v, k=16):
+    """Independent top-k: heapq over (value, -id), -0 folded into +0."""
+    vals = [float(x) + 0.0 for x in v]
+    best = heapq.nlargest(k, range(len(vals)), key=lambda i: (vals[i], -i))
+    return np.array(best), np.array([vals[i] for i in best])
+
+
+def _rows():
+    yield RNG.standard_normal(1000)
+    yield RNG.standard_normal(16)
+    yield RNG.standard_normal(17)
+    yield RNG.standard_normal(32001) * 3.0
+    yield RNG.integers(-3, 3, size=500).astype(np.float64)  # heavy ties
+    yield np.zeros(64)  # all tied
+    z = RNG.choice([0.0, -0.0, 1.0, -1.0], size=300)
+    yield z  # +-0 mixed with ties
+    r = np.full(200, -np.inf)
+    r[[5, 77, 150]] = [1.0, -2.0, 1.0]
+    yield r  # fewer than 16 finite values
+    yield np.arange(300, dtype=np.float64)  # ascending
+    yield np.arange(300, dtype=np.float64)[::-1].copy()  # descending
+    yield np.concatenate([np.full(40, 7.0), RNG.standard_normal(100)])
+
+
+@pytest.mark.parametrize("row", list(_rows()), ids=lambda r: f"V{len(r)}")
+def test_top16_matches_heapq(row):
+    ids, vals = oracle.top16(row)
+    rids, rvals = _nlargest_ref(row)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_array_equal(vals, rvals)
+
+
+def test_top16_known_answers():
+    ids, vals = oracle.top16(np.arange(100, dtype=np.float64))
+    np.testing.assert_array_equal(ids, np.arange(99, 83, -1))
+    ids, _ = oracle.top16(np.zeros(50))
+    np.testing.assert_array_equal(ids, np.arange(16))  # ties -> lowest ids
+    row = np.zeros(40)
+    row[3] = -0.0
+    row[30] = 0.0
+    ids, vals = oracle.top16(row)
+    assert 3 in ids and not np.signbit(vals).any()  # -0 == +0, reported as +0
+
+
+def test_top16_rejects_nan_and_short_rows():
+    with pytest.raises(ValueError):
+        oracle.top16(np.array([1.0, np.nan] + [0.0] * 20))
+    with pytest.raises(ValueError):
+        oracle.top16(np.zeros(15))
+
+
+def test_top16_bf16_rows_match_heapq():
+    bits = RNG.integers(0, 2**16, size=4000).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # drop inf/nan patterns
+    v = oracle.widen(bits, "bf16")
+    ids, vals = oracle.top16(v)
+    rids, rvals = _nlargest_ref(v)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_array_equal(vals, rvals)
+
+
+def test_widen_bf16_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x4049, 0x0001], np.uint16)
+    want = [1.0, -1.0, 0.0, -0.0, np.inf, -np.inf, 3.140625, 2.0 ** -133]
+    np.testing.assert_array_equal(oracle.widen(bits, "bf16"), want)
+
+
+# ---------------------------------------------------------------- gate
+
+
+def test_gate_zero_weight_is_half():
+    h = RNG.standard_normal((5, 64))
+    np.testing.assert_array_equal(oracle.gate(h, np.zeros((64, 256))), 0.5)
+
+
+def test_gate_one_hot_selects_weight_row():
+    W = RNG.standard_normal((32, 256))
+    h = np.zeros(32)
+    h[7] = 1.0
+    np.testing.assert_allclose(oracle.gate(h, W), scipy.special.expit(W[7]), rtol=1e-15)
+
+
+def test_gate_matches_scipy_expit():
+    h = RNG.standard_normal((9, 300))
+    W = RNG.standard_normal((300, 256)) * 0.05
+    z = np.einsum("nd,de->ne", h, W)
+    np.testing.assert_allclose(oracle.gate(h, W), scipy.special.expit(z), rtol=1e-13, atol=1e-15)
+
+
+def test_gate_symmetry_and_saturation():
+    h = RNG.standard_normal((3, 40))
+    W = RNG.standard_normal((40, 256))
+    np.testing.assert_allclose(oracle.gate(-h, W), 1.0 - oracle.gate(h, W), atol=1e-15)
+    g = oracle.gate(h * 1e4, W)
+    assert np.isfinite(g).all() and g.min() >= 0.0 and g.max() <= 1.0
+
+
+# ---------------------------------------------------------------- pair scores
+
+
+def _tables(V, scale=0.3):
+    A = RNG.standard_normal((V, 256)) * scale
+    Bt = RNG.standard_normal((V, 256)) * scale
+    return A, Bt
+
+
+def _cands(V, L):
+    return np.stack([RNG.choice(V, 16, replace=False) for _ in range(L)])
+
+
+def test_pair_scores_match_scalar_brute_force():
+    V, L = 200, 3
+    A, Bt = _tables(V)
+    cidx = _cands(V, L)
+    cval = RNG.standard_normal((L, 16))
+    g = RNG.random((L, 256))
+    prev = 17
+    S = oracle.pair_scores(cidx, cval, prev, g, lambda ids: A[ids], lambda ids: Bt[ids])
+    for t in range(L):
+        for i in range(16):
+            a = prev if t == 0 else cidx[t - 1][i]
+            for j in range(16):
+                b = cidx[t][j]
+                want = cval[t][j] + math.fsum(A[a][e] * g[t][e] * Bt[b][e] for e in range(256))
+                assert abs(S[t, i, j] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_pair_scores_zero_bilinear_is_logit():
+    V, L = 100, 4
+    cidx = _cands(V, L)
+    cval = RNG.standard_normal((L, 16))
+    g = RNG.random((L, 256))
+    S = oracle.pair_scores(cidx, cval, 3, g, lambda ids: np.zeros((len(ids), 256)),
+                           lambda ids: RNG.standard_normal((len(ids), 256)))
+    np.testing.assert_array_equal(S, np.broadcast_to(cval[:, None, :], S.shape))
+
+
+def test_pair_scores_closed_form_constant_rows():
+    # A rows = alpha, B rows = beta, gate = c  ->  bilinear = 256 * alpha * beta * c
+    V, L = 50, 2
+    cidx = _cands(V, L)
+    cval = np.zeros((L, 16))
+    alpha, beta, c = 0.5, -0.25, 0.75
+    S = oracle.pair_scores(cidx, cval, 1, np.full((L, 256), c), lambda ids: np.full((len(ids), 256), alpha),
+                           lambda ids: np.full((len(ids), 256), beta))
+    np.testing.assert_allclose(S, 256 * alpha * beta * c, rtol=1e-15)
+
+
+def test_pair_scores_roles_and_positions():
+    # A is non-zero only for token 5 and B only for token 9: the score of the pair
+    # (5 -> 9) carries the bilinear term, (9 -> 5) does not.  The gate picks one
+    # embedding coordinate per position (coordinate t at position t).
+    V, L = 30, 3
+    A = np.zeros((V, 256))
+    Bt = np.zeros((V, 256))
+    A[5] = np.arange(256) + 1.0
+    Bt[9] = 2.0 * (np.arange(256) + 1.0)
+    g = np.zeros((L, 256))
+    for t in range(L):
+        g[t, t] = 1.0
+    cidx = np.array([[9] + list(range(10, 25)), [5] + list(range(10, 25)), [9] + list(range(10, 25))])
+    cval = np.zeros((L, 16))
+    S = oracle.pair_scores(cidx, cval, 5, g, lambda ids: A[ids], lambda ids: Bt[ids])
+    # t=0: predecessor is the verified token 5, candidate slot 0 is token 9
+    assert S[0, 0, 0] == 1.0 * 2.0  # coordinate 0: A[5,0]=1, B[9,0]=2
+    assert (S[0, :, 0] == 2.0).all()  # repeated over predecessor slots
+    # t=1: predecessor slot 0 is token 9 (A[9]=0), candidate slot 0 is token 5 (B[5]=0)
+    assert S[1, 0, 0] == 0.0
+    # t=2: predecessor slot 0 is token 5, candidate slot 0 is token 9, gate coordinate 2
+    assert S[2, 0, 0] == 3.0 * 6.0
+    assert np.count_nonzero(S) == 16 + 1
+
+
+# ---------------------------------------------------------------- walk
+
+
+def test_walk_zero_bilinear_is_per_position_top1():
+    # With the bilinear term off, the selector reduces to plain DFlash, which keeps
+    # each position's own top pick (wpnews.pro, "The Right Tokens Are Already There").
+    V, L = 300, 6
+    logits = RNG.standard_normal((L, V))
+    cidx, cval = oracle.top16_rows(logits)
+    g = RNG.random((L, 256))
+    S = oracle.pair_scores(cidx, cval, 0, g, lambda ids: np.zeros((len(ids), 256)),
+                           lambda ids: np.ones((len(ids), 256)))
+    path, scores, slots, _ = oracle.walk(S, cidx)
+    np.testing.assert_array_equal(path, logits.argmax(axis=1))
+    np.testing.assert_array_equal(scores, logits.max(axis=1))
+    np.testing.assert_array_equal(slots, 0)
+
+
+def test_walk_follows_planted_chain():
+    # Token x_t -> x_{t+1} pairs get a bilinear bonus of 100 while U prefers other
+    # tokens; the greedy walk from x_0 must take the chain.
+    V, L = 64, 5
+    chain = [40, 41, 42, 43, 44, 45]  # chain[0] is the last verified token
+    A = np.zeros((V, 256))
+    Bt = np.zeros((V, 256))
+    for t in range(L):
+        A[chain[t], t] = 10.0
+        Bt[chain[t + 1], t] = 10.0
+    g = np.ones((L, 256))
+    cidx = np.stack([np.r_[np.arange(15), chain[t + 1]] for t in range(L)])  # chain token in slot 15
+    cval = np.tile(np.linspace(5.0, 1.0, 16), (L, 1))  # U prefers slot 0
+    S = oracle.pair_scores(cidx, cval, chain[0], g, lambda ids: A[ids], lambda ids: Bt[ids])
+    path, scores, slots, _ = oracle.walk(S, cidx)
+    np.testing.assert_array_equal(path, chain[1:])
+    np.testing.assert_array_equal(slots, 15)
+    np.testing.assert_allclose(scores, 1.0 + 100.0)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_greedy_walk_is_lexicographic_max_over_all_paths(L):
+    # Stepwise greedy with lowest-slot ties is the lexicographic maximum of
+    # (s_0, -j_0, s_1, -j_1, ...) over all 16^L slot paths.
+    S = np.round(RNG.standard_normal((L, 16, 16)) * 2.0, 1)  # coarse values -> ties happen
+    S[0] = S[0, 0][None, :]
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    _, _, slots, _ = oracle.walk(S, cidx)
+    best, best_key = None, None
+    for js in itertools.product(range(16), repeat=L):
+        key, prev = [], 0
+        for t, j in enumerate(js):
+            key += [S[t, prev, j], -j]
+            prev = j
+        if best_key is None or key > best_key:
+            best, best_key = js, key
+    np.testing.assert_array_equal(slots, best)
+
+
+def test_gumbel_walk_tiny_temperature_is_greedy():
+    L = 8
+    S = RNG.permutation(L * 256).reshape(L, 16, 16) * 1e-3  # distinct, margins >= 1e-3
+    S[0] = S[0, 0][None, :]
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    g_path, *_ = oracle.walk(S, cidx)
+    for seed in (1, 99, 2**40 + 3):
+        s_path, s_scores, _, _ = oracle.walk(S, cidx, "gumbel", 1e-8, seed, b=3)
+        np.testing.assert_array_equal(s_path, g_path)
+
+
+@pytest.mark.parametrize("T", [1.0, 2.5])
+def test_gumbel_max_frequencies_match_softmax(T):
+    row = np.linspace(-1.0, 1.5, 16)
+    S = np.broadcast_to(row, (1, 16, 16)).copy()
+    cidx = np.arange(16)[None, :]
+    n = 3000
+    counts = np.zeros(16)
+    for s in range(n):
+        _, _, slots, _ = oracle.walk(S, cidx, "gumbel", T, seed=s * 7919 + 1, b=s % 5)
+        counts[slots[0]] += 1
+    p = scipy.special.softmax(row / T)
+    chi2 = ((counts - n * p) ** 2 / (n * p)).sum()
+    assert scipy.stats.chi2.sf(chi2, df=15) > 1e-4
+
+
+def test_walk_rejects_bad_arguments():
+    S = np.zeros((1, 16, 16))
+    with pytest.raises(ValueError):
+        oracle.walk(S, np.arange(16)[None], "gumbel", 0.0)
+    with pytest.raises(ValueError):
+        oracle.walk(S, np.arange(16)[None], "beam")
+
+
+# ---------------------------------------------------------------- Philox / Gumbel noise
+
+_HELPER_SRC = os.path.join(os.path.dirname(__file__), "pins", "rocrand_philox.cpp")
+
+
+@pytest.fixture(scope="module")
+def rocrand_philox():
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available to build the rocRAND pin")
+    d = tempfile.mkdtemp(prefix="dfs_pin_")
+    exe = os.path.join(d, "rocrand_philox")
+    subprocess.run([hipcc, "-O1", _HELPER_SRC, "-o", exe], check=True, capture_output=True)
+    return exe
+
+
+def test_philox_matches_rocrand(rocrand_philox):
+    # the helper addresses the counter through a 64-bit offset of 4 * (j + t * 2^32): t < 2^30
+    cases = [(0, 0, 0, 0), (2**64 - 1, 2**32 - 1, 2**30 - 1, 2**32 - 1), (0x5EED, 63, 15, 15)]
+    cases += [tuple(int(x) for x in (RNG.integers(0, 2**63), RNG.integers(0, 4096), RNG.integers(0, 64),
+                                     RNG.integers(0, 16))) for _ in range(300)]
+    text = "".join(f"{s} {b} {t} {j}\n" for s, b, t, j in cases)
+    out = subprocess.run([rocrand_philox], input=text, capture_output=True, text=True, check=True).stdout
+    for (s, b, t, j), line in zip(cases, out.strip().splitlines()):
+        want = tuple(int(w) for w in line.split())
+        got = oracle.philox4x32_10((j, t, b, 0), (s & 0xFFFFFFFF, s >> 32))
+        assert got == want, (s, b, t, j)
+
+
+def test_uniform_map_is_open_interval_and_fp32_exact():
+    for x in (0, 1, 511, 512, 2**31, 2**32 - 1):
+        u = oracle.uniform_from_word(x)
+        assert 0.0 < u < 1.0
+        assert float(np.float32(u)) == u
+    assert oracle.uniform_from_word(0) == 2.0 ** -24
+    assert oracle.uniform_from_word(2**32 - 1) == 1.0 - 2.0 ** -24
+
+
+def test_gumbel_noise_moments():
+    g = np.array([oracle.gumbel(77, b, t, j) for b in range(40) for t in range(16) for j in range(16)])
+    n = g.size
+    assert abs(g.mean() - np.euler_gamma) < 5 * math.pi / math.sqrt(6 * n)
+    assert abs(g.var() - math.pi**2 / 6) < 0.1
+    # distinct (b, t, j) give distinct draws; the same triple repeats
+    assert len(set(g.tolist())) > 0.99 * n
+    assert ophilox.gumbel(77, 3, 4, 5) == ophilox.gumbel(77, 3, 4, 5)
+
+
+# ---------------------------------------------------------------- whole selector
+
+
+def test_select_sequence_end_to_end_small():
+    from workloads import make, variant
+
+    cfg = variant("tiny", V=500, d=64, L=4, batch=2, emb_std=0.5)
+    inp = make(cfg)
+    res = oracle.select(inp)
+    for i, r in enumerate(res):
+        logits = oracle.widen(inp.logits[i], "f32")
+        ids, vals = _nlargest_ref(logits[0])
+        np.testing.assert_array_equal(r.cand_idx[0], ids)
+        # the path's step scores are the pair-tensor entries along the path
+        prev = 0
+        for t in range(cfg.L):
+            assert r.scores[t] == r.pair[t, prev, r.slots[t]]
+            assert r.path[t] == r.cand_idx[t, r.slots[t]]
+            prev = r.slots[t]
