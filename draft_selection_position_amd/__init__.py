@@ -1,0 +1,311 @@
+"""DFlash 2 draft-path selector for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libdfs.so`` (C ABI declared in ``include/dfs.h``).  It
+only checks and marshals arguments: every step of the selector runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current stream.
+The library is required; there is no other code path.
+
+    import draft_selection_position_amd as dfs
+    path, scores = dfs.select(logits, hidden, prev_token, A, B, W_h)
+
+The selector (blog post "DFlash 2: Keep Drafting Parallel", section "A
+Lightweight Path Selector"): keep the 16 best candidates per block position,
+score every adjacent pair with S_t(a,b) = U_t(b) + <A(a) * sigmoid(h_t W_h), B(b)>,
+then walk the scores once from the last verified token.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "DfsError", "K", "E", "MAX_L", "lib", "lib_path", "topk", "gate", "pair_scores", "walk",
+    "select", "Selector", "select_workspace_bytes", "topk_workspace_bytes",
+    "gate_workspace_bytes", "status_str",
+]
+
+K = 16
+E = 256
+MAX_L = 16
+F32, BF16 = 0, 1
+GREEDY, GUMBEL = 0, 1
+_MODES = {"greedy": GREEDY, "gumbel": GUMBEL, "sampled": GUMBEL}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_lock = threading.Lock()
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libdfs.so")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("L", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("logits_dtype", ctypes.c_int), ("act_dtype", ctypes.c_int),
+                ("table_dtype", ctypes.c_int)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdfs.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m draft_selection_position_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i64, sz, i32p, f32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+        c_int, c_double, u64 = ctypes.c_int, ctypes.c_double, ctypes.c_uint64
+        L.dfs_status_str.argtypes, L.dfs_status_str.restype = [c_int], ctypes.c_char_p
+        L.dfs_abi_version.argtypes, L.dfs_abi_version.restype = [], c_int
+        L.dfs_topk_workspace_bytes.argtypes, L.dfs_topk_workspace_bytes.restype = [i64, i64, c_int], sz
+        L.dfs_topk.argtypes = [vp, c_int, i64, i64, c_int, i32p, f32p, vp, sz, vp]
+        L.dfs_topk.restype = c_int
+        L.dfs_gate_workspace_bytes.argtypes, L.dfs_gate_workspace_bytes.restype = [i64, i64, c_int], sz
+        L.dfs_gate.argtypes = [vp, vp, c_int, i64, i64, i64, f32p, vp, sz, vp]
+        L.dfs_gate.restype = c_int
+        L.dfs_pair_scores.argtypes = [i32p, f32p, i32p, f32p, vp, vp, c_int, i64, i64, i64, i64, c_int,
+                                      f32p, vp]
+        L.dfs_pair_scores.restype = c_int
+        L.dfs_walk.argtypes = [f32p, i32p, i64, i64, c_int, c_int, c_double, u64, i32p, f32p, vp]
+        L.dfs_walk.restype = c_int
+        L.dfs_select_workspace_bytes.argtypes = [ctypes.POINTER(_Shape)]
+        L.dfs_select_workspace_bytes.restype = sz
+        L.dfs_select.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int, c_double,
+                                 u64, vp, sz, i32p, f32p, vp]
+        L.dfs_select.restype = c_int
+        _lib = L
+    return _lib
+
+
+class DfsError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_str(code)}")
+
+
+def status_str(code: int) -> str:
+    return lib().dfs_status_str(int(code)).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise DfsError(rc, where)
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"{what} must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, what: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class _Workspace:
+    """A per-device cached byte buffer (grown on demand, never shrunk)."""
+
+    def __init__(self):
+        self._bufs: dict[torch.device, torch.Tensor] = {}
+
+    def get(self, device: torch.device, nbytes: int) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        buf = self._bufs.get(device)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self._bufs[device] = buf
+        return buf
+
+
+_WS = _Workspace()
+
+
+def _ws_arg(ws, device, nbytes):
+    if ws is None:
+        ws = _WS.get(device, nbytes)
+    elif nbytes and (ws.device != device or ws.numel() * ws.element_size() < nbytes):
+        raise ValueError(f"workspace must hold {nbytes} bytes on {device}")
+    return ws
+
+
+# ---------------------------------------------------------------- step entry points
+
+
+def topk_workspace_bytes(rows: int, V: int, dtype: torch.dtype) -> int:
+    return int(lib().dfs_topk_workspace_bytes(rows, V, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def topk(logits: torch.Tensor, k: int = K, workspace: torch.Tensor | None = None):
+    """Top-16 of each row of ``logits`` [..., V]: (ids int32 [..., 16], values fp32 [..., 16]).
+
+    Order: value descending, then id ascending.
+    """
+    _dev(logits, "logits")
+    dt = _dtype_code(logits, "logits")
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    lead = tuple(logits.shape[:-1])
+    idx = torch.empty(lead + (K,), dtype=torch.int32, device=logits.device)
+    val = torch.empty(lead + (K,), dtype=torch.float32, device=logits.device)
+    nb = int(lib().dfs_topk_workspace_bytes(rows, V, dt))
+    ws = _ws_arg(workspace, logits.device, nb)
+    _check(lib().dfs_topk(logits.data_ptr(), dt, rows, V, k, idx.data_ptr(), val.data_ptr(), _ptr(ws), nb,
+                          _stream(logits.device)), "dfs_topk")
+    return idx, val
+
+
+def gate_workspace_bytes(rows: int, d: int, dtype: torch.dtype) -> int:
+    return int(lib().dfs_gate_workspace_bytes(rows, d, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def gate(hidden: torch.Tensor, W_h: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """sigmoid(hidden @ W_h) in fp32: hidden [..., d], W_h [d, 256] (same dtype) -> [..., 256]."""
+    _dev(hidden, "hidden")
+    _dev(W_h, "W_h", hidden.dtype)
+    dt = _dtype_code(hidden, "hidden")
+    d = hidden.shape[-1]
+    if W_h.dim() != 2 or W_h.shape[0] != d:
+        raise ValueError(f"W_h must be [{d}, 256], got {tuple(W_h.shape)}")
+    rows = hidden.numel() // d if d else 0
+    out = torch.empty(tuple(hidden.shape[:-1]) + (E,), dtype=torch.float32, device=hidden.device)
+    nb = int(lib().dfs_gate_workspace_bytes(rows, d, dt))
+    ws = _ws_arg(workspace, hidden.device, nb)
+    _check(lib().dfs_gate(hidden.data_ptr(), W_h.data_ptr(), dt, rows, d, W_h.shape[1], out.data_ptr(),
+                          _ptr(ws), nb, _stream(hidden.device)), "dfs_gate")
+    return out
+
+
+def pair_scores(cand_idx: torch.Tensor, cand_val: torch.Tensor, prev_token: torch.Tensor,
+                gate_: torch.Tensor, A: torch.Tensor, B: torch.Tensor) -> torch.Tensor:
+    """S[b, t, i, j] for all adjacent candidate pairs: fp32 [batch, L, 16, 16]."""
+    _dev(cand_idx, "cand_idx", torch.int32)
+    _dev(cand_val, "cand_val", torch.float32)
+    _dev(prev_token, "prev_token", torch.int32)
+    _dev(gate_, "gate", torch.float32)
+    _dev(A, "A")
+    _dev(B, "B", A.dtype)
+    if cand_idx.dim() != 3 or cand_idx.shape[-1] != K or cand_val.shape != cand_idx.shape:
+        raise ValueError("cand_idx and cand_val must both be [batch, L, 16]")
+    batch, L = cand_idx.shape[0], cand_idx.shape[1]
+    if prev_token.shape != (batch,) or gate_.numel() != batch * L * E:
+        raise ValueError("prev_token must be [batch] and gate [batch*L, 256]")
+    if A.dim() != 2 or A.shape != B.shape:
+        raise ValueError("A and B must both be [V, 256]")
+    out = torch.empty((batch, L, K, K), dtype=torch.float32, device=cand_idx.device)
+    _check(lib().dfs_pair_scores(cand_idx.data_ptr(), cand_val.data_ptr(), prev_token.data_ptr(),
+                                 gate_.data_ptr(), A.data_ptr(), B.data_ptr(), _dtype_code(A, "A"), batch, L,
+                                 A.shape[0], A.shape[1], K, out.data_ptr(), _stream(A.device)),
+           "dfs_pair_scores")
+    return out
+
+
+def walk(pair: torch.Tensor, cand_idx: torch.Tensor, mode: str = "greedy", temperature: float = 1.0,
+         seed: int = 0):
+    """One walk per sequence over pair [batch, L, 16, 16]: (path int32 [batch, L], scores fp32)."""
+    _dev(pair, "pair", torch.float32)
+    _dev(cand_idx, "cand_idx", torch.int32)
+    if pair.dim() != 4 or pair.shape[2:] != (K, K) or cand_idx.shape != pair.shape[:3]:
+        raise ValueError("pair must be [batch, L, 16, 16] and cand_idx [batch, L, 16]")
+    batch, L = pair.shape[0], pair.shape[1]
+    path = torch.empty((batch, L), dtype=torch.int32, device=pair.device)
+    scores = torch.empty((batch, L), dtype=torch.float32, device=pair.device)
+    _check(lib().dfs_walk(pair.data_ptr(), cand_idx.data_ptr(), batch, L, K, _MODES[mode], float(temperature),
+                          int(seed) & (2**64 - 1), path.data_ptr(), scores.data_ptr(), _stream(pair.device)),
+           "dfs_walk")
+    return path, scores
+
+
+# ---------------------------------------------------------------- fused selector
+
+
+def _shape(batch, L, V, d, logits_dt, act_dt, table_dt) -> _Shape:
+    return _Shape(batch, L, V, d, logits_dt, act_dt, table_dt)
+
+
+def select_workspace_bytes(batch: int, L: int, V: int, d: int, logits_dtype=torch.bfloat16,
+                           act_dtype=torch.bfloat16, table_dtype=torch.bfloat16) -> int:
+    c = lambda t: BF16 if t == torch.bfloat16 else F32  # noqa: E731
+    s = _shape(batch, L, V, d, c(logits_dtype), c(act_dtype), c(table_dtype))
+    return int(lib().dfs_select_workspace_bytes(ctypes.byref(s)))
+
+
+def select(logits: torch.Tensor, hidden: torch.Tensor, prev_token: torch.Tensor, A: torch.Tensor,
+           B: torch.Tensor, W_h: torch.Tensor, k: int = K, mode: str = "greedy", temperature: float = 1.0,
+           seed: int = 0, workspace: torch.Tensor | None = None, out=None):
+    """The whole selector on one draft block per sequence.
+
+    logits [batch, L, V]; hidden [batch, L, d]; prev_token [batch] int32 (last
+    verified token); A, B [V, 256]; W_h [d, 256].  Returns (path int32 [batch, L],
+    scores fp32 [batch, L]).  ``out`` may pass preallocated (path, scores).
+    """
+    _dev(logits, "logits")
+    _dev(hidden, "hidden")
+    _dev(prev_token, "prev_token", torch.int32)
+    _dev(A, "A")
+    _dev(B, "B", A.dtype)
+    _dev(W_h, "W_h", hidden.dtype)
+    if logits.dim() != 3 or hidden.dim() != 3 or hidden.shape[:2] != logits.shape[:2]:
+        raise ValueError("logits must be [batch, L, V] and hidden [batch, L, d]")
+    batch, L, V = logits.shape
+    d = hidden.shape[2]
+    if A.shape != (V, E) or B.shape != (V, E) or W_h.shape != (d, E) or prev_token.shape != (batch,):
+        raise ValueError("A, B must be [V, 256], W_h [d, 256] and prev_token [batch]")
+    s = _shape(batch, L, V, d, _dtype_code(logits, "logits"), _dtype_code(hidden, "hidden"),
+               _dtype_code(A, "A"))
+    nb = int(lib().dfs_select_workspace_bytes(ctypes.byref(s)))
+    ws = _ws_arg(workspace, logits.device, nb)
+    if out is None:
+        path = torch.empty((batch, L), dtype=torch.int32, device=logits.device)
+        scores = torch.empty((batch, L), dtype=torch.float32, device=logits.device)
+    else:
+        path, scores = out
+    _check(lib().dfs_select(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(),
+                            B.data_ptr(), W_h.data_ptr(), k, ctypes.byref(s), _MODES[mode], float(temperature),
+                            int(seed) & (2**64 - 1), _ptr(ws), nb, path.data_ptr(), scores.data_ptr(),
+                            _stream(logits.device)), "dfs_select")
+    return path, scores
+
+
+class Selector:
+    """Fixed-shape selector with its own workspace and output buffers (no per-call allocation)."""
+
+    def __init__(self, batch: int, L: int, V: int, d: int, device="cuda", logits_dtype=torch.bfloat16,
+                 act_dtype=torch.bfloat16, table_dtype=torch.bfloat16, mode: str = "greedy",
+                 temperature: float = 1.0, seed: int = 0):
+        self.device = torch.device(device)
+        self.mode, self.temperature, self.seed = mode, temperature, seed
+        nb = select_workspace_bytes(batch, L, V, d, logits_dtype, act_dtype, table_dtype)
+        self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.device)
+        self.path = torch.empty((batch, L), dtype=torch.int32, device=self.device)
+        self.scores = torch.empty((batch, L), dtype=torch.float32, device=self.device)
+
+    def __call__(self, logits, hidden, prev_token, A, B, W_h):
+        return select(logits, hidden, prev_token, A, B, W_h, K, self.mode, self.temperature, self.seed,
+                      self.workspace, (self.path, self.scores))

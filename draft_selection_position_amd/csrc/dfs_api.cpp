@@ -1,0 +1,248 @@
+// C ABI of the selector: argument checks, workspace layout and launch order.
+// Every check happens on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/dfs.h"
+#include "dfs_internal.h"
+
+using namespace dfs;
+
+namespace {
+
+constexpr int64_t kMaxV = 2147483647;  // token ids are int32
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+int esize(dfs_dtype_t t) { return t == DFS_BF16 ? 2 : 4; }
+bool valid_dtype(int t) { return t == DFS_F32 || t == DFS_BF16; }
+
+// gfx950 check, cached per device.  0 = unknown, 1 = ok, 2 = other arch.
+std::atomic<int> g_arch_state[64];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return DFS_E_HIP;
+  }
+  if (dev < 64) {
+    const int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return DFS_OK;
+    if (st == 2) return DFS_E_ARCH;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return DFS_E_HIP;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? DFS_OK : DFS_E_ARCH;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DFS_OK : DFS_E_HIP; }
+
+int check_topk_args(const void* logits, int dt, int64_t rows, int64_t V, int k,
+                    const int32_t* out_idx, const float* out_val) {
+  if (!logits || !out_idx || !out_val) return DFS_E_NULL;
+  if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
+  if (k != DFS_K) return DFS_E_UNSUPPORTED;
+  if (rows < 1 || V < DFS_K || V > kMaxV) return DFS_E_SHAPE;
+  if (!aligned(logits, esize((dfs_dtype_t)dt)) || !aligned(out_idx, 4) || !aligned(out_val, 4))
+    return DFS_E_ALIGN;
+  return DFS_OK;
+}
+
+int check_gate_args(const void* hidden, const void* W_h, int dt, int64_t rows, int64_t d,
+                    int64_t E, const float* out) {
+  if (!hidden || !W_h || !out) return DFS_E_NULL;
+  if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
+  if (E != DFS_E) return DFS_E_UNSUPPORTED;
+  if (rows < 1 || d < 1) return DFS_E_SHAPE;
+  if (d % 8 != 0) return DFS_E_UNSUPPORTED;
+  if (!aligned(hidden, 16) || !aligned(W_h, 16) || !aligned(out, 4)) return DFS_E_ALIGN;
+  return DFS_OK;
+}
+
+int check_walk_mode(int mode, double temperature) {
+  if (mode != DFS_WALK_GREEDY && mode != DFS_WALK_GUMBEL) return DFS_E_UNSUPPORTED;
+  if (mode == DFS_WALK_GUMBEL && !(std::isfinite(temperature) && temperature > 0.0))
+    return DFS_E_ARG;
+  return DFS_OK;
+}
+
+// Workspace layout of dfs_select.
+struct SelectLayout {
+  TopkPlan topk;
+  GatePlan gate;
+  size_t cand_idx_off, cand_val_off, gate_off, topk_ws_off, gate_ws_off, total;
+};
+
+SelectLayout select_layout(const dfs_shape_t& s) {
+  SelectLayout l{};
+  const int64_t rows = s.batch * s.L;
+  l.topk = plan_topk(rows, s.V, esize(s.logits_dtype));
+  l.gate = plan_gate(rows, s.d, s.act_dtype == DFS_BF16);
+  size_t off = 0;
+  l.cand_idx_off = off;
+  off += align_up((size_t)rows * DFS_K * sizeof(int32_t), 256);
+  l.cand_val_off = off;
+  off += align_up((size_t)rows * DFS_K * sizeof(float), 256);
+  l.gate_off = off;
+  off += align_up((size_t)rows * DFS_E * sizeof(float), 256);
+  l.topk_ws_off = off;
+  off += l.topk.ws_bytes;
+  l.gate_ws_off = off;
+  off += l.gate.ws_bytes;
+  l.total = off;
+  return l;
+}
+
+int check_shape(const dfs_shape_t* s) {
+  if (!s) return DFS_E_NULL;
+  if (!valid_dtype(s->logits_dtype) || !valid_dtype(s->act_dtype) || !valid_dtype(s->table_dtype))
+    return DFS_E_UNSUPPORTED;
+  if (s->batch < 1 || s->L < 1 || s->L > DFS_MAX_L || s->V < DFS_K || s->V > kMaxV || s->d < 1)
+    return DFS_E_SHAPE;
+  if (s->d % 8 != 0) return DFS_E_UNSUPPORTED;
+  if (s->batch > (int64_t)1 << 30) return DFS_E_SHAPE;
+  return DFS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dfs_abi_version(void) { return DFS_ABI_VERSION; }
+
+const char* dfs_status_str(int status) {
+  switch (status) {
+    case DFS_OK: return "DFS_OK: success";
+    case DFS_E_NULL: return "DFS_E_NULL: a required pointer is NULL";
+    case DFS_E_SHAPE: return "DFS_E_SHAPE: a size is out of range";
+    case DFS_E_UNSUPPORTED:
+      return "DFS_E_UNSUPPORTED: k must be 16, E 256, d a multiple of 8, dtype and walk mode known";
+    case DFS_E_WORKSPACE: return "DFS_E_WORKSPACE: workspace missing or too small";
+    case DFS_E_ALIGN: return "DFS_E_ALIGN: a pointer is not aligned as required";
+    case DFS_E_HIP: return "DFS_E_HIP: no usable HIP device, or a HIP launch failed";
+    case DFS_E_ARCH: return "DFS_E_ARCH: the current device is not gfx950";
+    case DFS_E_ARG: return "DFS_E_ARG: invalid scalar argument (temperature must be finite and > 0)";
+    default: return "unknown dfs status";
+  }
+}
+
+size_t dfs_topk_workspace_bytes(int64_t rows, int64_t V, dfs_dtype_t dt) {
+  if (rows < 1 || V < DFS_K || V > kMaxV || !valid_dtype(dt)) return 0;
+  return plan_topk(rows, V, esize(dt)).ws_bytes;
+}
+
+int dfs_topk(const void* logits, dfs_dtype_t dt, int64_t rows, int64_t V, int k, int32_t* out_idx,
+             float* out_val, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_topk_args(logits, dt, rows, V, k, out_idx, out_val);
+  if (st != DFS_OK) return st;
+  const TopkPlan p = plan_topk(rows, V, esize(dt));
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return DFS_E_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_topk(p, logits, dt == DFS_BF16, out_idx, out_val, ws, stream));
+}
+
+size_t dfs_gate_workspace_bytes(int64_t rows, int64_t d, dfs_dtype_t dt) {
+  if (rows < 1 || d < 1 || d % 8 != 0 || !valid_dtype(dt)) return 0;
+  return plan_gate(rows, d, dt == DFS_BF16).ws_bytes;
+}
+
+int dfs_gate(const void* hidden, const void* W_h, dfs_dtype_t dt, int64_t rows, int64_t d,
+             int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_gate_args(hidden, W_h, dt, rows, d, E, out_gate);
+  if (st != DFS_OK) return st;
+  const GatePlan p = plan_gate(rows, d, dt == DFS_BF16);
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return DFS_E_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_gate(p, hidden, W_h, out_gate, ws, stream));
+}
+
+int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* prev_token,
+                    const float* gate, const void* A, const void* B, dfs_dtype_t table_dt,
+                    int64_t batch, int64_t L, int64_t V, int64_t E, int k, float* out_pair,
+                    hipStream_t stream) {
+  if (!cand_idx || !cand_val || !prev_token || !gate || !A || !B || !out_pair) return DFS_E_NULL;
+  if (!valid_dtype(table_dt) || k != DFS_K || E != DFS_E) return DFS_E_UNSUPPORTED;
+  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K || V > kMaxV)
+    return DFS_E_SHAPE;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(gate, 16) || !aligned(cand_idx, 4) ||
+      !aligned(cand_val, 4) || !aligned(prev_token, 4) || !aligned(out_pair, 4))
+    return DFS_E_ALIGN;
+  int st = check_device();
+  if (st != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_pair_walk(cand_idx, cand_val, prev_token, gate, A, B,
+                                     table_dt == DFS_BF16, batch, L, V, out_pair, nullptr, nullptr,
+                                     nullptr, stream));
+}
+
+int dfs_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L, int k,
+             dfs_walk_t mode, double temperature, uint64_t seed, int32_t* out_path,
+             float* out_scores, hipStream_t stream) {
+  if (!pair || !cand_idx || !out_path || !out_scores) return DFS_E_NULL;
+  if (k != DFS_K) return DFS_E_UNSUPPORTED;
+  int st = check_walk_mode(mode, temperature);
+  if (st != DFS_OK) return st;
+  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L) return DFS_E_SHAPE;
+  if (!aligned(pair, 4) || !aligned(cand_idx, 4) || !aligned(out_path, 4) ||
+      !aligned(out_scores, 4))
+    return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+  const WalkArgs w{(int)mode, temperature, seed};
+  return hip_status(launch_walk(pair, cand_idx, batch, L, w, out_path, out_scores, stream));
+}
+
+size_t dfs_select_workspace_bytes(const dfs_shape_t* shape) {
+  if (check_shape(shape) != DFS_OK) return 0;
+  return select_layout(*shape).total;
+}
+
+int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+               const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
+               double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+               float* out_scores, hipStream_t stream) {
+  if (!logits || !hidden || !prev_token || !A || !B || !W_h || !out_path || !out_scores)
+    return DFS_E_NULL;
+  int st = check_shape(shape);
+  if (st != DFS_OK) return st;
+  if (k != DFS_K) return DFS_E_UNSUPPORTED;
+  if ((st = check_walk_mode(mode, temperature)) != DFS_OK) return st;
+  const dfs_shape_t s = *shape;
+  if (!aligned(logits, esize(s.logits_dtype)) || !aligned(hidden, 16) || !aligned(W_h, 16) ||
+      !aligned(A, 16) || !aligned(B, 16) || !aligned(prev_token, 4) || !aligned(out_path, 4) ||
+      !aligned(out_scores, 4))
+    return DFS_E_ALIGN;
+  const SelectLayout l = select_layout(s);
+  if (!ws || ws_bytes < l.total) return DFS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+
+  char* w = static_cast<char*>(ws);
+  int32_t* cand_idx = reinterpret_cast<int32_t*>(w + l.cand_idx_off);
+  float* cand_val = reinterpret_cast<float*>(w + l.cand_val_off);
+  float* gate = reinterpret_cast<float*>(w + l.gate_off);
+  hipError_t e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
+                             w + l.topk_ws_off, stream);
+  if (e != hipSuccess) return DFS_E_HIP;
+  e = launch_gate(l.gate, hidden, W_h, gate, w + l.gate_ws_off, stream);
+  if (e != hipSuccess) return DFS_E_HIP;
+  const WalkArgs wa{(int)mode, temperature, seed};
+  e = launch_pair_walk(cand_idx, cand_val, prev_token, gate, A, B, s.table_dtype == DFS_BF16,
+                       s.batch, s.L, s.V, nullptr, &wa, out_path, out_scores, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

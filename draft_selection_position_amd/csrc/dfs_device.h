@@ -1,0 +1,84 @@
+// Device-side helpers shared by the selector's kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfs {
+
+constexpr int kK = 16;     // candidates per position
+constexpr int kE = 256;    // embedding / gate width
+constexpr int kWave = 64;  // CDNA wavefront
+
+// ---------------------------------------------------------------- bf16 <-> f32
+// bf16 is the upper half of an fp32 bit pattern; widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---------------------------------------------------------------- selection keys
+// Order-preserving map from a non-NaN float to uint32, with -0 folded into +0.
+__device__ __forceinline__ uint32_t mono32(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unmono32(uint32_t m) {
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
+}
+// 64-bit key: value in the high word, bit-inverted index in the low word, so a
+// larger key means a larger value, then a lower index.  Key 0 is never produced
+// for a non-NaN value and marks an empty slot.
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+  return ((uint64_t)mono32(v) << 32) | (uint32_t)(~idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
+__device__ __forceinline__ float key_value(uint64_t k) { return unmono32((uint32_t)(k >> 32)); }
+
+// ---------------------------------------------------------------- wave utilities
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  lo = (uint32_t)__shfl_xor((int)lo, m);
+  hi = (uint32_t)__shfl_xor((int)hi, m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
+  uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  lo = (uint32_t)__shfl((int)lo, src);
+  hi = (uint32_t)__shfl((int)hi, src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one 64-bit key per lane across the wave, descending: lane 0
+// ends with the largest key.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = shfl_xor_u64(x, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;
+      const bool take_max = (lower == desc);
+      const uint64_t mx = x > y ? x : y;
+      const uint64_t mn = x > y ? y : x;
+      x = take_max ? mx : mn;
+    }
+  }
+  return x;
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uniformf(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+}  // namespace dfs

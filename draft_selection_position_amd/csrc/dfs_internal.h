@@ -1,0 +1,60 @@
+// Host-side plans and kernel launchers of the selector (internal to libdfs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfs {
+
+// Workgroups a launch should offer MI355X (256 CUs) to keep every CU busy.
+constexpr int64_t kTargetBlocks = 2048;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- top-16
+struct TopkPlan {
+  int64_t rows, V;
+  int esize;       // bytes per logit
+  int parts;       // chunks per row (1 = no merge pass)
+  int64_t chunk;   // elements per chunk, a multiple of the 16-byte vector width
+  size_t ws_bytes; // partial lists when parts > 1
+};
+TopkPlan plan_topk(int64_t rows, int64_t V, int esize);
+hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
+                       float* out_val, void* ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- gate
+struct GatePlan {
+  int64_t rows, d;
+  bool bf16;
+  int splits;          // K-splits (partial sums reduced by the finish kernel)
+  int64_t kchunk;      // hidden elements per split
+  int row_tiles;       // 16-row MFMA tiles per wave (bf16 path)
+  size_t packed_off, packed_bytes;    // W_h packed for the matrix cores (bf16 path)
+  size_t partial_off, partial_bytes;  // [splits, rows, 256] fp32
+  size_t ws_bytes;
+};
+GatePlan plan_gate(int64_t rows, int64_t d, bool bf16);
+hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, float* out_gate,
+                       void* ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- pair scores and walk
+struct WalkArgs {
+  int mode;  // 0 greedy, 1 gumbel
+  double temperature;
+  uint64_t seed;
+};
+// Pair scores for every (sequence, position); optionally written to out_pair and
+// optionally followed by the walk in the same kernel (out_path/out_scores non-null).
+hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
+                            const int32_t* prev_token, const float* gate, const void* A,
+                            const void* B, bool bf16_tables, int64_t batch, int64_t L,
+                            int64_t V, float* out_pair, const WalkArgs* walk, int32_t* out_path,
+                            float* out_scores, hipStream_t stream);
+hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L,
+                       const WalkArgs& walk, int32_t* out_path, float* out_scores,
+                       hipStream_t stream);
+
+}  // namespace dfs

@@ -1,0 +1,318 @@
+// Vocabulary-wide top-16 per row in one streaming pass over the logits.
+//
+// DFlash 2 keeps the 16 best candidates of each block position instead of only
+// the top one (blog post "DFlash 2: Keep Drafting Parallel", section "The Right
+// Tokens Are Already There").  The order is value descending, then token id
+// ascending; -0 equals +0.
+//
+// Design (gfx950): the pass is HBM-bound, so each workgroup (4 waves) streams a
+// row chunk with 16-byte coalesced loads, four per thread in flight plus the
+// next iteration's four.  An element is only looked at further when it reaches
+// the wave's admission threshold; admitted elements are appended to a per-wave
+// LDS buffer as exact 64-bit (value, index) keys with one ballot per element
+// slot, and the buffer is merged into the wave's sorted top-16 (held in lanes
+// 0..15) by a 64-lane bitonic sort.  The 16th best key of any wave is a valid
+// threshold for the whole chunk and is shared through LDS.  The four wave lists
+// are merged at the end; rows split over several workgroups are merged by a
+// second kernel.  Every comparison is on exact integer keys, so the result does
+// not depend on the order in which elements are seen.
+#include "dfs_device.h"
+#include "dfs_internal.h"
+
+namespace dfs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnroll = 4;        // 16-byte vectors per thread per iteration
+constexpr int kMergeAt = 64;      // merge once more keys than this are buffered
+constexpr int kCap = kMergeAt + 8 * kWave;  // room for one whole vector per lane on top
+constexpr int kMinChunk = 4096;   // elements; below this a split does not pay
+
+template <bool kBf16>
+struct Elems;
+template <>
+struct Elems<true> {
+  static constexpr int per_vec = 8;
+  using T = uint16_t;
+};
+template <>
+struct Elems<false> {
+  static constexpr int per_vec = 4;
+  using T = float;
+};
+
+struct WaveTop {
+  uint64_t list;  // lanes 0..15: best keys so far, descending (0 = empty slot)
+  float thr;      // admission threshold, identical in every lane
+  int cnt;        // keys waiting in the buffer, identical in every lane
+};
+
+// Merge the buffered keys into the wave's list and raise the threshold.
+__device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint32_t* s_thr,
+                                           int lane) {
+  __builtin_amdgcn_wave_barrier();
+  int cnt = w.cnt;
+  while (cnt > 0) {
+    const int n = cnt < 48 ? cnt : 48;
+    uint64_t x = 0;
+    if (lane < 16) {
+      x = w.list;
+    } else if (lane - 16 < n) {
+      x = buf[cnt - n + (lane - 16)];
+    }
+    x = wave_sort_desc(x, lane);
+    w.list = lane < 16 ? x : 0;
+    cnt -= n;
+  }
+  w.cnt = 0;
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t k16 = shfl_u64(w.list, 15);
+  if (k16 != 0) {
+    uint32_t m = (uint32_t)(k16 >> 32);
+    uint32_t old = 0;
+    if (lane == 0) old = atomicMax(s_thr, m);
+    old = (uint32_t)__shfl((int)old, 0);
+    m = m > old ? m : old;
+    w.thr = uniformf(unmono32(m));
+  }
+}
+
+// Append this lane's element to the wave buffer when `adm`.
+__device__ __forceinline__ void append(WaveTop& w, bool adm, float v, uint32_t idx,
+                                       uint64_t* buf) {
+  const uint64_t mask = __ballot(adm);
+  if (mask == 0) return;
+  const int pos = w.cnt + lanes_below(mask);
+  if (adm) buf[pos] = make_key(v, idx);
+  w.cnt = uniform(w.cnt + __popcll(mask));
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float load_scalar(const typename Elems<kBf16>::T* p, int64_t i) {
+  if constexpr (kBf16) {
+    return bf16_to_f32(p[i]);
+  } else {
+    return p[i];
+  }
+}
+
+// Admission test and append for one 16-byte vector (8 bf16 or 4 fp32 values),
+// then a merge if the buffer has filled past kMergeAt.  On a wave's first vector
+// (`seed`), the threshold is first raised to the 16th largest lane maximum: those
+// 16 maxima are distinct elements, so nothing below it can make the top 16.
+template <bool kBf16>
+__device__ __forceinline__ void scan_vec(const uint4& d, uint32_t idx0, WaveTop& w, uint64_t* buf,
+                                         uint32_t* s_thr, int lane, bool seed) {
+  constexpr int PV = Elems<kBf16>::per_vec;
+  float v[PV];
+  if constexpr (kBf16) {
+    v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
+    v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+    v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
+    v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+  } else {
+    v[0] = __uint_as_float(d.x); v[1] = __uint_as_float(d.y);
+    v[2] = __uint_as_float(d.z); v[3] = __uint_as_float(d.w);
+  }
+  // fmaxf ignores NaN, so padding lanes (all-NaN) never pass.
+  float m = v[0];
+#pragma unroll
+  for (int e = 1; e < PV; ++e) m = fmaxf(m, v[e]);
+  if (seed) {
+    const uint64_t lk = (m == m) ? make_key(m, (uint32_t)lane) : 0ull;
+    const uint64_t k16 = shfl_u64(wave_sort_desc(lk, lane), 15);
+    if (k16 != 0) {
+      const float t = key_value(k16);
+      if (t > w.thr) w.thr = uniformf(t);
+    }
+  }
+  if (__ballot(m >= w.thr) == 0) return;
+#pragma unroll
+  for (int e = 0; e < PV; ++e) append(w, v[e] >= w.thr, v[e], idx0 + e, buf);
+  if (w.cnt > kMergeAt) wave_merge(w, buf, s_thr, lane);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(const void* __restrict__ logits,
+                                                              int64_t V, int parts, int64_t chunk,
+                                                              uint64_t* __restrict__ partial,
+                                                              int32_t* __restrict__ out_idx,
+                                                              float* __restrict__ out_val) {
+  using T = typename Elems<kBf16>::T;
+  constexpr int PV = Elems<kBf16>::per_vec;
+  __shared__ uint64_t s_buf[kWaves][kCap];
+  __shared__ uint64_t s_list[kWaves * kK];
+  __shared__ uint32_t s_thr;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t row = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
+  const T* rowp = static_cast<const T*>(logits) + row * V;
+  const int64_t beg = (int64_t)part * chunk;
+  const int64_t end = beg + chunk < V ? beg + chunk : V;
+
+  if (tid == 0) s_thr = 0u;
+  __syncthreads();
+
+  uint64_t* buf = s_buf[wave];
+  WaveTop w;
+  w.list = 0;
+  w.thr = -INFINITY;
+  w.cnt = 0;
+
+  // [vb, ve) is the 16-byte aligned middle of the chunk; the rest is scalar.
+  const uintptr_t a_beg = (uintptr_t)(rowp + beg);
+  int64_t vb = beg + (int64_t)(((16u - (a_beg & 15u)) & 15u) / sizeof(T));
+  if (vb > end) vb = end;
+  const int64_t nvec = (end - vb) / PV;
+  const int64_t ve = vb + nvec * PV;
+
+  if (wave == 0) {
+    const int nhead = (int)(vb - beg);
+    const int ntail = (int)(end - ve);
+    int64_t i = -1;
+    if (lane < nhead) {
+      i = beg + lane;
+    } else if (lane < nhead + ntail) {
+      i = ve + (lane - nhead);
+    }
+    float v = 0.0f;
+    if (i >= 0) v = load_scalar<kBf16>(rowp, i);
+    append(w, i >= 0 && v >= w.thr, v, (uint32_t)i, buf);  // at most 14 keys
+  }
+
+  const uint4* vp = reinterpret_cast<const uint4*>(rowp + vb);
+  const int64_t step = (int64_t)kThreads * kUnroll;
+  const int64_t niter = (nvec + step - 1) / step;
+  const uint4 pad = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);  // NaN
+  uint4 cur[kUnroll], nxt[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t vid = (int64_t)u * kThreads + tid;
+    cur[u] = pad;
+    if (vid < nvec) cur[u] = vp[vid];
+  }
+  for (int64_t it = 0; it < niter; ++it) {
+    if (it + 1 < niter) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t vid = (it + 1) * step + (int64_t)u * kThreads + tid;
+        nxt[u] = pad;
+        if (vid < nvec) nxt[u] = vp[vid];
+      }
+    }
+    {  // other waves may have raised the chunk's threshold
+      const uint32_t m = uniform(
+          (int)__hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+      if (m != 0u) {
+        const float t = unmono32(m);
+        if (t > w.thr) w.thr = uniformf(t);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t vid = it * step + (int64_t)u * kThreads + tid;
+      scan_vec<kBf16>(cur[u], (uint32_t)(vb + vid * PV), w, buf, &s_thr, lane,
+                      it == 0 && u == 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+  }
+
+  if (w.cnt > 0) wave_merge(w, buf, &s_thr, lane);
+  if (lane < kK) s_list[wave * kK + lane] = w.list;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t x = s_list[lane];  // kWaves * kK == 64 keys
+    x = wave_sort_desc(x, lane);
+    if (lane < kK) {
+      if (parts == 1) {
+        out_idx[row * kK + lane] = (int32_t)key_index(x);
+        out_val[row * kK + lane] = key_value(x);
+      } else {
+        partial[(row * parts + part) * kK + lane] = x;
+      }
+    }
+  }
+}
+
+// Merge `parts` partial top-16 lists per row (one workgroup per row).
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ partial,
+                                                              int parts,
+                                                              int32_t* __restrict__ out_idx,
+                                                              float* __restrict__ out_val) {
+  __shared__ uint64_t s_list[kWaves * kK];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t row = blockIdx.x;
+  const uint64_t* src = partial + row * parts * kK;
+  uint64_t list = 0;
+  // Each sort takes the wave's list plus up to three more lists (48 keys).
+  for (int p0 = wave * 3; p0 < parts; p0 += kWaves * 3) {
+    uint64_t x = 0;
+    if (lane < kK) {
+      x = list;
+    } else {
+      const int p = p0 + (lane - kK) / kK;
+      if (p < parts) x = src[(int64_t)p * kK + (lane & (kK - 1))];
+    }
+    x = wave_sort_desc(x, lane);
+    list = lane < kK ? x : 0;
+  }
+  if (lane < kK) s_list[wave * kK + lane] = list;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t x = wave_sort_desc(s_list[lane], lane);
+    if (lane < kK) {
+      out_idx[row * kK + lane] = (int32_t)key_index(x);
+      out_val[row * kK + lane] = key_value(x);
+    }
+  }
+}
+
+}  // namespace
+
+TopkPlan plan_topk(int64_t rows, int64_t V, int esize) {
+  TopkPlan p{};
+  p.rows = rows;
+  p.V = V;
+  p.esize = esize;
+  const int64_t pv = 16 / esize;
+  int64_t parts = 1;
+  if (rows < kTargetBlocks) {
+    parts = cdiv(kTargetBlocks, rows);
+    int64_t maxp = V / kMinChunk;
+    if (maxp < 1) maxp = 1;
+    if (parts > maxp) parts = maxp;
+    if (parts > 64) parts = 64;
+  }
+  const int64_t chunk = (int64_t)align_up((size_t)cdiv(V, parts), (size_t)pv);
+  p.parts = (int)cdiv(V, chunk);
+  p.chunk = chunk;
+  p.ws_bytes = p.parts > 1 ? align_up((size_t)rows * p.parts * kK * sizeof(uint64_t), 256) : 0;
+  return p;
+}
+
+hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
+                       float* out_val, void* ws, hipStream_t stream) {
+  uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
+  const dim3 grid((unsigned)(p.rows * p.parts));
+  if (bf16) {
+    topk_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial,
+                                                           out_idx, out_val);
+  } else {
+    topk_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk,
+                                                            partial, out_idx, out_val);
+  }
+  if (p.parts > 1) {
+    topk_merge_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.parts, out_idx,
+                                                                        out_val);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfs

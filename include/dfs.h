@@ -1,0 +1,164 @@
+/*
+ * dfs.h -- C ABI of the DFlash 2 draft-path selector for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (blog post "DFlash 2: Keep Drafting Parallel", Inco AI, 2026):
+ *   1. per block position t, keep the 16 highest-logit candidates C_t of the
+ *      drafter's vocabulary logits U_t                     (section "The Right Tokens
+ *      Are Already There");
+ *   2. score every adjacent (predecessor a, candidate b) pair
+ *         S_t(a,b) = U_t(b) + < A(a) (elementwise) H(h_t), B(b) >
+ *      with 256-wide token embeddings A, B and a context gate H(h_t) computed from
+ *      the drafter hidden state h_t   (section "A Lightweight Path Selector"; the
+ *      equation itself survives in the twiscan.com Chinese translation);
+ *   3. walk the precomputed scores once from the last verified token: greedy takes
+ *      the best successor at each step, sampling draws from the same scores;
+ *   4. no extra backbone or LM-head pass: only the drafter's outputs are read.
+ *
+ * Parameterisation chosen here where the pages are silent:
+ *   H(h_t) = sigmoid(h_t W_h), W_h of shape [d, 256];  A, B are [V, 256] tables.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     dfs_shape_t pointer, which is host memory read during the call only.  The
+ *     library allocates nothing and keeps no pointer after it returns.
+ *   - Every call only enqueues kernels on `stream` (NULL = the device's null
+ *     stream) on the current HIP device and returns without synchronising.
+ *     Results are valid once the stream has reached that point.
+ *   - All tensors are dense and row-major (C order) with the shapes given.
+ *   - Return value: DFS_OK (0) or one of the positive dfs_status_t codes.
+ *     Arguments are checked on the host before anything is enqueued; on an error
+ *     nothing is enqueued and no output is written.  dfs_status_str() names a code.
+ *   - Device-side contracts that are not checked: logits hold no NaN (-inf is
+ *     allowed), every token id passed in lies in [0, V), and input and output
+ *     buffers do not overlap.
+ *   - Calls on different streams may run concurrently; calls that share a
+ *     workspace buffer must be ordered by the caller.
+ *   - Results are bitwise deterministic for identical inputs.
+ */
+#ifndef DFS_H_
+#define DFS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFS_K 16      /* candidates kept per block position */
+#define DFS_E 256     /* embedding and gate width */
+#define DFS_MAX_L 16  /* longest block handled; the post's blocks span 4 to 16 tokens */
+
+typedef enum {
+  DFS_OK = 0,
+  DFS_E_NULL = 1,        /* a required pointer is NULL */
+  DFS_E_SHAPE = 2,       /* a size is out of range (batch, rows < 1; V < 16; L not in [1,16]; ...) */
+  DFS_E_UNSUPPORTED = 3, /* k != 16, E != 256, an unknown dtype or walk mode, or d not a multiple of 8 */
+  DFS_E_WORKSPACE = 4,   /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  DFS_E_ALIGN = 5,       /* a pointer is not aligned as documented */
+  DFS_E_HIP = 6,         /* no usable HIP device, or a HIP launch error */
+  DFS_E_ARCH = 7,        /* the current device is not gfx950 */
+  DFS_E_ARG = 8          /* a scalar argument is invalid (e.g. temperature <= 0 for sampling) */
+} dfs_status_t;
+
+typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype_t;
+
+typedef enum {
+  DFS_WALK_GREEDY = 0, /* argmax successor at each step, lowest candidate slot on ties */
+  DFS_WALK_GUMBEL = 1  /* Gumbel-max draw from softmax(S / temperature) over the 16 candidates */
+} dfs_walk_t;
+
+/* Shape of one dfs_select call. */
+typedef struct {
+  int64_t batch;             /* sequences, >= 1 */
+  int64_t L;                 /* block positions per sequence, 1..16 */
+  int64_t V;                 /* vocabulary size, 16..2^31-1 */
+  int64_t d;                 /* drafter hidden width, >= 8, multiple of 8 */
+  dfs_dtype_t logits_dtype;  /* logits */
+  dfs_dtype_t act_dtype;     /* hidden and W_h */
+  dfs_dtype_t table_dtype;   /* A and B */
+} dfs_shape_t;
+
+/* ---------------------------------------------------------------- top-16
+ * For each of `rows` rows of `logits` [rows, V] (dtype dt), the k = 16 largest
+ * entries ordered by value descending, then token id ascending (ties go to the
+ * lower id); -0 and +0 count as equal and +0 is reported.
+ *   out_idx [rows, 16] int32 token ids;  out_val [rows, 16] fp32 values (exact
+ *   widening of the input values).
+ * Alignment: logits to its element size; out_idx, out_val to 4 bytes; ws to 256.
+ * ws: dfs_topk_workspace_bytes(rows, V, dt) bytes of scratch (may be 0, then ws may
+ * be NULL).                                                                      */
+size_t dfs_topk_workspace_bytes(int64_t rows, int64_t V, dfs_dtype_t dt);
+int dfs_topk(const void* logits, dfs_dtype_t dt, int64_t rows, int64_t V, int k,
+             int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- context gate
+ * out_gate[r, e] = sigmoid( sum_c hidden[r, c] * W_h[c, e] ),  r < rows, e < E = 256.
+ *   hidden [rows, d] and W_h [d, 256] of dtype dt; products and sums in fp32;
+ *   out_gate [rows, 256] fp32.
+ * Alignment: hidden, W_h 16 bytes; out_gate 4 bytes; ws 256 bytes.
+ * ws: dfs_gate_workspace_bytes(rows, d, dt) bytes of scratch.                       */
+size_t dfs_gate_workspace_bytes(int64_t rows, int64_t d, dfs_dtype_t dt);
+int dfs_gate(const void* hidden, const void* W_h, dfs_dtype_t dt, int64_t rows, int64_t d,
+             int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- pair scores
+ * For sequence b and position t (row r = b*L + t):
+ *   t >= 1:  out_pair[b, t, i, j] = cand_val[r, j]
+ *              + sum_e A[cand_idx[r-1, i], e] * gate[r, e] * B[cand_idx[r, j], e]
+ *   t == 0:  the predecessor is prev_token[b] for every slot i (the row repeats).
+ *   cand_idx [batch, L, 16] int32, cand_val [batch, L, 16] fp32 (a dfs_topk result),
+ *   prev_token [batch] int32 (last verified token), gate [batch*L, 256] fp32
+ *   (a dfs_gate result), A, B [V, 256] of dtype table_dt.
+ *   out_pair [batch, L, 16, 16] fp32.  Sums in fp32 on the matrix cores; for bf16
+ *   tables the gated predecessor embedding is split into two bf16 terms, so the
+ *   product is exact to about 2^-17 relative before fp32 accumulation.
+ * Alignment: A, B, gate 16 bytes; the int32/fp32 arrays 4 bytes.                   */
+int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* prev_token,
+                    const float* gate, const void* A, const void* B, dfs_dtype_t table_dt,
+                    int64_t batch, int64_t L, int64_t V, int64_t E, int k, float* out_pair,
+                    hipStream_t stream);
+
+/* ---------------------------------------------------------------- walk
+ * One walk per sequence over pair [batch, L, 16, 16] (a dfs_pair_scores result):
+ * start at predecessor slot 0 of position 0 (the last verified token's row); at
+ * step t choose slot j* in row i (the previous choice):
+ *   greedy:  j* = argmax_j pair[b,t,i,j], lowest j on ties;
+ *   gumbel:  j* = argmax_j pair[b,t,i,j] / temperature + g(seed, b, t, j), in fp64,
+ *            g = -log(-log(u)), u = ((x >> 9) + 0.5) * 2^-23, x = word 0 of
+ *            Philox4x32-10 with counter (j, t, b, 0) and key (seed low, seed high).
+ *   out_path [batch, L] int32 = cand_idx[b, t, j*];
+ *   out_scores [batch, L] fp32 = pair[b, t, i, j*] (un-noised, not divided by T).
+ * temperature must be finite and > 0 in gumbel mode (ignored for greedy).          */
+int dfs_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L, int k,
+             dfs_walk_t mode, double temperature, uint64_t seed, int32_t* out_path,
+             float* out_scores, hipStream_t stream);
+
+/* ---------------------------------------------------------------- fused selector
+ * The whole selector: dfs_topk over logits [batch, L, V], dfs_gate over hidden
+ * [batch, L, d] with W_h [d, 256], then pair scores and the walk fused in one
+ * kernel (scores stay on chip).  Same results as calling the four steps in turn.
+ * prev_token [batch] int32; A, B [V, 256]; out_path [batch, L] int32; out_scores
+ * [batch, L] fp32.  Alignment as in the step entry points; ws 256 bytes.
+ * ws: dfs_select_workspace_bytes(shape) bytes of scratch (about 9 MB at batch 256,
+ * L 16, V 151936, d 5120).                                                        */
+size_t dfs_select_workspace_bytes(const dfs_shape_t* shape);
+int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+               const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
+               double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+               float* out_scores, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* dfs_status_str(int status);
+
+/* ABI version of this header and library (major * 100 + minor). */
+#define DFS_ABI_VERSION 100
+int dfs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFS_H_ */

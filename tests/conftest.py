@@ -16,3 +16,24 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def root_dir():
     return ROOT
+
+
+_FULL = {}
+
+
+@pytest.fixture(scope="session")
+def full_workload():
+    """Full-size seeded inputs of a named workload, on the host and on cuda:0 (cached)."""
+
+    def get(name):
+        if name not in _FULL:
+            from workloads import make
+
+            from .parity import upload
+
+            print(f"generating workload {name}", flush=True)
+            inp = make(name)
+            _FULL[name] = (inp, upload(inp))
+        return _FULL[name]
+
+    return get

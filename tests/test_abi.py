@@ -1,0 +1,139 @@
+"""The C ABI: library loads, exports what include/dfs.h declares, and rejects bad
+arguments on the host before touching any device (CPU only; no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_selection_position_amd as dfs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dfs.h")
+P = 0x10000  # a fake, 256-byte-aligned device address; never dereferenced by these calls
+OK, E_NULL, E_SHAPE, E_UNSUP, E_WS, E_ALIGN, E_HIP, E_ARCH, E_ARG = range(9)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dfs_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dfs.lib_path()):
+        pytest.skip("libdfs.so not built")
+    return dfs.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.dfs_abi_version() == 100
+    for code in range(9):
+        s = dfs.status_str(code)
+        assert s.startswith("DFS_")
+    assert dfs.status_str(12345) == "unknown dfs status"
+
+
+def test_workspace_queries_are_host_only(L):
+    assert dfs.topk_workspace_bytes(4096, 151936, __import__("torch").bfloat16) == 0  # one chunk per row
+    assert dfs.topk_workspace_bytes(16, 151936, __import__("torch").bfloat16) > 0  # split rows
+    assert L.dfs_topk_workspace_bytes(0, 100, 1) == 0
+    assert dfs.gate_workspace_bytes(16, 5120, __import__("torch").bfloat16) > 0
+    nb = dfs.select_workspace_bytes(256, 16, 151936, 5120)
+    assert 4 << 20 < nb < 64 << 20
+    assert dfs.select_workspace_bytes(1, 17, 1000, 64) == 0  # L > 16 is rejected
+
+
+def _topk(L, logits=P, dt=1, rows=8, V=1000, k=16, idx=P, val=P, ws=P, wsb=1 << 20):
+    return L.dfs_topk(logits, dt, rows, V, k, idx, val, ws, wsb, None)
+
+
+def test_topk_validation(L):
+    assert _topk(L, logits=None) == E_NULL
+    assert _topk(L, idx=None) == E_NULL
+    assert _topk(L, k=8) == E_UNSUP
+    assert _topk(L, dt=7) == E_UNSUP
+    assert _topk(L, rows=0) == E_SHAPE
+    assert _topk(L, V=15) == E_SHAPE
+    assert _topk(L, V=2**31) == E_SHAPE
+    assert _topk(L, logits=P + 1) == E_ALIGN
+    assert _topk(L, dt=0, logits=P + 2) == E_ALIGN
+    assert _topk(L, val=P + 2) == E_ALIGN
+    assert _topk(L, rows=8, V=151936, ws=None, wsb=0) == E_WS  # split rows need scratch
+
+
+def test_gate_validation(L):
+    def g(h=P, w=P, dt=1, rows=4, d=64, E=256, out=P, ws=P, wsb=1 << 24):
+        return L.dfs_gate(h, w, dt, rows, d, E, out, ws, wsb, None)
+
+    assert g(h=None) == E_NULL
+    assert g(E=128) == E_UNSUP
+    assert g(d=60) == E_UNSUP
+    assert g(rows=0) == E_SHAPE
+    assert g(h=P + 8) == E_ALIGN
+    assert g(ws=None, wsb=0) == E_WS
+
+
+def test_pair_and_walk_validation(L):
+    def p(ci=P, cv=P, pt=P, g=P, A=P, B=P, dt=1, b=2, Lp=4, V=100, E=256, k=16, out=P):
+        return L.dfs_pair_scores(ci, cv, pt, g, A, B, dt, b, Lp, V, E, k, out, None)
+
+    assert p(A=None) == E_NULL
+    assert p(k=4) == E_UNSUP
+    assert p(E=64) == E_UNSUP
+    assert p(Lp=17) == E_SHAPE
+    assert p(Lp=0) == E_SHAPE
+    assert p(V=10) == E_SHAPE
+    assert p(g=P + 4) == E_ALIGN
+
+    def w(pair=P, ci=P, b=2, Lw=4, k=16, mode=0, T=1.0, seed=0, path=P, sc=P):
+        return L.dfs_walk(pair, ci, b, Lw, k, mode, T, seed, path, sc, None)
+
+    assert w(pair=None) == E_NULL
+    assert w(mode=2) == E_UNSUP
+    assert w(mode=1, T=0.0) == E_ARG
+    assert w(mode=1, T=float("nan")) == E_ARG
+    assert w(mode=1, T=float("inf")) == E_ARG
+    assert w(Lw=0) == E_SHAPE
+    assert w(path=P + 2) == E_ALIGN
+
+
+def test_select_validation(L):
+    shape = dfs._Shape(2, 4, 1000, 64, 1, 1, 1)
+
+    def s(lg=P, h=P, pt=P, A=P, B=P, W=P, k=16, sh=ctypes.byref(shape), mode=0, T=1.0, ws=P, wsb=1 << 26,
+          path=P, sc=P):
+        return L.dfs_select(lg, h, pt, A, B, W, k, sh, mode, T, 0, ws, wsb, path, sc, None)
+
+    assert s(lg=None) == E_NULL
+    assert s(sh=None) == E_NULL
+    assert s(k=32) == E_UNSUP
+    assert s(mode=1, T=-1.0) == E_ARG
+    assert s(h=P + 2) == E_ALIGN
+    assert s(ws=P + 64) == E_ALIGN
+    assert s(wsb=16) == E_WS
+    assert s(ws=None) == E_WS
+    for bad in [dict(batch=0), dict(L=17), dict(V=3), dict(d=0)]:
+        sh = dfs._Shape(2, 4, 1000, 64, 1, 1, 1)
+        for k_, v_ in bad.items():
+            setattr(sh, k_, v_)
+        assert s(sh=ctypes.byref(sh)) == E_SHAPE
+    sh = dfs._Shape(2, 4, 1000, 60, 1, 1, 1)
+    assert s(sh=ctypes.byref(sh)) == E_UNSUP
+    sh = dfs._Shape(2, 4, 1000, 64, 1, 5, 1)
+    assert s(sh=ctypes.byref(sh)) == E_UNSUP
+
+
+def test_valid_arguments_without_a_device_report_hip_error(L):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _topk(L, rows=4096, V=151936) == E_HIP

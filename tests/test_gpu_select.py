@@ -1,0 +1,100 @@
+"""GPU parity of the fused dfs_select against the oracle, on the five workloads and variants."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make, variant
+
+from .parity import check_path, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_selection_position_amd as dfs
+
+    dfs.lib()
+
+
+def _select(dev, cfg):
+    import draft_selection_position_amd as dfs
+
+    path, scores = dfs.select(dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"],
+                              mode=cfg.walk, temperature=cfg.temperature, seed=cfg.walk_seed)
+    torch.cuda.synchronize()
+    return path.cpu().numpy(), scores.cpu().numpy()
+
+
+def _check(inp, path, scores, seqs):
+    cfg = inp.config
+    near = 0
+    for i in seqs:
+        res = oracle.select_sequence(inp, int(i))
+        rep = check_path(path[i], scores[i], res, cfg.walk, cfg.temperature, cfg.walk_seed, int(inp.seq_ids[i]))
+        near += len(rep["near_ties"])
+    return near
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_select_full_size_configs(cfg, full_workload):
+    inp, dev = full_workload(cfg.name)
+    print(f"select {cfg.name}: batch {cfg.batch} L {cfg.L} V {cfg.V} d {cfg.d} walk {cfg.walk}", flush=True)
+    path, scores = _select(dev, cfg)
+    seqs = range(cfg.batch) if cfg.batch <= 4 else np.unique(
+        np.r_[0, cfg.batch - 1, np.random.default_rng(2).choice(cfg.batch, 10, replace=False)])
+    near = _check(inp, path, scores, seqs)
+    print(f"select {cfg.name}: {len(seqs)} sequences checked, {near} near-tie steps", flush=True)
+
+
+VARIANTS = [
+    variant("tiny", emb_std=0.3),  # the bilinear term moves the walk off the top-1
+    variant("tiny", emb_std=0.3, L=1),
+    variant("tiny", emb_std=0.3, L=3, V=32001, batch=5),
+    variant("single_stream", emb_std=0.3, batch=6, V=32001, d=512),
+    variant("single_stream", emb_std=0.3, batch=4, L=7, tie_levels=16, d=256),
+    variant("sampled", emb_std=0.3, batch=6, V=50000, d=256, temperature=0.7, walk_seed=12345),
+    variant("sampled", emb_std=0.3, batch=3, V=50000, d=256, L=5, temperature=2.0, walk_seed=2**63 + 5),
+    variant("throughput", emb_std=0.3, batch=3, V=40000, d=1024),
+]
+
+
+@pytest.mark.parametrize("cfg", VARIANTS, ids=lambda c: c.name)
+def test_select_variants(cfg):
+    inp = make(cfg)
+    print(f"select variant {cfg.name}", flush=True)
+    path, scores = _select(upload(inp), cfg)
+    _check(inp, path, scores, range(cfg.batch))
+    if cfg.emb_std >= 0.3 and cfg.walk == "greedy":
+        # the bilinear term must matter: some step leaves the per-position top-1
+        top1 = np.stack([oracle.top16_rows(oracle.widen(inp.logits[i], cfg.dtype))[0][:, 0]
+                         for i in range(cfg.batch)])
+        if cfg.L > 1:
+            assert (path != top1).any()
+
+
+def test_select_equals_step_chain():
+    import draft_selection_position_amd as dfs
+
+    cfg = variant("single_stream", emb_std=0.3, batch=5, V=20000, d=256)
+    dev = upload(make(cfg))
+    path, scores = dfs.select(dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])
+    idx, val = dfs.topk(dev["logits"])
+    g = dfs.gate(dev["hidden"], dev["W_h"])
+    pair = dfs.pair_scores(idx, val, dev["prev_token"], g, dev["A"], dev["B"])
+    p2, s2 = dfs.walk(pair, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(path, p2)
+    assert torch.equal(scores, s2)
+
+
+def test_select_is_deterministic(full_workload):
+    inp, dev = full_workload("small_batch")
+    first = _select(dev, inp.config)
+    for _ in range(10):
+        again = _select(dev, inp.config)
+        np.testing.assert_array_equal(first[0], again[0])
+        np.testing.assert_array_equal(first[1], again[1])

@@ -1,0 +1,117 @@
+"""GPU parity of dfs_gate, dfs_pair_scores and dfs_walk against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make, variant
+
+from .parity import assert_scores, check_path, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_selection_position_amd as dfs
+
+    dfs.lib()
+
+
+def dfs_mod():
+    import draft_selection_position_amd as dfs
+
+    return dfs
+
+
+# ---------------------------------------------------------------- gate
+
+GATE_ATOL = 2e-5  # fp32 sums of d bf16 products; sigmoid slope <= 1/4
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_gate_full_size_configs(cfg, full_workload):
+    inp, dev = full_workload(cfg.name)
+    print(f"gate {cfg.name}: rows {cfg.batch * cfg.L} d {cfg.d}", flush=True)
+    g = dfs_mod().gate(dev["hidden"].view(-1, cfg.d), dev["W_h"])
+    torch.cuda.synchronize()
+    g = g.cpu().numpy().astype(np.float64)
+    h = oracle.widen(inp.hidden.reshape(-1, cfg.d), cfg.dtype)
+    W = oracle.widen(inp.W_h, cfg.dtype)
+    rows = np.arange(h.shape[0]) if h.shape[0] <= 64 else np.random.default_rng(1).choice(h.shape[0], 64, False)
+    want = oracle.gate(h[rows], W)
+    np.testing.assert_allclose(g[rows], want, rtol=0, atol=GATE_ATOL)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,d", [(1, 8), (37, 72), (16, 5120), (300, 1000), (2049, 256), (4100, 64)])
+def test_gate_shapes(rows, d, dtype):
+    rng = np.random.default_rng(rows * 7 + d)
+    h = rng.standard_normal((rows, d)).astype(np.float32)
+    W = (rng.standard_normal((d, 256)) * 0.05).astype(np.float32)
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+
+        h, W = f32_to_bf16_bits(h), f32_to_bf16_bits(W)
+    g = dfs_mod().gate(to_dev(h), to_dev(W))
+    torch.cuda.synchronize()
+    want = oracle.gate(oracle.widen(h, dtype), oracle.widen(W, dtype))
+    np.testing.assert_allclose(g.cpu().numpy(), want, rtol=0, atol=GATE_ATOL)
+
+
+# ---------------------------------------------------------------- pair scores and walk
+
+
+def _oracle_steps(inp):
+    """Oracle candidates, gate, pair tensor and walk for every sequence of inp."""
+    return oracle.select(inp)
+
+
+def _upload_steps(res, inp):
+    cidx = torch.from_numpy(np.stack([r.cand_idx for r in res]).astype(np.int32)).cuda()
+    cval = torch.from_numpy(np.stack([r.cand_val for r in res]).astype(np.float32)).cuda()
+    gate = torch.from_numpy(np.stack([r.gate for r in res]).astype(np.float32)).cuda()
+    prev = torch.from_numpy(inp.prev_token.astype(np.int32)).cuda()
+    return cidx, cval, gate, prev
+
+
+PAIR_CASES = [
+    variant("tiny", V=3000, d=64, batch=3),
+    variant("tiny", V=3000, d=64, batch=2, emb_std=0.3, L=16),
+    variant("single_stream", V=5000, d=128, batch=4, emb_std=0.3),
+    variant("single_stream", V=5000, d=128, batch=2, L=1, emb_std=0.3),
+    variant("sampled", V=6000, d=64, batch=5, emb_std=0.3, L=7),
+]
+
+
+@pytest.mark.parametrize("cfg", PAIR_CASES, ids=lambda c: c.name)
+def test_pair_scores_match_oracle(cfg):
+    inp = make(cfg)
+    res = _oracle_steps(inp)
+    cidx, cval, gate, prev = _upload_steps(res, inp)
+    A, B = to_dev(inp.A), to_dev(inp.B)
+    pair = dfs_mod().pair_scores(cidx, cval, prev, gate, A, B)
+    torch.cuda.synchronize()
+    got = pair.cpu().numpy()
+    # the oracle's pair tensor used the fp64 gate; the GPU got it rounded to fp32
+    want = np.stack([r.pair for r in res])
+    assert_scores(got, want, "pair")
+    err = np.abs(got - want).max()
+    print(f"pair {cfg.name}: max abs error {err:.3g}", flush=True)
+    assert err < 5e-5  # much tighter than the tolerance: hi/lo bf16 split + fp32 sums
+
+
+@pytest.mark.parametrize("cfg", PAIR_CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("gumbel", 1.0), ("gumbel", 0.7)])
+def test_walk_matches_oracle(cfg, mode, T):
+    inp = make(variant(cfg, walk=mode, temperature=T, walk_seed=0xABCDEF123))
+    res = _oracle_steps(inp)
+    cidx = torch.from_numpy(np.stack([r.cand_idx for r in res]).astype(np.int32)).cuda()
+    pair = torch.from_numpy(np.stack([r.pair for r in res]).astype(np.float32)).cuda()
+    path, scores = dfs_mod().walk(pair, cidx, mode, T, inp.walk_seed)
+    torch.cuda.synchronize()
+    path, scores = path.cpu().numpy(), scores.cpu().numpy()
+    for i, r in enumerate(res):
+        check_path(path[i], scores[i], r, mode, T, inp.walk_seed, int(inp.seq_ids[i]))
