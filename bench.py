@@ -23,6 +23,65 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft blocks/sec through dfs_select; top-16 HBM GB/s as % of peak"
 HBM_PEAK_GBS = 8000.0
+# Sources of the top-16 kernel; HBM traffic figures taken with rocprofv3 counters
+# are reported only while these files hash to the value recorded with them.
+TOPK_SOURCES = ["draft_selection_position_amd/csrc/topk.hip", "draft_selection_position_amd/csrc/dfs_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_throughput_traffic.txt")
+
+
+def topk_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in TOPK_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """(fetch+write bytes per top-16 launch, record) from the committed counter summary, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256_16") != topk_source_sha() or rec.get("workload") != workload:
+        return None
+    return float(rec["hbm_bytes_per_launch"]), rec
+
+
+def _kname(full: str) -> str:
+    return full.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def summarize_rocprof(d: str) -> None:
+    """Print per-kernel average durations and per-dispatch counters from a rocprofv3 csv directory."""
+    import csv
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"## kernel stats ({os.path.relpath(path, d)})")
+        print("| kernel | calls | avg us | min us | max us | % |")
+        print("|---|---|---|---|---|---|")
+        for r in csv.DictReader(open(path)):
+            name = _kname(r["Name"])
+            print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                  f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        agg = {}
+        for r in csv.DictReader(open(path)):
+            name = _kname(r["Kernel_Name"])
+            key = (name, r["Counter_Name"], r.get("Grid_Size", ""))
+            agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        print(f"## counters ({os.path.relpath(path, d)}), mean per dispatch")
+        print("| kernel | counter | grid | dispatches | mean value |")
+        print("|---|---|---|---|---|")
+        for (name, cn, g), v in sorted(agg.items()):
+            print(f"| {name} | {cn} | {g} | {len(v)} | {sum(v) / len(v):.1f} |")
 
 
 def _affinity() -> int:
@@ -85,7 +144,13 @@ def main() -> int:
     ap.add_argument("--workload", default="throughput")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU work of the baseline sample")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="also run device-to-device copies of this size (counter calibration)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the selector on a single GPU; --gpus must be 1 "
@@ -171,6 +236,16 @@ def main() -> int:
     idx3, val3 = idx.view(cfg.batch, cfg.L, 16), val.view(cfg.batch, cfg.L, 16)
     pair_ms = timed(lambda: dfs.pair_scores(idx3, val3, dev["prev_token"], g, dev["A"], dev["B"]))
 
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=logits2d.device).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = recorded_traffic(cfg.name)
     out = {
         "metric": METRIC,
         "value": blocks_per_s,
@@ -187,7 +262,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "batch": cfg.batch, "L": cfg.L, "V": cfg.V, "d": cfg.d, "k": 16,
                    "E": 256, "walk": cfg.walk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": topk_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": topk_gbs / HBM_PEAK_GBS, "traffic": None if traffic is None else traffic[0],
                      "kernel": "topk_chunk_kernel", "bytes_per_launch": topk_bytes, "avg_ms": topk_ms},
         "step_ms": {"topk": topk_ms, "gate": gate_ms, "pair_scores": pair_ms, "select": ms_per_step},
         "host_wall_s": wall,

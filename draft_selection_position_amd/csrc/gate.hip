@@ -28,42 +28,90 @@ constexpr int kTargetWG = 256;   // one workgroup per CU is enough for this smal
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// Wp[kb][n][kk] = W[kb*32 + kk][n], zero past d.
+// Wp[kb][n][kk] = W[kb*32 + kk][n], zero past d: one workgroup per 32-row slab of
+// W, read with 16-byte loads, transposed through LDS, written with 16-byte stores.
 __global__ __launch_bounds__(kThreads) void pack_w_kernel(const uint16_t* __restrict__ W,
                                                           int64_t d, uint16_t* __restrict__ Wp) {
-  const int n = threadIdx.x;
-  const int64_t kb = blockIdx.x >> 2;
-  const int g = blockIdx.x & 3;  // which 8 of the 32 k values
-  uint16_t v[8];
+  __shared__ uint16_t tile[kKB][kE + 8];  // +8: spread the column reads over banks
+  const int tid = threadIdx.x;
+  const int64_t kb = blockIdx.x;
+  {
+    const int kk = tid >> 3;         // 32 rows, 8 threads per row
+    const int n0 = (tid & 7) * 32;   // 32 columns per thread
+    const int64_t k = kb * kKB + kk;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t k = kb * kKB + g * 8 + i;
-    v[i] = k < d ? W[k * kE + n] : (uint16_t)0;
+    for (int c = 0; c < 4; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (k < d) v = *reinterpret_cast<const uint4*>(W + k * kE + n0 + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[kk][n0 + 8 * c + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+        tile[kk][n0 + 8 * c + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+      }
+    }
   }
-  uint4 o;
-  o.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-  o.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-  o.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-  o.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-  *reinterpret_cast<uint4*>(Wp + ((kb * kE + n) * kKB + g * 8)) = o;
+  __syncthreads();
+  const int n = tid;  // one output column (32 k values = 64 bytes) per thread
+  uint4* dst = reinterpret_cast<uint4*>(Wp + (kb * kE + n) * kKB);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[8 * c + 2 * e][n] | ((uint32_t)tile[8 * c + 2 * e + 1][n] << 16);
+    dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
+constexpr int kGemmThreads = 512;  // 4 column slices x 2 k parities
+
 template <int MT>
-__global__ __launch_bounds__(kThreads) void gate_mfma_kernel(const uint16_t* __restrict__ H,
-                                                             const uint16_t* __restrict__ Wp,
-                                                             int64_t rows, int64_t d,
-                                                             int64_t kchunk, int splits,
-                                                             float* __restrict__ partial,
-                                                             float* __restrict__ out) {
+struct GemmFrag {
+  uint4 a[MT];
+  uint4 b[4];
+};
+
+template <int MT>
+__device__ __forceinline__ void gemm_load(GemmFrag<MT>& f, const uint16_t* __restrict__ H,
+                                          const uint16_t* __restrict__ Wp, int64_t rows, int64_t d,
+                                          int64_t m0, int64_t kb, int nslice, int r, int q) {
+  const int64_t k = kb * kKB + 8 * q;  // this lane's 8 k values; d % 8 == 0
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t m = m0 + 16 * mt + r;
+    f.a[mt] = make_uint4(0u, 0u, 0u, 0u);
+    if (m < rows && k < d) f.a[mt] = *reinterpret_cast<const uint4*>(H + m * d + k);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n = 64 * nslice + 16 * nt + r;
+    f.b[nt] = *reinterpret_cast<const uint4*>(Wp + (kb * kE + n) * kKB + 8 * q);
+  }
+}
+
+// Z tile [16 MT rows x 256 columns] of one K split.  Wave w owns columns
+// [64 (w % 4), + 64) and the k steps of parity w / 4; the two parities are added
+// through LDS in a fixed order at the end.
+template <int MT>
+__global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t* __restrict__ H,
+                                                                 const uint16_t* __restrict__ Wp,
+                                                                 int64_t rows, int64_t d,
+                                                                 int64_t kchunk, int splits,
+                                                                 float* __restrict__ partial,
+                                                                 float* __restrict__ out) {
+  __shared__ float red[4][MT * 16][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  const int nslice = wave & 3;
+  const int par = wave >> 2;
   const int r = lane & 15;
   const int q = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16 * MT;
   const int s = blockIdx.y;
-  const int64_t kb0 = (int64_t)s * kchunk / kKB;
-  int64_t kb1 = ((int64_t)s + 1) * kchunk / kKB;
   const int64_t KB = (d + kKB - 1) / kKB;
+  const int64_t kb0 = (int64_t)s * (kchunk / kKB);
+  int64_t kb1 = kb0 + kchunk / kKB;
   if (kb1 > KB) kb1 = KB;
 
   f32x4 acc[MT][4];
@@ -72,30 +120,30 @@ __global__ __launch_bounds__(kThreads) void gate_mfma_kernel(const uint16_t* __r
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  for (int64_t kb = kb0; kb < kb1; ++kb) {
-    const int64_t k = kb * kKB + 8 * q;  // this lane's 8 k values; d % 8 == 0
-    uint4 a[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int64_t m = m0 + 16 * mt + r;
-      a[mt] = zero;
-      if (m < rows && k < d) a[mt] = *reinterpret_cast<const uint4*>(H + m * d + k);
-    }
-    uint4 b[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = 64 * wave + 16 * nt + r;
-      b[nt] = *reinterpret_cast<const uint4*>(Wp + (kb * kE + n) * kKB + 8 * q);
-    }
+  int64_t kb = kb0 + par;
+  GemmFrag<MT> cur, nxt;
+  if (kb < kb1) gemm_load<MT>(cur, H, Wp, rows, d, m0, kb, nslice, r, q);
+  for (; kb < kb1; kb += 2) {
+    if (kb + 2 < kb1) gemm_load<MT>(nxt, H, Wp, rows, d, m0, kb + 2, nslice, r, q);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a[mt]), __builtin_bit_cast(bf16x8, b[nt]), acc[mt][nt], 0, 0,
-            0);
+            __builtin_bit_cast(bf16x8, cur.a[mt]), __builtin_bit_cast(bf16x8, cur.b[nt]),
+            acc[mt][nt], 0, 0, 0);
+    cur = nxt;
   }
+  if (par == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[nslice][(mt * 4 + nt) * 4 + i][lane] = acc[mt][nt][i];
+  }
+  __syncthreads();
+  if (par == 1) return;
   // lane holds D[4q + i][r] of each 16x16 tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -103,13 +151,14 @@ __global__ __launch_bounds__(kThreads) void gate_mfma_kernel(const uint16_t* __r
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const float z = acc[mt][nt][i] + red[nslice][(mt * 4 + nt) * 4 + i][lane];
         const int64_t m = m0 + 16 * mt + 4 * q + i;
-        const int n = 64 * wave + 16 * nt + r;
+        const int n = 64 * nslice + 16 * nt + r;
         if (m < rows) {
           if (splits == 1) {
-            out[m * kE + n] = sigmoidf(acc[mt][nt][i]);
+            out[m * kE + n] = sigmoidf(z);
           } else {
-            partial[((int64_t)s * rows + m) * kE + n] = acc[mt][nt][i];
+            partial[((int64_t)s * rows + m) * kE + n] = z;
           }
         }
       }
@@ -208,16 +257,16 @@ hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, f
   if (p.bf16) {
     uint16_t* Wp = reinterpret_cast<uint16_t*>(wsb + p.packed_off);
     const int64_t KB = cdiv(p.d, kKB);
-    pack_w_kernel<<<dim3((unsigned)(KB * 4)), kThreads, 0, stream>>>(
+    pack_w_kernel<<<dim3((unsigned)KB), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(W_h), p.d, Wp);
     const uint16_t* H = static_cast<const uint16_t*>(hidden);
     if (p.row_tiles == 4) {
       const dim3 grid((unsigned)cdiv(p.rows, 64), (unsigned)p.splits);
-      gate_mfma_kernel<4><<<grid, kThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
+      gate_mfma_kernel<4><<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
                                                           partial, out_gate);
     } else {
       const dim3 grid((unsigned)cdiv(p.rows, 16), (unsigned)p.splits);
-      gate_mfma_kernel<1><<<grid, kThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
+      gate_mfma_kernel<1><<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
                                                           partial, out_gate);
     }
   } else {

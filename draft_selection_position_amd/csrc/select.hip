@@ -10,10 +10,13 @@
 //
 // Design (gfx950): one workgroup per sequence, one wave per block position.  A
 // position's 16x16 score tile is exactly one 16x16 output of the matrix cores with
-// K = 256.  The sum over the embedding index e is order-free, so lane group
-// q = lane / 16 takes e in [64q, 64q + 64): every lane then loads its predecessor
-// row and candidate row fragments as contiguous 16-byte vectors straight from
-// the tables, with no LDS staging.  For bf16 tables the gated predecessor
+// K = 256.  The sum over the embedding index e is order-free, so the k slots of
+// the MFMAs may be mapped to e freely, as long as both operands agree: MFMA step c
+// gives lane group q = lane / 16 the eight values e = 64 (c / 2) + 16 q + 8 (c % 2)
+// + 0..7.  Each lane then loads its predecessor-row and candidate-row fragments as
+// 16-byte vectors straight from the tables (no LDS staging), and the four lane
+// groups of a row cover one whole 128-byte line in two load instructions.  For
+// bf16 tables the gated predecessor
 // embedding A(a) * g (fp32) is split as hi + lo in bf16 and fed to two MFMAs, so
 // the products are exact to ~2^-17 before fp32 accumulation.  The tiles stay in
 // LDS and wave 0 walks them.
@@ -59,11 +62,12 @@ __device__ __forceinline__ double gumbel_noise(uint64_t seed, uint32_t b, uint32
 
 // The walk of one sequence over score tiles in LDS; run by one whole wave.
 __device__ __forceinline__ void walk_tiles(const float (*sS)[kK][kPad], const double (*sN)[kK],
-                                           const int32_t* __restrict__ cand_idx, int64_t b, int L,
-                                           int mode, double temperature,
-                                           int32_t* __restrict__ out_path,
+                                           const int32_t (*sC)[kK], int64_t b, int L, int mode,
+                                           double temperature, int32_t* __restrict__ out_path,
                                            float* __restrict__ out_scores, int lane) {
   int i = 0;  // predecessor slot; every row of position 0 is the verified token's row
+  int32_t my_tok = 0;
+  float my_score = 0.0f;
   for (int t = 0; t < L; ++t) {
     const float s = lane < kK ? sS[t][i][lane] : -INFINITY;
     int bj = lane;
@@ -91,12 +95,15 @@ __device__ __forceinline__ void walk_tiles(const float (*sS)[kK][kPad], const do
       }
     }
     const int j = uniform(__shfl(bj, 0));
-    if (lane == 0) {
-      const int64_t row = b * L + t;
-      out_path[row] = cand_idx[row * kK + j];
-      out_scores[row] = sS[t][i][j];
+    if (lane == t) {
+      my_tok = sC[t][j];
+      my_score = sS[t][i][j];
     }
     i = j;
+  }
+  if (lane < L) {
+    out_path[b * L + lane] = my_tok;
+    out_scores[b * L + lane] = my_score;
   }
 }
 
@@ -110,6 +117,7 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
     float* __restrict__ out_scores) {
   __shared__ float sS[kMaxL][kK][kPad];
   __shared__ double sN[kMaxL][kK];
+  __shared__ int32_t sC[kMaxL][kK];
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;  // block position of this wave
   const int64_t b = blockIdx.x;
@@ -124,23 +132,26 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
   pred = pred < 0 ? 0 : (pred >= V ? V - 1 : pred);
   cand = cand < 0 ? 0 : (cand >= V ? V - 1 : cand);
   const float u = cand_val[row * kK + r];
-  const float4* g4 = reinterpret_cast<const float4*>(gate + row * kE + 64 * q);
+  if (kWalk && lane < kK) sC[t][lane] = (int32_t)cand_idx[row * kK + lane];
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kBf16Tables) {
+    // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
     const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) +
-                                                       pred * kE + 64 * q);
+                                                       pred * kE + 16 * q);
     const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
-                                                       cand * kE + 64 * q);
+                                                       cand * kE + 16 * q);
+    const float4* g4 = reinterpret_cast<const float4*>(gate + row * kE + 16 * q);
     bf16x8 av[8], bv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      av[c] = Ap[c];
-      bv[c] = Bp[c];
+      av[c] = Ap[8 * (c >> 1) + (c & 1)];
+      bv[c] = Bp[8 * (c >> 1) + (c & 1)];
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float4 ga = g4[2 * c], gb = g4[2 * c + 1];
+      const int gi = 16 * (c >> 1) + 2 * (c & 1);  // float4 index of this fragment's gate values
+      const float4 ga = g4[gi], gb = g4[gi + 1];
       const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
       bf16x8 hi, lo;
 #pragma unroll
@@ -153,13 +164,17 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv[c], acc, 0, 0, 0);
     }
   } else {
+    // fp32 (one k slot per lane and step): step 4 c + s gives lane group q the value
+    // e = 16 c + 4 q + s, so a lane reads e = 16 c + 4 q + 0..3 as one float4 and
+    // feeds it to four consecutive steps (same mapping for A, gate and B).
     const float4* Ap = reinterpret_cast<const float4*>(static_cast<const float*>(A_) + pred * kE +
-                                                       64 * q);
+                                                       4 * q);
     const float4* Bp = reinterpret_cast<const float4*>(static_cast<const float*>(B_) + cand * kE +
-                                                       64 * q);
+                                                       4 * q);
+    const float4* gq = reinterpret_cast<const float4*>(gate + row * kE + 4 * q);
 #pragma unroll 4
     for (int c = 0; c < 16; ++c) {
-      const float4 a = Ap[c], bb = Bp[c], g = g4[c];
+      const float4 a = Ap[4 * c], bb = Bp[4 * c], g = gq[4 * c];
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
   if constexpr (kWalk) {
     if (mode == 1 && lane < kK) sN[t][lane] = gumbel_noise(seed, (uint32_t)b, (uint32_t)t, lane);
     __syncthreads();
-    if (t == 0) walk_tiles(sS, sN, cand_idx, b, L, mode, temperature, out_path, out_scores, lane);
+    if (t == 0) walk_tiles(sS, sN, sC, b, L, mode, temperature, out_path, out_scores, lane);
   }
 }
 
@@ -188,15 +203,17 @@ __global__ __launch_bounds__(kWave) void walk_kernel(const float* __restrict__ p
                                                      float* __restrict__ out_scores) {
   __shared__ float sS[kMaxL][kK][kPad];
   __shared__ double sN[kMaxL][kK];
+  __shared__ int32_t sC[kMaxL][kK];
   const int lane = threadIdx.x;
   const int64_t b = blockIdx.x;
   const float* src = pair + b * L * kK * kK;
   for (int e = lane; e < L * kK * kK; e += kWave) sS[e / (kK * kK)][(e / kK) % kK][e % kK] = src[e];
+  for (int e = lane; e < L * kK; e += kWave) sC[e / kK][e % kK] = cand_idx[b * L * kK + e];
   if (mode == 1)
     for (int e = lane; e < L * kK; e += kWave)
       sN[e / kK][e % kK] = gumbel_noise(seed, (uint32_t)b, (uint32_t)(e / kK), (uint32_t)(e % kK));
   __syncthreads();
-  walk_tiles(sS, sN, cand_idx, b, L, mode, temperature, out_path, out_scores, lane);
+  walk_tiles(sS, sN, sC, b, L, mode, temperature, out_path, out_scores, lane);
 }
 
 template <bool kBf16, bool kWritePair, bool kWalk>

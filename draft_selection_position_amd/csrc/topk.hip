@@ -6,8 +6,8 @@
 // ascending; -0 equals +0.
 //
 // Design (gfx950): the pass is HBM-bound, so each workgroup (4 waves) streams a
-// row chunk with 16-byte coalesced loads, four per thread in flight plus the
-// next iteration's four.  An element is only looked at further when it reaches
+// row chunk with 16-byte coalesced non-temporal loads, the next iteration's
+// vectors in flight while the current ones are scanned.  An element is only looked at further when it reaches
 // the wave's admission threshold; admitted elements are appended to a per-wave
 // LDS buffer as exact 64-bit (value, index) keys with one ballot per element
 // slot, and the buffer is merged into the wave's sorted top-16 (held in lanes
@@ -22,9 +22,27 @@
 namespace dfs {
 namespace {
 
+// Tuning knobs (compile-time); the defaults are the measured best on MI355X at
+// 4096 rows x 151936 bf16: two 16-byte vectors per thread per iteration (plus
+// the next two in flight), registers capped for 8 waves per SIMD (exactly two
+// rounds of workgroups, no ragged tail) and non-temporal loads, which keep the
+// streamed logits from displacing anything in the caches.
+#ifndef DFS_TOPK_UNROLL
+#define DFS_TOPK_UNROLL 2
+#endif
+#ifndef DFS_TOPK_WAVES_PER_EU
+#define DFS_TOPK_WAVES_PER_EU 8
+#endif
+#ifndef DFS_TOPK_NONTEMPORAL
+#define DFS_TOPK_NONTEMPORAL 1
+#endif
+#ifndef DFS_TOPK_TARGET_BLOCKS
+#define DFS_TOPK_TARGET_BLOCKS 2048
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 4;        // 16-byte vectors per thread per iteration
+constexpr int kUnroll = DFS_TOPK_UNROLL;  // 16-byte vectors per thread per iteration
 constexpr int kMergeAt = 64;      // merge once more keys than this are buffered
 constexpr int kCap = kMergeAt + 8 * kWave;  // room for one whole vector per lane on top
 constexpr int kMinChunk = 4096;   // elements; below this a split does not pay
@@ -88,6 +106,16 @@ __device__ __forceinline__ void append(WaveTop& w, bool adm, float v, uint32_t i
   w.cnt = uniform(w.cnt + __popcll(mask));
 }
 
+__device__ __forceinline__ uint4 load_vec(const uint4* p) {
+#if DFS_TOPK_NONTEMPORAL
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
 template <bool kBf16>
 __device__ __forceinline__ float load_scalar(const typename Elems<kBf16>::T* p, int64_t i) {
   if constexpr (kBf16) {
@@ -134,7 +162,7 @@ __device__ __forceinline__ void scan_vec(const uint4& d, uint32_t idx0, WaveTop&
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(const void* __restrict__ logits,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TOPK_WAVES_PER_EU))) void topk_chunk_kernel(const void* __restrict__ logits,
                                                               int64_t V, int parts, int64_t chunk,
                                                               uint64_t* __restrict__ partial,
                                                               int32_t* __restrict__ out_idx,
@@ -193,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(const void* __rest
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t vid = (int64_t)u * kThreads + tid;
     cur[u] = pad;
-    if (vid < nvec) cur[u] = vp[vid];
+    if (vid < nvec) cur[u] = load_vec(vp + vid);
   }
   for (int64_t it = 0; it < niter; ++it) {
     if (it + 1 < niter) {
@@ -201,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(const void* __rest
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t vid = (it + 1) * step + (int64_t)u * kThreads + tid;
         nxt[u] = pad;
-        if (vid < nvec) nxt[u] = vp[vid];
+        if (vid < nvec) nxt[u] = load_vec(vp + vid);
       }
     }
     {  // other waves may have raised the chunk's threshold
@@ -283,8 +311,8 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int esize) {
   p.esize = esize;
   const int64_t pv = 16 / esize;
   int64_t parts = 1;
-  if (rows < kTargetBlocks) {
-    parts = cdiv(kTargetBlocks, rows);
+  if (rows < DFS_TOPK_TARGET_BLOCKS) {
+    parts = cdiv(DFS_TOPK_TARGET_BLOCKS, rows);
     int64_t maxp = V / kMinChunk;
     if (maxp < 1) maxp = 1;
     if (parts > maxp) parts = maxp;
