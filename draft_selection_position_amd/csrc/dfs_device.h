@@ -35,6 +35,10 @@ __device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
 __device__ __forceinline__ float key_value(uint64_t k) { return unmono32((uint32_t)(k >> 32)); }
 
+// The context gate's nonlinearity; every kernel that applies it uses this one
+// definition, so the fused and unfused paths give identical bits.
+__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
+
 // ---------------------------------------------------------------- wave utilities
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 

@@ -24,9 +24,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kKB = 32;          // k per MFMA step
-constexpr int kTargetWG = 256;   // one workgroup per CU is enough for this small GEMM
-
-__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
+#ifndef DFS_GATE_TARGET_WG
+#define DFS_GATE_TARGET_WG 256
+#endif
+constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims for
 
 // Wp[kb][n][kk] = W[kb*32 + kk][n], zero past d: one workgroup per 32-row slab of
 // W, read with 16-byte loads, transposed through LDS, written with 16-byte stores.
@@ -64,101 +65,130 @@ __global__ __launch_bounds__(kThreads) void pack_w_kernel(const uint16_t* __rest
   }
 }
 
-constexpr int kGemmThreads = 512;  // 4 column slices x 2 k parities
+#ifndef DFS_GATE_DEPTH
+#define DFS_GATE_DEPTH 4
+#endif
+constexpr int kGemmThreads = 256;       // 4 waves, one per 64-column slice
+constexpr int kTileM = 64;              // rows per workgroup
+constexpr int kDepth = DFS_GATE_DEPTH;  // k steps in flight per thread (register ring)
+constexpr int kLdsPitch = kKB + 8;      // bf16 per LDS row (+16 bytes against bank conflicts)
 
-template <int MT>
-struct GemmFrag {
-  uint4 a[MT];
-  uint4 b[4];
-};
-
-template <int MT>
-__device__ __forceinline__ void gemm_load(GemmFrag<MT>& f, const uint16_t* __restrict__ H,
-                                          const uint16_t* __restrict__ Wp, int64_t rows, int64_t d,
-                                          int64_t m0, int64_t kb, int nslice, int r, int q) {
-  const int64_t k = kb * kKB + 8 * q;  // this lane's 8 k values; d % 8 == 0
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t m = m0 + 16 * mt + r;
-    f.a[mt] = make_uint4(0u, 0u, 0u, 0u);
-    if (m < rows && k < d) f.a[mt] = *reinterpret_cast<const uint4*>(H + m * d + k);
-  }
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = 64 * nslice + 16 * nt + r;
-    f.b[nt] = *reinterpret_cast<const uint4*>(Wp + (kb * kE + n) * kKB + 8 * q);
-  }
+// H piece of thread tid for k step kb: row m0 + tid / 4, k [32 kb + 8 (tid % 4), + 8).
+// Loads are never predicated (compiler-visible branches around loads make it wait
+// for every load in flight): a piece outside H is read from a clamped address and
+// zeroed when it is stored to LDS.
+__device__ __forceinline__ uint4 load_h_piece(const uint16_t* __restrict__ H, int64_t rows, int64_t d,
+                                              int64_t m0, int64_t kb, int tid) {
+  int64_t m = m0 + (tid >> 2);
+  int64_t k = kb * kKB + 8 * (tid & 3);  // d % 8 == 0: the 8 values are all in or all out
+  m = m < rows ? m : rows - 1;
+  k = k < d ? k : d - 8;
+  return *reinterpret_cast<const uint4*>(H + m * d + k);
 }
 
-// Z tile [16 MT rows x 256 columns] of one K split.  Wave w owns columns
-// [64 (w % 4), + 64) and the k steps of parity w / 4; the two parities are added
-// through LDS in a fixed order at the end.
-template <int MT>
+__device__ __forceinline__ bool h_piece_valid(int64_t rows, int64_t d, int64_t m0, int64_t kb,
+                                              int tid) {
+  return m0 + (tid >> 2) < rows && kb * kKB + 8 * (tid & 3) < d;
+}
+
+// W_h operand of lane (r, q) of wave w for k step kb and column tile nt: the packed
+// slab holds column n's 32 k values contiguously, so this is one 16-byte load in
+// MFMA operand order.
+__device__ __forceinline__ uint4 load_w_frag(const uint16_t* __restrict__ Wp, int64_t kb, int wave,
+                                             int nt, int r, int q) {
+  return *reinterpret_cast<const uint4*>(Wp + (kb * kE + 64 * wave + 16 * nt + r) * kKB + 8 * q);
+}
+
+// Z tile [64 rows x 256 columns] of one K split.  Wave w owns columns
+// [64 w, + 64) for all 64 rows.  Per k step, the workgroup's H tile (64 x 32,
+// needed by every wave) goes through one of two LDS buffers with one barrier;
+// each wave's W_h fragments (its own columns, needed by no other wave) go straight
+// from memory into registers.  Both are loaded kDepth k steps ahead of use.
 __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t* __restrict__ H,
                                                                  const uint16_t* __restrict__ Wp,
                                                                  int64_t rows, int64_t d,
                                                                  int64_t kchunk, int splits,
                                                                  float* __restrict__ partial,
                                                                  float* __restrict__ out) {
-  __shared__ float red[4][MT * 16][kWave];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int nslice = wave & 3;
-  const int par = wave >> 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kLdsPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int r = lane & 15;
   const int q = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 16 * MT;
-  const int s = blockIdx.y;
+  // Workgroup id -> (K split, row tile) with the split fastest: workgroups are
+  // dealt to the 8 XCDs round-robin, so with splits dividing 8 each XCD's L2 only
+  // ever holds one K slice of the packed W_h.
+  const int s = (int)(blockIdx.x % (unsigned)splits);
+  const int64_t m0 = (int64_t)(blockIdx.x / (unsigned)splits) * kTileM;
   const int64_t KB = (d + kKB - 1) / kKB;
   const int64_t kb0 = (int64_t)s * (kchunk / kKB);
   int64_t kb1 = kb0 + kchunk / kKB;
   if (kb1 > KB) kb1 = KB;
 
-  f32x4 acc[MT][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int64_t kb = kb0 + par;
-  GemmFrag<MT> cur, nxt;
-  if (kb < kb1) gemm_load<MT>(cur, H, Wp, rows, d, m0, kb, nslice, r, q);
-  for (; kb < kb1; kb += 2) {
-    if (kb + 2 < kb1) gemm_load<MT>(nxt, H, Wp, rows, d, m0, kb + 2, nslice, r, q);
+  // register ring of kDepth k steps: H piece and the four W_h fragments
+  uint4 ra[kDepth], rb0[kDepth], rb1[kDepth], rb2[kDepth], rb3[kDepth];
+  auto fill = [&](int j, int64_t kb) {
+    ra[j] = load_h_piece(H, rows, d, m0, kb, tid);
+    rb0[j] = load_w_frag(Wp, kb, wave, 0, r, q);
+    rb1[j] = load_w_frag(Wp, kb, wave, 1, r, q);
+    rb2[j] = load_w_frag(Wp, kb, wave, 2, r, q);
+    rb3[j] = load_w_frag(Wp, kb, wave, 3, r, q);
+  };
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int j = 0; j < kDepth; ++j) fill(j, kb0 + j < kb1 ? kb0 + j : kb1 - 1);
+
+  auto step = [&](int64_t kb, uint4 a, uint4 b0, uint4 b1, uint4 b2, uint4 b3) {
+    const int st = (int)((kb - kb0) & 1);
+    const uint32_t keep = h_piece_valid(rows, d, m0, kb, tid) ? 0xffffffffu : 0u;
+    *reinterpret_cast<uint4*>(&sA[st][tid >> 2][8 * (tid & 3)]) =
+        make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep);
+    __syncthreads();
+    const bf16x8 bfr[4] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1),
+                           __builtin_bit_cast(bf16x8, b2), __builtin_bit_cast(bf16x8, b3)};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sA[st][16 * mt + r][8 * q]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, cur.a[mt]), __builtin_bit_cast(bf16x8, cur.b[nt]),
-            acc[mt][nt], 0, 0, 0);
-    cur = nxt;
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  // Full batches of kDepth steps, branch-free: each slot is consumed, then refilled
+  // with the step kDepth ahead (past the end: a harmless reload of the last step).
+  int64_t base = kb0;
+  for (; base + kDepth <= kb1; base += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      step(base + j, ra[j], rb0[j], rb1[j], rb2[j], rb3[j]);
+      fill(j, base + j + kDepth < kb1 ? base + j + kDepth : kb1 - 1);
+    }
   }
-  if (par == 1) {
+  // The last (kb1 - base) < kDepth steps are already in slots 0, 1, ...
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[nslice][(mt * 4 + nt) * 4 + i][lane] = acc[mt][nt][i];
-  }
-  __syncthreads();
-  if (par == 1) return;
+  for (int j = 0; j < kDepth; ++j)
+    if (base + j < kb1) step(base + j, ra[j], rb0[j], rb1[j], rb2[j], rb3[j]);
+
   // lane holds D[4q + i][r] of each 16x16 tile
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float z = acc[mt][nt][i] + red[nslice][(mt * 4 + nt) * 4 + i][lane];
         const int64_t m = m0 + 16 * mt + 4 * q + i;
-        const int n = 64 * nslice + 16 * nt + r;
+        const int n = 64 * wave + 16 * nt + r;
         if (m < rows) {
           if (splits == 1) {
-            out[m * kE + n] = sigmoidf(z);
+            out[m * kE + n] = sigmoidf(acc[mt][nt][i]);
           } else {
-            partial[((int64_t)s * rows + m) * kE + n] = z;
+            partial[((int64_t)s * rows + m) * kE + n] = acc[mt][nt][i];
           }
         }
       }
@@ -199,14 +229,25 @@ __global__ __launch_bounds__(kThreads) void gate_f32_kernel(const float* __restr
   }
 }
 
-// out[m, n] = sigmoid(sum over splits, in split order).
+// out[m, n] = sigmoid(sum over splits, in split order).  The loads are issued
+// eight at a time ahead of the (ordered) additions.
 __global__ __launch_bounds__(kThreads) void gate_finish_kernel(const float* __restrict__ partial,
                                                                int64_t rows, int splits,
                                                                float* __restrict__ out) {
   const int64_t m = blockIdx.x;
   const int n = threadIdx.x;
+  const float* p = partial + m * kE + n;
+  const int64_t stride = rows * kE;
   float z = 0.0f;
-  for (int s = 0; s < splits; ++s) z += partial[((int64_t)s * rows + m) * kE + n];
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(s + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) z += v[u];
+  }
+  for (; s < splits; ++s) z += p[(int64_t)s * stride];
   out[m * kE + n] = sigmoidf(z);
 }
 
@@ -219,8 +260,8 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   p.bf16 = bf16;
   size_t off = 0;
   if (bf16) {
-    p.row_tiles = rows >= 2048 ? 4 : 1;
-    const int64_t mtiles = cdiv(rows, 16 * p.row_tiles);
+    p.row_tiles = kTileM / 16;
+    const int64_t mtiles = cdiv(rows, kTileM);
     const int64_t KB = cdiv(d, kKB);
     int64_t splits = cdiv(kTargetWG, mtiles);
     const int64_t max_splits = KB / 2 > 1 ? KB / 2 : 1;  // at least two k steps per split
@@ -260,15 +301,9 @@ hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, f
     pack_w_kernel<<<dim3((unsigned)KB), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(W_h), p.d, Wp);
     const uint16_t* H = static_cast<const uint16_t*>(hidden);
-    if (p.row_tiles == 4) {
-      const dim3 grid((unsigned)cdiv(p.rows, 64), (unsigned)p.splits);
-      gate_mfma_kernel<4><<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
-                                                          partial, out_gate);
-    } else {
-      const dim3 grid((unsigned)cdiv(p.rows, 16), (unsigned)p.splits);
-      gate_mfma_kernel<1><<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
-                                                          partial, out_gate);
-    }
+    const dim3 grid((unsigned)(cdiv(p.rows, kTileM) * p.splits));
+    gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
+                                                         partial, out_gate);
   } else {
     const dim3 grid((unsigned)cdiv(p.rows, kF32Rows), (unsigned)p.splits);
     gate_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(hidden),

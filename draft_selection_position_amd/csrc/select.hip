@@ -30,7 +30,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxL = 16;
-constexpr int kPad = kK + 1;  // LDS row pitch of a score tile
 
 // ---------------------------------------------------------------- Philox4x32-10
 // Counter-based generator of Salmon, Moraes, Dror and Shaw (SC'11): ten rounds
@@ -60,50 +59,63 @@ __device__ __forceinline__ double gumbel_noise(uint64_t seed, uint32_t b, uint32
   return -log(-log(u));
 }
 
-// The walk of one sequence over score tiles in LDS; run by one whole wave.
-__device__ __forceinline__ void walk_tiles(const float (*sS)[kK][kPad], const double (*sN)[kK],
+// The walk of one sequence over score tiles in LDS.  It is a chain of L dependent
+// 16-way argmaxes, so one lane runs it: each step reads the predecessor's row of
+// 16 scores from LDS and keeps the first maximum (lowest slot on ties).
+__device__ __forceinline__ void walk_tiles(const float (*sS)[kK][kK], const double (*sN)[kK],
                                            const int32_t (*sC)[kK], int64_t b, int L, int mode,
                                            double temperature, int32_t* __restrict__ out_path,
                                            float* __restrict__ out_scores, int lane) {
+  if (lane != 0) return;
   int i = 0;  // predecessor slot; every row of position 0 is the verified token's row
-  int32_t my_tok = 0;
-  float my_score = 0.0f;
   for (int t = 0; t < L; ++t) {
-    const float s = lane < kK ? sS[t][i][lane] : -INFINITY;
-    int bj = lane;
+    const float4* rp = reinterpret_cast<const float4*>(sS[t][i]);
+    float row[kK];
+#pragma unroll
+    for (int c = 0; c < kK / 4; ++c) {
+      const float4 v = rp[c];
+      row[4 * c] = v.x;
+      row[4 * c + 1] = v.y;
+      row[4 * c + 2] = v.z;
+      row[4 * c + 3] = v.w;
+    }
+    int j = 0;
     if (mode == 0) {
-      float bv = s;
+      float best = row[0];
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov > bv || (ov == bv && oj < bj)) {
-          bv = ov;
-          bj = oj;
+      for (int c = 1; c < kK; ++c)
+        if (row[c] > best) {
+          best = row[c];
+          j = c;
         }
-      }
     } else {
-      double bv = lane < kK ? (double)s / temperature + sN[t][lane] : -INFINITY;
+      double best = (double)row[0] / temperature + sN[t][0];
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        const double ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov > bv || (ov == bv && oj < bj)) {
-          bv = ov;
-          bj = oj;
+      for (int c = 1; c < kK; ++c) {
+        const double v = (double)row[c] / temperature + sN[t][c];
+        if (v > best) {
+          best = v;
+          j = c;
         }
       }
     }
-    const int j = uniform(__shfl(bj, 0));
-    if (lane == t) {
-      my_tok = sC[t][j];
-      my_score = sS[t][i][j];
-    }
+    out_path[b * L + t] = sC[t][j];
+    out_scores[b * L + t] = row[j];
     i = j;
   }
-  if (lane < L) {
-    out_path[b * L + lane] = my_tok;
-    out_scores[b * L + lane] = my_score;
+}
+
+// Gate values g[row, e0 .. e0 + N) of the finished gate [rows, 256].
+template <int N>
+__device__ __forceinline__ void load_gate(const float* __restrict__ gate, int64_t row, int e0,
+                                          float* g) {
+#pragma unroll
+  for (int c = 0; c < N / 4; ++c) {
+    const float4 v = *reinterpret_cast<const float4*>(gate + row * kE + e0 + 4 * c);
+    g[4 * c] = v.x;
+    g[4 * c + 1] = v.y;
+    g[4 * c + 2] = v.z;
+    g[4 * c + 3] = v.w;
   }
 }
 
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
     float* __restrict__ out_pair,
     int mode, double temperature, uint64_t seed, int32_t* __restrict__ out_path,
     float* __restrict__ out_scores) {
-  __shared__ float sS[kMaxL][kK][kPad];
+  __shared__ float sS[kMaxL][kK][kK];
   __shared__ double sN[kMaxL][kK];
   __shared__ int32_t sC[kMaxL][kK];
   const int lane = threadIdx.x & (kWave - 1);
@@ -141,7 +153,6 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
                                                        pred * kE + 16 * q);
     const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
                                                        cand * kE + 16 * q);
-    const float4* g4 = reinterpret_cast<const float4*>(gate + row * kE + 16 * q);
     bf16x8 av[8], bv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -150,9 +161,8 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int gi = 16 * (c >> 1) + 2 * (c & 1);  // float4 index of this fragment's gate values
-      const float4 ga = g4[gi], gb = g4[gi + 1];
-      const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      float g[8];
+      load_gate<8>(gate, row, 64 * (c >> 1) + 16 * q + 8 * (c & 1), g);
       bf16x8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -171,10 +181,12 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
                                                        4 * q);
     const float4* Bp = reinterpret_cast<const float4*>(static_cast<const float*>(B_) + cand * kE +
                                                        4 * q);
-    const float4* gq = reinterpret_cast<const float4*>(gate + row * kE + 4 * q);
 #pragma unroll 4
     for (int c = 0; c < 16; ++c) {
-      const float4 a = Ap[4 * c], bb = Bp[4 * c], g = gq[4 * c];
+      const float4 a = Ap[4 * c], bb = Bp[4 * c];
+      float gv[4];
+      load_gate<4>(gate, row, 16 * c + 4 * q, gv);
+      const float4 g = make_float4(gv[0], gv[1], gv[2], gv[3]);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(kWave) void walk_kernel(const float* __restrict__ p
                                                      int mode, double temperature, uint64_t seed,
                                                      int32_t* __restrict__ out_path,
                                                      float* __restrict__ out_scores) {
-  __shared__ float sS[kMaxL][kK][kPad];
+  __shared__ float sS[kMaxL][kK][kK];
   __shared__ double sN[kMaxL][kK];
   __shared__ int32_t sC[kMaxL][kK];
   const int lane = threadIdx.x;

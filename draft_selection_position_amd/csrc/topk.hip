@@ -126,13 +126,16 @@ __device__ __forceinline__ float load_scalar(const typename Elems<kBf16>::T* p, 
 }
 
 // Admission test and append for one 16-byte vector (8 bf16 or 4 fp32 values),
-// then a merge if the buffer has filled past kMergeAt.  On a wave's first vector
-// (`seed`), the threshold is first raised to the 16th largest lane maximum: those
-// 16 maxima are distinct elements, so nothing below it can make the top 16.
+// then a merge if the buffer has filled past kMergeAt.  A vector past the end of
+// the chunk (`valid` false) is replaced by NaNs, which never pass.  On a wave's
+// first vector (`seed`), the threshold is first raised to the 16th largest lane
+// maximum: those 16 maxima are distinct elements, so nothing below it can make
+// the top 16.
 template <bool kBf16>
-__device__ __forceinline__ void scan_vec(const uint4& d, uint32_t idx0, WaveTop& w, uint64_t* buf,
-                                         uint32_t* s_thr, int lane, bool seed) {
+__device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, WaveTop& w,
+                                         uint64_t* buf, uint32_t* s_thr, int lane, bool seed) {
   constexpr int PV = Elems<kBf16>::per_vec;
+  if (!valid) d = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
   float v[PV];
   if constexpr (kBf16) {
     v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
@@ -212,42 +215,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
     append(w, i >= 0 && v >= w.thr, v, (uint32_t)i, buf);  // at most 14 keys
   }
 
+  // Main loop.  Every iteration issues the next iteration's loads before scanning
+  // the current vectors; the loads are unconditional (indices past the end are
+  // clamped to the last vector and flagged invalid) and the two register buffers
+  // alternate (no copies), so the compiler waits for exactly the vectors it is
+  // about to scan and leaves the next ones in flight.
   const uint4* vp = reinterpret_cast<const uint4*>(rowp + vb);
   const int64_t step = (int64_t)kThreads * kUnroll;
   const int64_t niter = (nvec + step - 1) / step;
-  const uint4 pad = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);  // NaN
-  uint4 cur[kUnroll], nxt[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t vid = (int64_t)u * kThreads + tid;
-    cur[u] = pad;
-    if (vid < nvec) cur[u] = load_vec(vp + vid);
-  }
-  for (int64_t it = 0; it < niter; ++it) {
-    if (it + 1 < niter) {
+  if (niter > 0) {
+    const int64_t last = nvec - 1;
+    uint4 bufA[kUnroll], bufB[kUnroll];
+    auto load_iter = [&](uint4* dst, int64_t it) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int64_t vid = (it + 1) * step + (int64_t)u * kThreads + tid;
-        nxt[u] = pad;
-        if (vid < nvec) nxt[u] = load_vec(vp + vid);
+        const int64_t vid = it * step + (int64_t)u * kThreads + tid;
+        dst[u] = load_vec(vp + (vid < nvec ? vid : last));
       }
-    }
-    {  // other waves may have raised the chunk's threshold
-      const uint32_t m = uniform(
-          (int)__hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-      if (m != 0u) {
-        const float t = unmono32(m);
-        if (t > w.thr) w.thr = uniformf(t);
+    };
+    auto scan_iter = [&](const uint4* src, int64_t it) {
+      {  // other waves may have raised the chunk's threshold
+        const uint32_t m = uniform(
+            (int)__hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (m != 0u) {
+          const float t = unmono32(m);
+          if (t > w.thr) w.thr = uniformf(t);
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t vid = it * step + (int64_t)u * kThreads + tid;
-      scan_vec<kBf16>(cur[u], (uint32_t)(vb + vid * PV), w, buf, &s_thr, lane,
-                      it == 0 && u == 0);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t vid = it * step + (int64_t)u * kThreads + tid;
+        scan_vec<kBf16>(src[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, &s_thr, lane,
+                        it == 0 && u == 0);
+      }
+    };
+    load_iter(bufA, 0);
+    int64_t it = 0;
+    for (; it + 2 <= niter; it += 2) {  // no exit in the middle: exact load waits
+      load_iter(bufB, it + 1);
+      scan_iter(bufA, it);
+      load_iter(bufA, it + 2);
+      scan_iter(bufB, it + 1);
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+    if (it < niter) scan_iter(bufA, it);  // odd count: bufA holds the last iteration
   }
 
   if (w.cnt > 0) wave_merge(w, buf, &s_thr, lane);
