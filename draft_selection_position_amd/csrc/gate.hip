@@ -68,18 +68,19 @@ __global__ __launch_bounds__(kThreads) void pack_w_kernel(const uint16_t* __rest
 #ifndef DFS_GATE_DEPTH
 #define DFS_GATE_DEPTH 4
 #endif
-constexpr int kGemmThreads = 256;       // 4 waves, one per 64-column slice
+constexpr int kGemmThreads = 512;       // 8 waves, one per 32-column slice
 constexpr int kTileM = 64;              // rows per workgroup
 constexpr int kDepth = DFS_GATE_DEPTH;  // k steps in flight per thread (register ring)
-constexpr int kLdsPitch = kKB + 8;      // bf16 per LDS row (+16 bytes against bank conflicts)
+constexpr int kLdsPitch = kKB + 8;      // bf16 per LDS row of the H tile (+16 bytes)
+constexpr int kOutPitch = kE + 4;       // fp32 per LDS row of the output tile
 
-// H piece of thread tid for k step kb: row m0 + tid / 4, k [32 kb + 8 (tid % 4), + 8).
+// H piece of thread tid (< 256) for k step kb: row m0 + tid / 4, k [32 kb + 8 (tid % 4), + 8).
 // Loads are never predicated (compiler-visible branches around loads make it wait
 // for every load in flight): a piece outside H is read from a clamped address and
 // zeroed when it is stored to LDS.
 __device__ __forceinline__ uint4 load_h_piece(const uint16_t* __restrict__ H, int64_t rows, int64_t d,
                                               int64_t m0, int64_t kb, int tid) {
-  int64_t m = m0 + (tid >> 2);
+  int64_t m = m0 + ((tid & 255) >> 2);
   int64_t k = kb * kKB + 8 * (tid & 3);  // d % 8 == 0: the 8 values are all in or all out
   m = m < rows ? m : rows - 1;
   k = k < d ? k : d - 8;
@@ -88,22 +89,23 @@ __device__ __forceinline__ uint4 load_h_piece(const uint16_t* __restrict__ H, in
 
 __device__ __forceinline__ bool h_piece_valid(int64_t rows, int64_t d, int64_t m0, int64_t kb,
                                               int tid) {
-  return m0 + (tid >> 2) < rows && kb * kKB + 8 * (tid & 3) < d;
+  return m0 + ((tid & 255) >> 2) < rows && kb * kKB + 8 * (tid & 3) < d;
 }
 
-// W_h operand of lane (r, q) of wave w for k step kb and column tile nt: the packed
+// W_h operand of lane (r, q) for k step kb and output column n: the packed
 // slab holds column n's 32 k values contiguously, so this is one 16-byte load in
 // MFMA operand order.
-__device__ __forceinline__ uint4 load_w_frag(const uint16_t* __restrict__ Wp, int64_t kb, int wave,
-                                             int nt, int r, int q) {
-  return *reinterpret_cast<const uint4*>(Wp + (kb * kE + 64 * wave + 16 * nt + r) * kKB + 8 * q);
+__device__ __forceinline__ uint4 load_w_frag(const uint16_t* __restrict__ Wp, int64_t kb, int n,
+                                             int q) {
+  return *reinterpret_cast<const uint4*>(Wp + (kb * kE + n) * kKB + 8 * q);
 }
 
 // Z tile [64 rows x 256 columns] of one K split.  Wave w owns columns
-// [64 w, + 64) for all 64 rows.  Per k step, the workgroup's H tile (64 x 32,
-// needed by every wave) goes through one of two LDS buffers with one barrier;
-// each wave's W_h fragments (its own columns, needed by no other wave) go straight
-// from memory into registers.  Both are loaded kDepth k steps ahead of use.
+// [32 w, + 32) of all 64 rows: 8 MFMA tiles.  Per k step the H tile (64 x 32,
+// shared by all waves) goes through one of two LDS buffers with one barrier, and
+// each wave's W_h fragments (its own columns, fetched by no other wave) go straight
+// from memory to registers; both are loaded kDepth steps ahead of use.  The result is transposed through
+// LDS so that every row is stored as contiguous 16-byte pieces.
 __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t* __restrict__ H,
                                                                  const uint16_t* __restrict__ Wp,
                                                                  int64_t rows, int64_t d,
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
                                                                  float* __restrict__ partial,
                                                                  float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kLdsPitch];
+  __shared__ __attribute__((aligned(16))) float sOut[kTileM][kOutPitch];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -126,37 +129,37 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
   int64_t kb1 = kb0 + kchunk / kKB;
   if (kb1 > KB) kb1 = KB;
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // register ring of kDepth k steps: H piece and the four W_h fragments
-  uint4 ra[kDepth], rb0[kDepth], rb1[kDepth], rb2[kDepth], rb3[kDepth];
+  // register ring of kDepth k steps: H piece (threads < 256) and two W_h fragments
+  uint4 ra[kDepth], rb0[kDepth], rb1[kDepth];
+  const int nb = 32 * wave + r;
   auto fill = [&](int j, int64_t kb) {
     ra[j] = load_h_piece(H, rows, d, m0, kb, tid);
-    rb0[j] = load_w_frag(Wp, kb, wave, 0, r, q);
-    rb1[j] = load_w_frag(Wp, kb, wave, 1, r, q);
-    rb2[j] = load_w_frag(Wp, kb, wave, 2, r, q);
-    rb3[j] = load_w_frag(Wp, kb, wave, 3, r, q);
+    rb0[j] = load_w_frag(Wp, kb, nb, q);
+    rb1[j] = load_w_frag(Wp, kb, nb + 16, q);
   };
 #pragma unroll
   for (int j = 0; j < kDepth; ++j) fill(j, kb0 + j < kb1 ? kb0 + j : kb1 - 1);
 
-  auto step = [&](int64_t kb, uint4 a, uint4 b0, uint4 b1, uint4 b2, uint4 b3) {
+  auto step = [&](int64_t kb, uint4 a, uint4 b0, uint4 b1) {
     const int st = (int)((kb - kb0) & 1);
-    const uint32_t keep = h_piece_valid(rows, d, m0, kb, tid) ? 0xffffffffu : 0u;
-    *reinterpret_cast<uint4*>(&sA[st][tid >> 2][8 * (tid & 3)]) =
-        make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep);
+    if (tid < 256) {
+      const uint32_t keep = h_piece_valid(rows, d, m0, kb, tid) ? 0xffffffffu : 0u;
+      *reinterpret_cast<uint4*>(&sA[st][tid >> 2][8 * (tid & 3)]) =
+          make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep);
+    }
     __syncthreads();
-    const bf16x8 bfr[4] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1),
-                           __builtin_bit_cast(bf16x8, b2), __builtin_bit_cast(bf16x8, b3)};
+    const bf16x8 bfr[2] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1)};
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sA[st][16 * mt + r][8 * q]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[nt], acc[mt][nt], 0, 0, 0);
     }
   };
@@ -166,32 +169,38 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
   for (; base + kDepth <= kb1; base += kDepth) {
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) {
-      step(base + j, ra[j], rb0[j], rb1[j], rb2[j], rb3[j]);
+      step(base + j, ra[j], rb0[j], rb1[j]);
       fill(j, base + j + kDepth < kb1 ? base + j + kDepth : kb1 - 1);
     }
   }
   // The last (kb1 - base) < kDepth steps are already in slots 0, 1, ...
 #pragma unroll
   for (int j = 0; j < kDepth; ++j)
-    if (base + j < kb1) step(base + j, ra[j], rb0[j], rb1[j], rb2[j], rb3[j]);
+    if (base + j < kb1) step(base + j, ra[j], rb0[j], rb1[j]);
 
-  // lane holds D[4q + i][r] of each 16x16 tile
+  // lane holds D[4q + i][r] of each 16x16 tile -> LDS, then row-contiguous stores
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + 16 * mt + 4 * q + i;
-        const int n = 64 * wave + 16 * nt + r;
-        if (m < rows) {
-          if (splits == 1) {
-            out[m * kE + n] = sigmoidf(acc[mt][nt][i]);
-          } else {
-            partial[((int64_t)s * rows + m) * kE + n] = acc[mt][nt][i];
-          }
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        sOut[16 * mt + 4 * q + i][32 * wave + 16 * nt + r] = acc[mt][nt][i];
+  __syncthreads();
+  // 64 rows x 64 float4: thread t stores float4 (t % 64) of rows t / 64, + 8, ...
+  const int c4 = tid & 63;
+#pragma unroll
+  for (int rr = tid >> 6; rr < kTileM; rr += kGemmThreads / 64) {
+    const int64_t m = m0 + rr;
+    if (m >= rows) break;
+    float4 v = *reinterpret_cast<const float4*>(&sOut[rr][4 * c4]);
+    if (splits == 1) {
+      v = make_float4(sigmoidf(v.x), sigmoidf(v.y), sigmoidf(v.z), sigmoidf(v.w));
+      *reinterpret_cast<float4*>(out + m * kE + 4 * c4) = v;
+    } else {
+      *reinterpret_cast<float4*>(partial + ((int64_t)s * rows + m) * kE + 4 * c4) = v;
+    }
+  }
 }
 
 constexpr int kF32Rows = 8;
