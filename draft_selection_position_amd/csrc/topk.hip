@@ -23,12 +23,12 @@ namespace dfs {
 namespace {
 
 // Tuning knobs (compile-time); the defaults are the measured best on MI355X at
-// 4096 rows x 151936 bf16: two 16-byte vectors per thread per iteration (plus
+// 4096 rows x 151936 bf16: three 16-byte vectors per thread per iteration (plus
 // the next two in flight), registers capped for 8 waves per SIMD (exactly two
 // rounds of workgroups, no ragged tail) and non-temporal loads, which keep the
 // streamed logits from displacing anything in the caches.
 #ifndef DFS_TOPK_UNROLL
-#define DFS_TOPK_UNROLL 2
+#define DFS_TOPK_UNROLL 3
 #endif
 #ifndef DFS_TOPK_WAVES_PER_EU
 #define DFS_TOPK_WAVES_PER_EU 8
@@ -106,14 +106,17 @@ __device__ __forceinline__ void append(WaveTop& w, bool adm, float v, uint32_t i
   w.cnt = uniform(w.cnt + __popcll(mask));
 }
 
-__device__ __forceinline__ uint4 load_vec(const uint4* p) {
-#if DFS_TOPK_NONTEMPORAL
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// 16-byte loads of the chunk's aligned middle go through a buffer resource (base
+// and size in scalar registers, 32-bit byte offset per lane): fewer per-lane
+// registers than 64-bit pointers, and the hardware range check returns zeros
+// instead of touching memory past the end (those vectors are flagged invalid).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer
+constexpr int kCacheNonTemporal = 2;         // "nt": stream through, do not keep
+__device__ __forceinline__ uint4 load_vec(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0,
+                                                        DFS_TOPK_NONTEMPORAL ? kCacheNonTemporal : 0);
   return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *p;
-#endif
 }
 
 template <bool kBf16>
@@ -216,21 +219,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
   }
 
   // Main loop.  Every iteration issues the next iteration's loads before scanning
-  // the current vectors; the loads are unconditional (indices past the end are
-  // clamped to the last vector and flagged invalid) and the two register buffers
-  // alternate (no copies), so the compiler waits for exactly the vectors it is
-  // about to scan and leaves the next ones in flight.
-  const uint4* vp = reinterpret_cast<const uint4*>(rowp + vb);
+  // the current vectors; the loads are unconditional (vectors past the end come
+  // back as zeros and are flagged invalid) and the two register buffers alternate
+  // (no copies), so the compiler waits for exactly the vectors it is about to scan
+  // and leaves the next ones in flight.
   const int64_t step = (int64_t)kThreads * kUnroll;
   const int64_t niter = (nvec + step - 1) / step;
   if (niter > 0) {
-    const int64_t last = nvec - 1;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(rowp + vb), (short)0, (int)(nvec * 16), kRawBufferWord3);
     uint4 bufA[kUnroll], bufB[kUnroll];
     auto load_iter = [&](uint4* dst, int64_t it) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int64_t vid = it * step + (int64_t)u * kThreads + tid;
-        dst[u] = load_vec(vp + (vid < nvec ? vid : last));
+        const uint32_t vid = (uint32_t)(it * step) + (uint32_t)(u * kThreads + tid);
+        dst[u] = load_vec(rsrc, vid * 16u);  // past the end: zeros, flagged invalid below
       }
     };
     auto scan_iter = [&](const uint4* src, int64_t it) {
