@@ -98,3 +98,21 @@ def test_select_is_deterministic(full_workload):
         again = _select(dev, inp.config)
         np.testing.assert_array_equal(first[0], again[0])
         np.testing.assert_array_equal(first[1], again[1])
+
+
+@pytest.mark.parametrize("name", ["small_batch", "sampled"])
+def test_select_equals_step_chain_two_streams(name, full_workload):
+    # >= 64 MiB of logits: dfs_select runs the gate on its second stream
+    import draft_selection_position_amd as dfs
+
+    inp, dev = full_workload(name)
+    cfg = inp.config
+    assert dev["logits"].numel() * dev["logits"].element_size() >= 64 << 20
+    path, scores = _select(dev, cfg)
+    idx, val = dfs.topk(dev["logits"])
+    g = dfs.gate(dev["hidden"], dev["W_h"])
+    pair = dfs.pair_scores(idx, val, dev["prev_token"], g, dev["A"], dev["B"])
+    p2, s2 = dfs.walk(pair, idx, cfg.walk, cfg.temperature, cfg.walk_seed)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(path, p2.cpu().numpy())
+    np.testing.assert_array_equal(scores, s2.cpu().numpy())
