@@ -147,6 +147,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run device-to-device copies of this size (counter calibration)")
     ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time dfs_select replayed from a captured HIP graph (one launch per step)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
@@ -236,6 +238,32 @@ def main() -> int:
     idx3, val3 = idx.view(cfg.batch, cfg.L, 16), val.view(cfg.batch, cfg.L, 16)
     pair_ms = timed(lambda: dfs.pair_scores(idx3, val3, dev["prev_token"], g, dev["A"], dev["B"]))
 
+    graph_ms = None
+    if args.graph:
+        # One dfs_select captured into a graph on a side stream, then replayed: the
+        # host submits one graph launch per step instead of the individual kernels.
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            for _ in range(3):
+                call()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+        if not torch.equal(sel.path.cpu(), torch.from_numpy(path)):
+            raise RuntimeError("graph replay gave a different path than eager dfs_select")
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device=logits2d.device).fill_(1)
@@ -267,6 +295,8 @@ def main() -> int:
         "step_ms": {"topk": topk_ms, "gate": gate_ms, "pair_scores": pair_ms, "select": ms_per_step},
         "host_wall_s": wall,
     }
+    if graph_ms is not None:
+        out["graph_replay"] = {"ms_per_step": graph_ms, "value": cfg.batch / (graph_ms * 1e-3)}
     if cpu is not None:
         paths = cpu.pop("_paths")
         mism = near = 0

@@ -294,18 +294,44 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, prev_token: torch.Tensor,
 
 
 class Selector:
-    """Fixed-shape selector with its own workspace and output buffers (no per-call allocation)."""
+    """Fixed-shape selector with its own workspace and output buffers (no per-call allocation).
+
+    Tensor shapes, dtypes and devices are checked against the construction-time
+    shape on every call, but with one tuple comparison each; the call then goes
+    straight to dfs_select.  The path and scores buffers are reused by every call.
+    """
 
     def __init__(self, batch: int, L: int, V: int, d: int, device="cuda", logits_dtype=torch.bfloat16,
                  act_dtype=torch.bfloat16, table_dtype=torch.bfloat16, mode: str = "greedy",
                  temperature: float = 1.0, seed: int = 0):
         self.device = torch.device(device)
-        self.mode, self.temperature, self.seed = mode, temperature, seed
-        nb = select_workspace_bytes(batch, L, V, d, logits_dtype, act_dtype, table_dtype)
-        self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.device)
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.mode, self.temperature, self.seed = _MODES[mode], float(temperature), int(seed) & (2**64 - 1)
+        c = lambda t: BF16 if t == torch.bfloat16 else F32  # noqa: E731
+        self._shape = _Shape(batch, L, V, d, c(logits_dtype), c(act_dtype), c(table_dtype))
+        nb = int(lib().dfs_select_workspace_bytes(ctypes.byref(self._shape)))
+        if nb == 0:
+            raise ValueError("unsupported selector shape")
+        self._ws_bytes = nb
+        self.workspace = torch.empty(nb, dtype=torch.uint8, device=self.device)
         self.path = torch.empty((batch, L), dtype=torch.int32, device=self.device)
         self.scores = torch.empty((batch, L), dtype=torch.float32, device=self.device)
+        self._expect = (
+            ((batch, L, V), logits_dtype), ((batch, L, d), act_dtype), ((batch,), torch.int32),
+            ((V, E), table_dtype), ((V, E), table_dtype), ((d, E), act_dtype),
+        )
+        self._fn = lib().dfs_select
 
     def __call__(self, logits, hidden, prev_token, A, B, W_h):
-        return select(logits, hidden, prev_token, A, B, W_h, K, self.mode, self.temperature, self.seed,
-                      self.workspace, (self.path, self.scores))
+        args = (logits, hidden, prev_token, A, B, W_h)
+        for t, (shape, dtype) in zip(args, self._expect):
+            if t.shape != shape or t.dtype != dtype or t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"selector input must be a contiguous {dtype} tensor of shape {shape} "
+                                 f"on {self.device}")
+        rc = self._fn(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(), B.data_ptr(),
+                      W_h.data_ptr(), K, ctypes.byref(self._shape), self.mode, self.temperature, self.seed,
+                      self.workspace.data_ptr(), self._ws_bytes, self.path.data_ptr(), self.scores.data_ptr(),
+                      torch.cuda.current_stream(self.device).cuda_stream)
+        _check(rc, "dfs_select")
+        return self.path, self.scores
