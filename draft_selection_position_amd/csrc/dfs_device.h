@@ -42,16 +42,42 @@ __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(
 // ---------------------------------------------------------------- wave utilities
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-  lo = (uint32_t)__shfl_xor((int)lo, m);
-  hi = (uint32_t)__shfl_xor((int)hi, m);
+// x of lane (this lane ^ j) for j = 1, 2, 4, ..., 32, without going through LDS:
+// DPP quad permutes for 1 and 2, DPP row shifts / rotates for 4 and 8 (a row is 16
+// lanes; row_shl:n reads lane + n, row_shr:n lane - n, row_ror:8 lane ^ 8), and
+// gfx950's permlane swaps for 16 and 32 (called with both operands x, the first
+// result holds rows 0, 0, 2, 2 / halves 0, 0 and the second rows 1, 1, 3, 3 /
+// halves 1, 1).  j must be a compile-time constant after inlining.
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t x, int j, int lane) {
+  switch (j) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x104, 0xF, 0xF, false);
+      const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, false);
+      return (lane & 4) ? dn : up;
+    }
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      return (lane & 16) ? p[0] : p[1];
+    }
+    default: {
+      const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      return (lane & 32) ? p[0] : p[1];
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int j, int lane) {
+  const uint32_t lo = xor_lanes((uint32_t)x, j, lane);
+  const uint32_t hi = xor_lanes((uint32_t)(x >> 32), j, lane);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
-  uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-  lo = (uint32_t)__shfl((int)lo, src);
-  hi = (uint32_t)__shfl((int)hi, src);
+// x of lane `src` (a wave-uniform lane number), in every lane.
+__device__ __forceinline__ uint64_t lane_u64(uint64_t x, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), src);
   return ((uint64_t)hi << 32) | lo;
 }
 
@@ -62,7 +88,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t y = shfl_xor_u64(x, j);
+      const uint64_t y = shfl_xor_u64(x, j, lane);
       const bool lower = (lane & j) == 0;
       const bool desc = (lane & k) == 0;
       const bool take_max = (lower == desc);

@@ -18,8 +18,9 @@
 // groups of a row cover one whole 128-byte line in two load instructions.  For
 // bf16 tables the gated predecessor
 // embedding A(a) * g (fp32) is split as hi + lo in bf16 and fed to two MFMAs, so
-// the products are exact to ~2^-17 before fp32 accumulation.  The tiles stay in
-// LDS and wave 0 walks them.
+// the products are exact to ~2^-17 before fp32 accumulation.  Each wave reduces
+// its tile to the successor of every predecessor slot; one lane then follows the
+// chain through LDS.
 #include "dfs_device.h"
 #include "dfs_internal.h"
 
@@ -59,49 +60,81 @@ __device__ __forceinline__ double gumbel_noise(uint64_t seed, uint32_t b, uint32
   return -log(-log(u));
 }
 
-// The walk of one sequence over score tiles in LDS.  It is a chain of L dependent
-// 16-way argmaxes, so one lane runs it: each step reads the predecessor's row of
-// 16 scores from LDS and keeps the first maximum (lowest slot on ties).
-__device__ __forceinline__ void walk_tiles(const float (*sS)[kK][kK], const double (*sN)[kK],
-                                           const int32_t (*sC)[kK], int64_t b, int L, int mode,
-                                           double temperature, int32_t* __restrict__ out_path,
-                                           float* __restrict__ out_scores, int lane) {
-  if (lane != 0) return;
-  int i = 0;  // predecessor slot; every row of position 0 is the verified token's row
-  for (int t = 0; t < L; ++t) {
-    const float4* rp = reinterpret_cast<const float4*>(sS[t][i]);
-    float row[kK];
+// The walk, split in two.  First, for every position t and predecessor slot a,
+// the successor slot the walk would take from a: an argmax over the 16 candidate
+// slots of the score tile, lowest slot on ties (greedy), or of
+// S_t(a, j) / temperature + g(seed, b, t, j) in fp64 (Gumbel-max), computed for
+// all a and t at once.  The tile of position t is held by one wave as lane
+// (q, r) = (lane / 16, lane % 16) with s[i] = S_t(4q + i, r), so the argmax over
+// j = r is a reduction inside one 16-lane row (DPP, no LDS).  Second, the chain
+// itself: from slot 0 at t = 0 (every row of position 0 is the verified token's
+// row) follow the successor table, one dependent LDS read per step.
+struct WalkTables {
+  int32_t next[kMaxL][kK];  // successor slot of (t, a)
+  float best[kMaxL][kK];    // S_t(a, next) (the score without noise)
+  int32_t cand[kMaxL][kK];  // token id of (t, slot)
+};
+
+__device__ __forceinline__ void successors(const float (&s)[4], int t, int lane, int mode,
+                                           double temperature, uint64_t seed, int64_t b,
+                                           WalkTables& w) {
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  if (mode == 0) {
 #pragma unroll
-    for (int c = 0; c < kK / 4; ++c) {
-      const float4 v = rp[c];
-      row[4 * c] = v.x;
-      row[4 * c + 1] = v.y;
-      row[4 * c + 2] = v.z;
-      row[4 * c + 3] = v.w;
-    }
-    int j = 0;
-    if (mode == 0) {
-      float best = row[0];
+    for (int i = 0; i < 4; ++i) {
+      float v = s[i];
+      int j = r;
 #pragma unroll
-      for (int c = 1; c < kK; ++c)
-        if (row[c] > best) {
-          best = row[c];
-          j = c;
-        }
-    } else {
-      double best = (double)row[0] / temperature + sN[t][0];
-#pragma unroll
-      for (int c = 1; c < kK; ++c) {
-        const double v = (double)row[c] / temperature + sN[t][c];
-        if (v > best) {
-          best = v;
-          j = c;
-        }
+      for (int m = 1; m < kK; m <<= 1) {
+        const float ov = __uint_as_float(xor_lanes(__float_as_uint(v), m, lane));
+        const int oj = (int)xor_lanes((uint32_t)j, m, lane);
+        const bool take = ov > v || (ov == v && oj < j);
+        v = take ? ov : v;
+        j = take ? oj : j;
+      }
+      if (r == i) {
+        w.next[t][4 * q + i] = j;
+        w.best[t][4 * q + i] = v;
       }
     }
-    out_path[b * L + t] = sC[t][j];
-    out_scores[b * L + t] = row[j];
-    i = j;
+  } else {
+    const double g = gumbel_noise(seed, (uint32_t)b, (uint32_t)t, (uint32_t)r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double v = (double)s[i] / temperature + g;
+      float raw = s[i];
+      int j = r;
+#pragma unroll
+      for (int m = 1; m < kK; m <<= 1) {
+        const uint64_t bits = (uint64_t)__double_as_longlong(v);
+        const uint32_t lo = xor_lanes((uint32_t)bits, m, lane);
+        const uint32_t hi = xor_lanes((uint32_t)(bits >> 32), m, lane);
+        const double ov = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+        const float oraw = __uint_as_float(xor_lanes(__float_as_uint(raw), m, lane));
+        const int oj = (int)xor_lanes((uint32_t)j, m, lane);
+        const bool take = ov > v || (ov == v && oj < j);
+        v = take ? ov : v;
+        raw = take ? oraw : raw;
+        j = take ? oj : j;
+      }
+      if (r == i) {
+        w.next[t][4 * q + i] = j;
+        w.best[t][4 * q + i] = raw;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void chase(const WalkTables& w, int64_t b, int L,
+                                      int32_t* __restrict__ out_path,
+                                      float* __restrict__ out_scores) {
+  int a = 0;
+  for (int t = 0; t < L; ++t) {
+    const int j = w.next[t][a];
+    out_path[b * L + t] = w.cand[t][j];
+    out_scores[b * L + t] = w.best[t][a];
+    a = j;
   }
 }
 
@@ -119,17 +152,19 @@ __device__ __forceinline__ void load_gate(const float* __restrict__ gate, int64_
   }
 }
 
+// One workgroup of 16 waves per CU is all a launch of <= 256 sequences gives, so
+// registers are not rationed for a second one: every load of a wave can be in
+// flight at once.
 template <bool kBf16Tables, bool kWritePair, bool kWalk>
-__global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
+__global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4, 4))) void pair_walk_kernel(
     const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_val,
     const int32_t* __restrict__ prev_token, const float* __restrict__ gate,
     const void* __restrict__ A_, const void* __restrict__ B_, int L, int64_t V,
     float* __restrict__ out_pair,
     int mode, double temperature, uint64_t seed, int32_t* __restrict__ out_path,
     float* __restrict__ out_scores) {
-  __shared__ float sS[kMaxL][kK][kK];
-  __shared__ double sN[kMaxL][kK];
-  __shared__ int32_t sC[kMaxL][kK];
+  __shared__ WalkTables sW;
+  __shared__ __attribute__((aligned(16))) float sG[kBf16Tables ? kMaxL : 1][kE];
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;  // block position of this wave
   const int64_t b = blockIdx.x;
@@ -137,18 +172,25 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
   const int q = lane >> 4;  // embedding quarter [64q, 64q + 64)
   const int64_t row = b * L + t;
 
+  // (a pointer select, not a branch: no load has to wait for another)
+  const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
+  const int32_t pred_id = *pred_p;
+  const int32_t cand_id = cand_idx[row * kK + r];
+  const float u = cand_val[row * kK + r];
   // Ids outside [0, V) break the caller's contract; clamp them so that no gather
   // leaves the tables.
-  int64_t pred = t == 0 ? prev_token[b] : cand_idx[(row - 1) * kK + r];
-  int64_t cand = cand_idx[row * kK + r];
-  pred = pred < 0 ? 0 : (pred >= V ? V - 1 : pred);
-  cand = cand < 0 ? 0 : (cand >= V ? V - 1 : cand);
-  const float u = cand_val[row * kK + r];
-  if (kWalk && lane < kK) sC[t][lane] = (int32_t)cand_idx[row * kK + lane];
+  const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
+  const int64_t cand = cand_id < 0 ? 0 : (cand_id >= V ? V - 1 : cand_id);
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kBf16Tables) {
-    // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
+    // The gate row does not depend on the candidate ids: it is fetched (one
+    // 16-byte piece per lane) before the ids arrive and parked in LDS, so that
+    // all sixteen table-row fragments can be in flight at once right after.  The
+    // scheduling barriers keep that order.  Fragment c of this lane: elements
+    // [64 (c / 2) + 16 q + 8 (c % 2), + 8).
+    const float4 gp = *reinterpret_cast<const float4*>(gate + row * kE + 4 * lane);
+    __builtin_amdgcn_sched_barrier(0);
     const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) +
                                                        pred * kE + 16 * q);
     const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
@@ -159,10 +201,16 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
       av[c] = Ap[8 * (c >> 1) + (c & 1)];
       bv[c] = Bp[8 * (c >> 1) + (c & 1)];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    *reinterpret_cast<float4*>(&sG[t][4 * lane]) = gp;
+    __builtin_amdgcn_wave_barrier();  // the row is read back by other lanes of this wave only
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float g[8];
-      load_gate<8>(gate, row, 64 * (c >> 1) + 16 * q + 8 * (c & 1), g);
+      const float4 g0 = *reinterpret_cast<const float4*>(&sG[t][64 * (c >> 1) + 16 * q + 8 * (c & 1)]);
+      const float4 g1 = *reinterpret_cast<const float4*>(&sG[t][64 * (c >> 1) + 16 * q + 8 * (c & 1) + 4]);
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
       bf16x8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -193,39 +241,44 @@ __global__ __launch_bounds__(kWave * kMaxL) void pair_walk_kernel(
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w * g.w, bb.w, acc, 0, 0, 0);
     }
   }
+  if (kWalk && lane < kK) sW.cand[t][lane] = cand_id;
   // lane holds D[4q + i][r]: predecessor slot 4q + i, candidate slot r
+  float sc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float s = acc[i] + u;
-    if constexpr (kWalk) sS[t][4 * q + i][r] = s;
-    if constexpr (kWritePair) out_pair[(row * kK + 4 * q + i) * kK + r] = s;
+    sc[i] = acc[i] + u;
+    if constexpr (kWritePair) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
   }
   if constexpr (kWalk) {
-    if (mode == 1 && lane < kK) sN[t][lane] = gumbel_noise(seed, (uint32_t)b, (uint32_t)t, lane);
+    successors(sc, t, lane, mode, temperature, seed, b, sW);
     __syncthreads();
-    if (t == 0) walk_tiles(sS, sN, sC, b, L, mode, temperature, out_path, out_scores, lane);
+    if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
   }
 }
 
-// Walk over a pair tensor in memory: one wave per sequence.
-__global__ __launch_bounds__(kWave) void walk_kernel(const float* __restrict__ pair,
-                                                     const int32_t* __restrict__ cand_idx, int L,
-                                                     int mode, double temperature, uint64_t seed,
-                                                     int32_t* __restrict__ out_path,
-                                                     float* __restrict__ out_scores) {
-  __shared__ float sS[kMaxL][kK][kK];
-  __shared__ double sN[kMaxL][kK];
-  __shared__ int32_t sC[kMaxL][kK];
-  const int lane = threadIdx.x;
+// Walk over a pair tensor in memory: one workgroup per sequence, one wave per
+// position, each wave reading its score tile in the lane layout of the matrix-core
+// result above, so both walks run the same code on the same values.
+__global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __restrict__ pair,
+                                                            const int32_t* __restrict__ cand_idx,
+                                                            int L, int mode, double temperature,
+                                                            uint64_t seed,
+                                                            int32_t* __restrict__ out_path,
+                                                            float* __restrict__ out_scores) {
+  __shared__ WalkTables sW;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = threadIdx.x / kWave;
   const int64_t b = blockIdx.x;
-  const float* src = pair + b * L * kK * kK;
-  for (int e = lane; e < L * kK * kK; e += kWave) sS[e / (kK * kK)][(e / kK) % kK][e % kK] = src[e];
-  for (int e = lane; e < L * kK; e += kWave) sC[e / kK][e % kK] = cand_idx[b * L * kK + e];
-  if (mode == 1)
-    for (int e = lane; e < L * kK; e += kWave)
-      sN[e / kK][e % kK] = gumbel_noise(seed, (uint32_t)b, (uint32_t)(e / kK), (uint32_t)(e % kK));
+  const int64_t row = b * L + t;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = pair[(row * kK + 4 * q + i) * kK + r];
+  if (lane < kK) sW.cand[t][lane] = cand_idx[row * kK + lane];
+  successors(sc, t, lane, mode, temperature, seed, b, sW);
   __syncthreads();
-  walk_tiles(sS, sN, sC, b, L, mode, temperature, out_path, out_scores, lane);
+  if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
 }
 
 template <bool kBf16, bool kWritePair, bool kWalk>
@@ -267,9 +320,8 @@ hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
 hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L,
                        const WalkArgs& walk, int32_t* out_path, float* out_scores,
                        hipStream_t stream) {
-  walk_kernel<<<dim3((unsigned)batch), kWave, 0, stream>>>(pair, cand_idx, (int)L, walk.mode,
-                                                          walk.temperature, walk.seed, out_path,
-                                                          out_scores);
+  walk_kernel<<<dim3((unsigned)batch), dim3((unsigned)(kWave * L)), 0, stream>>>(
+      pair, cand_idx, (int)L, walk.mode, walk.temperature, walk.seed, out_path, out_scores);
   return hipGetLastError();
 }
 

@@ -85,12 +85,12 @@ __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint
   }
   w.cnt = 0;
   __builtin_amdgcn_wave_barrier();
-  const uint64_t k16 = shfl_u64(w.list, 15);
+  const uint64_t k16 = lane_u64(w.list, 15);
   if (k16 != 0) {
     uint32_t m = (uint32_t)(k16 >> 32);
     uint32_t old = 0;
     if (lane == 0) old = atomicMax(s_thr, m);
-    old = (uint32_t)__shfl((int)old, 0);
+    old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
     m = m > old ? m : old;
     w.thr = uniformf(unmono32(m));
   }
@@ -155,7 +155,7 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
   for (int e = 1; e < PV; ++e) m = fmaxf(m, v[e]);
   if (seed) {
     const uint64_t lk = (m == m) ? make_key(m, (uint32_t)lane) : 0ull;
-    const uint64_t k16 = shfl_u64(wave_sort_desc(lk, lane), 15);
+    const uint64_t k16 = lane_u64(wave_sort_desc(lk, lane), 15);
     if (k16 != 0) {
       const float t = key_value(k16);
       if (t > w.thr) w.thr = uniformf(t);
