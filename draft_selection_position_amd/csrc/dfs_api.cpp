@@ -5,7 +5,6 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
-#include <mutex>
 
 #include "../../include/dfs.h"
 #include "dfs_internal.h"
@@ -45,41 +44,6 @@ int check_device() {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DFS_OK : DFS_E_HIP; }
-
-// dfs_select runs the gate on a second stream of the same device, concurrently
-// with the top-16 pass (the pass streams HBM and leaves the matrix cores idle),
-// when the logits are at least this large; on MI355X this measured 7-8% faster
-// at 32 x 16 x 151936 and 64 x 16 x 262144, neutral at 256 x 16 x 151936 (the pass
-// then fills every CU) and slower for single-sequence blocks, where the extra
-// fork/join costs more than it hides.  0 disables the second stream.
-#ifndef DFS_SELECT_OVERLAP_MIN_BYTES
-#define DFS_SELECT_OVERLAP_MIN_BYTES (64ll << 20)
-#endif
-
-// Per-device side stream (default priority) and fork/join events, created on
-// first use and kept for the life of the process.  The enqueue sequence that uses
-// them is serialised by g_side_mu, so concurrent callers cannot interleave their
-// fork/join records.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-SideStream g_side[64];
-
-int side_stream(SideStream** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DFS_E_HIP;
-  SideStream& ss = g_side[dev];
-  if (!ss.stream) {
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      return DFS_E_HIP;
-  }
-  *out = &ss;
-  return DFS_OK;
-}
 
 int check_topk_args(const void* logits, int dt, int64_t rows, int64_t V, int k,
                     const int32_t* out_idx, const float* out_val) {
@@ -218,7 +182,7 @@ int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_
   int st = check_device();
   if (st != DFS_OK) return st;
   (void)hipGetLastError();
-  return hip_status(launch_pair_walk(cand_idx, cand_val, prev_token, gate, A, B,
+  return hip_status(launch_pair_walk(cand_idx, cand_val, prev_token, GateSrc{gate, 1, 0}, A, B,
                                      table_dt == DFS_BF16, batch, L, V, out_pair, nullptr, nullptr,
                                      nullptr, stream));
 }
@@ -270,33 +234,25 @@ int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token
   int32_t* cand_idx = reinterpret_cast<int32_t*>(w + l.cand_idx_off);
   float* cand_val = reinterpret_cast<float*>(w + l.cand_val_off);
   float* gate = reinterpret_cast<float*>(w + l.gate_off);
-  hipError_t e;
-  const int64_t logit_bytes = s.batch * s.L * s.V * esize(s.logits_dtype);
-  if (DFS_SELECT_OVERLAP_MIN_BYTES > 0 && logit_bytes >= DFS_SELECT_OVERLAP_MIN_BYTES) {
-    // fork: the side stream starts where `stream` is; join: `stream` waits for the gate
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* ss = nullptr;
-    if (side_stream(&ss) != DFS_OK) return DFS_E_HIP;
-    if (hipEventRecord(ss->fork, stream) != hipSuccess ||
-        hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+  // One stream, in order: the top-16 pass (the W_h packing slabs ride in its
+  // tail), the gate GEMM, the gate finish when the K split is wider than the pair
+  // kernel adds up itself, then pair scores and the walk in one kernel.
+  char* gws = w + l.gate_ws_off;
+  const PackJob job = gate_pack_job(l.gate, W_h, gws);
+  hipError_t e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
+                             w + l.topk_ws_off, stream, &job);
+  if (e != hipSuccess) return DFS_E_HIP;
+  if ((e = launch_gate_gemm(l.gate, hidden, W_h, gate, gws, stream)) != hipSuccess) return DFS_E_HIP;
+  GateSrc gs{gate, 1, 0};
+  if (l.gate.splits > 1) {
+    if (l.gate.splits <= pair_max_gate_splits()) {
+      gs = GateSrc{gate_partials(l.gate, gws), l.gate.splits, s.batch * s.L * DFS_E};
+    } else if ((e = launch_gate_finish(l.gate, gate, gws, stream)) != hipSuccess) {
       return DFS_E_HIP;
-    e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
-                    w + l.topk_ws_off, stream);
-    if (e != hipSuccess) return DFS_E_HIP;
-    e = launch_gate(l.gate, hidden, W_h, gate, w + l.gate_ws_off, ss->stream);
-    if (e != hipSuccess) return DFS_E_HIP;
-    if (hipEventRecord(ss->join, ss->stream) != hipSuccess ||
-        hipStreamWaitEvent(stream, ss->join, 0) != hipSuccess)
-      return DFS_E_HIP;
-  } else {
-    e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
-                    w + l.topk_ws_off, stream);
-    if (e != hipSuccess) return DFS_E_HIP;
-    e = launch_gate(l.gate, hidden, W_h, gate, w + l.gate_ws_off, stream);
-    if (e != hipSuccess) return DFS_E_HIP;
+    }
   }
   const WalkArgs wa{(int)mode, temperature, seed};
-  e = launch_pair_walk(cand_idx, cand_val, prev_token, gate, A, B, s.table_dtype == DFS_BF16,
+  e = launch_pair_walk(cand_idx, cand_val, prev_token, gs, A, B, s.table_dtype == DFS_BF16,
                        s.batch, s.L, s.V, nullptr, &wa, out_path, out_scores, stream);
   return hip_status(e);
 }

@@ -13,6 +13,14 @@ constexpr int64_t kTargetBlocks = 2048;
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A W_h packing job (gate_pack.h) riding along with another launch (nslabs == 0: none).
+struct PackJob {
+  const uint16_t* W;
+  int64_t d;
+  uint16_t* Wp;
+  int nslabs;
+};
+
 // ---------------------------------------------------------------- top-16
 struct TopkPlan {
   int64_t rows, V;
@@ -22,8 +30,10 @@ struct TopkPlan {
   size_t ws_bytes; // partial lists when parts > 1
 };
 TopkPlan plan_topk(int64_t rows, int64_t V, int esize);
+// `pack` (may be null): W_h packing slabs run as extra workgroups of the same launch.
 hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
-                       float* out_val, void* ws, hipStream_t stream);
+                       float* out_val, void* ws, hipStream_t stream,
+                       const PackJob* pack = nullptr);
 
 // ---------------------------------------------------------------- gate
 struct GatePlan {
@@ -37,8 +47,18 @@ struct GatePlan {
   size_t ws_bytes;
 };
 GatePlan plan_gate(int64_t rows, int64_t d, bool bf16);
+// The whole gate: pack W_h (bf16), GEMM, finish (when split).
 hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, float* out_gate,
                        void* ws, hipStream_t stream);
+// Its parts, for callers that place them themselves.  The packing job (bf16 only;
+// nslabs == 0 otherwise) must complete before the GEMM; with splits > 1 the GEMM
+// leaves partial sums [splits, rows, 256] at gate_partials() and out_gate is only
+// written by the finish.
+PackJob gate_pack_job(const GatePlan& p, const void* W_h, void* ws);
+hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W_h,
+                            float* out_gate, void* ws, hipStream_t stream);
+hipError_t launch_gate_finish(const GatePlan& p, float* out_gate, void* ws, hipStream_t stream);
+const float* gate_partials(const GatePlan& p, const void* ws);
 
 // ---------------------------------------------------------------- pair scores and walk
 struct WalkArgs {
@@ -46,10 +66,19 @@ struct WalkArgs {
   double temperature;
   uint64_t seed;
 };
+// Where the pair kernel finds the gate: the finished gate [rows, 256] (splits 1),
+// or up to pair_max_gate_splits() K-split partial sums [splits, rows, 256], `stride`
+// floats apart, which it adds up in split order and passes through the sigmoid.
+struct GateSrc {
+  const float* gate;
+  int splits;
+  int64_t stride;
+};
+int pair_max_gate_splits();
 // Pair scores for every (sequence, position); optionally written to out_pair and
 // optionally followed by the walk in the same kernel (out_path/out_scores non-null).
 hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
-                            const int32_t* prev_token, const float* gate, const void* A,
+                            const int32_t* prev_token, const GateSrc& gate, const void* A,
                             const void* B, bool bf16_tables, int64_t batch, int64_t L,
                             int64_t V, float* out_pair, const WalkArgs* walk, int32_t* out_path,
                             float* out_scores, hipStream_t stream);

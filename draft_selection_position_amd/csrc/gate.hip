@@ -8,13 +8,16 @@
 // bf16 path (gfx950 matrix cores): Z[rows, 256] = H[rows, d] x W_h[d, 256] with
 // V_MFMA_F32_16X16X32_BF16.  The MFMA wants every lane's operand to be 8
 // consecutive k values, but W_h is n-contiguous, so W_h is first repacked once per
-// call into [d/32][256][32] (2.6 MB at d = 5120, stays in L2) and both operands are
-// then read straight from memory with 16-byte loads.  Each wave owns 64 output
-// columns and 16 * MT rows; small row counts split K across workgroups and a
-// finish kernel adds the partial sums in a fixed order and applies the sigmoid.
+// call into [d/32][256][32] (gate_pack.h; 2.6 MB at d = 5120, stays in L2) and both
+// operands are then read straight from memory with 16-byte loads.  A workgroup
+// computes a 64-row x 256-column tile over one K split, each of its 8 waves 32
+// columns; row counts too small to fill the chip split K, and the partial sums
+// are added in split order (by the finish kernel here, or by the pair kernel
+// that reads the gate) before the sigmoid.
 // fp32 path: plain FMA over a [8 rows x 256 columns] tile per workgroup.
 #include "dfs_device.h"
 #include "dfs_internal.h"
+#include "gate_pack.h"
 
 namespace dfs {
 namespace {
@@ -24,45 +27,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kKB = 32;          // k per MFMA step
+static_assert(kKB == kPackK, "the GEMM steps through W_h one packed slab at a time");
 #ifndef DFS_GATE_TARGET_WG
 #define DFS_GATE_TARGET_WG 256
 #endif
 constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims for
 
-// Wp[kb][n][kk] = W[kb*32 + kk][n], zero past d: one workgroup per 32-row slab of
-// W, read with 16-byte loads, transposed through LDS, written with 16-byte stores.
-__global__ __launch_bounds__(kThreads) void pack_w_kernel(const uint16_t* __restrict__ W,
-                                                          int64_t d, uint16_t* __restrict__ Wp) {
-  __shared__ uint16_t tile[kKB][kE + 8];  // +8: spread the column reads over banks
-  const int tid = threadIdx.x;
-  const int64_t kb = blockIdx.x;
-  {
-    const int kk = tid >> 3;         // 32 rows, 8 threads per row
-    const int n0 = (tid & 7) * 32;   // 32 columns per thread
-    const int64_t k = kb * kKB + kk;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (k < d) v = *reinterpret_cast<const uint4*>(W + k * kE + n0 + 8 * c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tile[kk][n0 + 8 * c + 2 * e] = (uint16_t)(w[e] & 0xffffu);
-        tile[kk][n0 + 8 * c + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-      }
-    }
-  }
-  __syncthreads();
-  const int n = tid;  // one output column (32 k values = 64 bytes) per thread
-  uint4* dst = reinterpret_cast<uint4*>(Wp + (kb * kE + n) * kKB);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[8 * c + 2 * e][n] | ((uint32_t)tile[8 * c + 2 * e + 1][n] << 16);
-    dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+__global__ __launch_bounds__(kPackThreads) void pack_w_kernel(const uint16_t* __restrict__ W,
+                                                              int64_t d, uint16_t* __restrict__ Wp) {
+  __shared__ uint16_t tile[kPackK][kPackPitch];
+  pack_w_slab(W, d, Wp, blockIdx.x, threadIdx.x, tile);
 }
 
 #ifndef DFS_GATE_DEPTH
@@ -203,14 +177,20 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
   }
 }
 
-constexpr int kF32Rows = 8;
+constexpr int kF32Rows = 8;     // rows per workgroup
+constexpr int kF32KBlock = 256; // k staged in LDS at a time
+constexpr int kF32Unroll = 16;  // W_h loads in flight per thread
 
+// One thread per output column n, eight rows per workgroup, k range of one split.
+// The H rows of each k block are staged in LDS (read back as broadcasts); the
+// W_h column values are loaded 16 ahead of the FMAs.  Accumulation is in k order.
 __global__ __launch_bounds__(kThreads) void gate_f32_kernel(const float* __restrict__ H,
                                                             const float* __restrict__ W,
                                                             int64_t rows, int64_t d,
                                                             int64_t kchunk, int splits,
                                                             float* __restrict__ partial,
                                                             float* __restrict__ out) {
+  __shared__ float sH[kF32Rows][kF32KBlock];
   const int n = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * kF32Rows;
   const int s = blockIdx.y;
@@ -219,11 +199,31 @@ __global__ __launch_bounds__(kThreads) void gate_f32_kernel(const float* __restr
   float acc[kF32Rows];
 #pragma unroll
   for (int i = 0; i < kF32Rows; ++i) acc[i] = 0.0f;
-  for (int64_t k = k0; k < k1; ++k) {
-    const float w = W[k * kE + n];
+  for (int64_t kb = k0; kb < k1; kb += kF32KBlock) {
+    const int kc = (int)(k1 - kb < kF32KBlock ? k1 - kb : kF32KBlock);
+    __syncthreads();  // the previous block has been consumed
+    for (int e = n; e < kF32Rows * kF32KBlock; e += kThreads) {
+      const int i = e / kF32KBlock, kk = e % kF32KBlock;
+      float v = 0.0f;
+      if (kk < kc && m0 + i < rows) v = H[(m0 + i) * d + kb + kk];
+      sH[i][kk] = v;
+    }
+    __syncthreads();
+    int k = 0;
+    for (; k + kF32Unroll <= kc; k += kF32Unroll) {
+      float w[kF32Unroll];
 #pragma unroll
-    for (int i = 0; i < kF32Rows; ++i)
-      if (m0 + i < rows) acc[i] = fmaf(H[(m0 + i) * d + k], w, acc[i]);
+      for (int u = 0; u < kF32Unroll; ++u) w[u] = W[(kb + k + u) * kE + n];
+#pragma unroll
+      for (int u = 0; u < kF32Unroll; ++u)
+#pragma unroll
+        for (int i = 0; i < kF32Rows; ++i) acc[i] = fmaf(sH[i][k + u], w[u], acc[i]);
+    }
+    for (; k < kc; ++k) {
+      const float w = W[(kb + k) * kE + n];
+#pragma unroll
+      for (int i = 0; i < kF32Rows; ++i) acc[i] = fmaf(sH[i][k], w, acc[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < kF32Rows; ++i) {
@@ -300,15 +300,24 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   return p;
 }
 
-hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, float* out_gate,
-                       void* ws, hipStream_t stream) {
+PackJob gate_pack_job(const GatePlan& p, const void* W_h, void* ws) {
+  if (!p.bf16) return PackJob{nullptr, 0, nullptr, 0};
+  return PackJob{static_cast<const uint16_t*>(W_h), p.d,
+                 reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.packed_off),
+                 (int)cdiv(p.d, kKB)};
+}
+
+const float* gate_partials(const GatePlan& p, const void* ws) {
+  return p.splits > 1 ? reinterpret_cast<const float*>(static_cast<const char*>(ws) + p.partial_off)
+                      : nullptr;
+}
+
+hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W_h,
+                            float* out_gate, void* ws, hipStream_t stream) {
   char* wsb = static_cast<char*>(ws);
   float* partial = p.splits > 1 ? reinterpret_cast<float*>(wsb + p.partial_off) : nullptr;
   if (p.bf16) {
-    uint16_t* Wp = reinterpret_cast<uint16_t*>(wsb + p.packed_off);
-    const int64_t KB = cdiv(p.d, kKB);
-    pack_w_kernel<<<dim3((unsigned)KB), kThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(W_h), p.d, Wp);
+    const uint16_t* Wp = reinterpret_cast<const uint16_t*>(wsb + p.packed_off);
     const uint16_t* H = static_cast<const uint16_t*>(hidden);
     const dim3 grid((unsigned)(cdiv(p.rows, kTileM) * p.splits));
     gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
@@ -319,11 +328,26 @@ hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, f
                                                    static_cast<const float*>(W_h), p.rows, p.d,
                                                    p.kchunk, p.splits, partial, out_gate);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_finish(const GatePlan& p, float* out_gate, void* ws, hipStream_t stream) {
   if (p.splits > 1) {
-    gate_finish_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.rows, p.splits,
-                                                                        out_gate);
+    gate_finish_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(gate_partials(p, ws), p.rows,
+                                                                        p.splits, out_gate);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, float* out_gate,
+                       void* ws, hipStream_t stream) {
+  if (p.bf16) {
+    const PackJob job = gate_pack_job(p, W_h, ws);
+    pack_w_kernel<<<dim3((unsigned)job.nslabs), kPackThreads, 0, stream>>>(job.W, job.d, job.Wp);
+  }
+  hipError_t e = launch_gate_gemm(p, hidden, W_h, out_gate, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_gate_finish(p, out_gate, ws, stream);
 }
 
 }  // namespace dfs

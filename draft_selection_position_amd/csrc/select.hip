@@ -138,18 +138,34 @@ __device__ __forceinline__ void chase(const WalkTables& w, int64_t b, int L,
   }
 }
 
-// Gate values g[row, e0 .. e0 + N) of the finished gate [rows, 256].
-template <int N>
-__device__ __forceinline__ void load_gate(const float* __restrict__ gate, int64_t row, int e0,
-                                          float* g) {
+// Gate splits the pair kernel adds up itself (more are finished by a kernel of
+// their own first).
+constexpr int kMaxGateSplits = 4;
+
+// This lane's 16-byte piece [4 lane, + 4) of the gate row `row`: the finished gate
+// (splits == 1), or the K-split partial sums [splits, rows, 256] (row stride
+// `stride` between splits) added in split order from zero, exactly as the finish
+// kernel adds them, then passed through the sigmoid.  The loads are not
+// predicated (a clamped split index), so none waits for another.
+__device__ __forceinline__ float4 gate_piece(const float* __restrict__ gate, int splits,
+                                             int64_t stride, int64_t row, int lane) {
+  const float* p = gate + row * kE + 4 * lane;
+  float4 v[kMaxGateSplits];
 #pragma unroll
-  for (int c = 0; c < N / 4; ++c) {
-    const float4 v = *reinterpret_cast<const float4*>(gate + row * kE + e0 + 4 * c);
-    g[4 * c] = v.x;
-    g[4 * c + 1] = v.y;
-    g[4 * c + 2] = v.z;
-    g[4 * c + 3] = v.w;
+  for (int u = 0; u < kMaxGateSplits; ++u)
+    v[u] = *reinterpret_cast<const float4*>(p + (int64_t)(u < splits ? u : splits - 1) * stride);
+  if (splits == 1) return v[0];
+  float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int u = 0; u < kMaxGateSplits; ++u) {
+    if (u < splits) {
+      z.x += v[u].x;
+      z.y += v[u].y;
+      z.z += v[u].z;
+      z.w += v[u].w;
+    }
   }
+  return make_float4(sigmoidf(z.x), sigmoidf(z.y), sigmoidf(z.z), sigmoidf(z.w));
 }
 
 // One workgroup of 16 waves per CU is all a launch of <= 256 sequences gives, so
@@ -158,13 +174,12 @@ __device__ __forceinline__ void load_gate(const float* __restrict__ gate, int64_
 template <bool kBf16Tables, bool kWritePair, bool kWalk>
 __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4, 4))) void pair_walk_kernel(
     const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_val,
-    const int32_t* __restrict__ prev_token, const float* __restrict__ gate,
-    const void* __restrict__ A_, const void* __restrict__ B_, int L, int64_t V,
-    float* __restrict__ out_pair,
-    int mode, double temperature, uint64_t seed, int32_t* __restrict__ out_path,
-    float* __restrict__ out_scores) {
+    const int32_t* __restrict__ prev_token, const float* __restrict__ gate, int gate_splits,
+    int64_t gate_stride, const void* __restrict__ A_, const void* __restrict__ B_, int L,
+    int64_t V, float* __restrict__ out_pair, int mode, double temperature, uint64_t seed,
+    int32_t* __restrict__ out_path, float* __restrict__ out_scores) {
   __shared__ WalkTables sW;
-  __shared__ __attribute__((aligned(16))) float sG[kBf16Tables ? kMaxL : 1][kE];
+  __shared__ __attribute__((aligned(16))) float sG[kMaxL][kE];  // gate row of each position
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;  // block position of this wave
   const int64_t b = blockIdx.x;
@@ -182,15 +197,15 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
   const int64_t cand = cand_id < 0 ? 0 : (cand_id >= V ? V - 1 : cand_id);
 
+  // The gate row does not depend on the candidate ids: it is fetched (one 16-byte
+  // piece per lane) before the ids arrive and parked in LDS, so that the table-row
+  // fragments can all be in flight at once right after.  The scheduling barriers
+  // keep that order; the row is read back by other lanes of the same wave only.
+  const float4 gp = gate_piece(gate, gate_splits, gate_stride, row, lane);
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kBf16Tables) {
-    // The gate row does not depend on the candidate ids: it is fetched (one
-    // 16-byte piece per lane) before the ids arrive and parked in LDS, so that
-    // all sixteen table-row fragments can be in flight at once right after.  The
-    // scheduling barriers keep that order.  Fragment c of this lane: elements
-    // [64 (c / 2) + 16 q + 8 (c % 2), + 8).
-    const float4 gp = *reinterpret_cast<const float4*>(gate + row * kE + 4 * lane);
-    __builtin_amdgcn_sched_barrier(0);
+    // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
     const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) +
                                                        pred * kE + 16 * q);
     const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
     }
     __builtin_amdgcn_sched_barrier(0);
     *reinterpret_cast<float4*>(&sG[t][4 * lane]) = gp;
-    __builtin_amdgcn_wave_barrier();  // the row is read back by other lanes of this wave only
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float g[8];
@@ -229,12 +244,12 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
                                                        4 * q);
     const float4* Bp = reinterpret_cast<const float4*>(static_cast<const float*>(B_) + cand * kE +
                                                        4 * q);
+    *reinterpret_cast<float4*>(&sG[t][4 * lane]) = gp;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll 4
     for (int c = 0; c < 16; ++c) {
       const float4 a = Ap[4 * c], bb = Bp[4 * c];
-      float gv[4];
-      load_gate<4>(gate, row, 16 * c + 4 * q, gv);
-      const float4 g = make_float4(gv[0], gv[1], gv[2], gv[3]);
+      const float4 g = *reinterpret_cast<const float4*>(&sG[t][16 * c + 4 * q]);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
@@ -283,22 +298,25 @@ __global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __rest
 
 template <bool kBf16, bool kWritePair, bool kWalk>
 void launch_pw(int64_t batch, int64_t L, int64_t V, const int32_t* cand_idx, const float* cand_val,
-               const int32_t* prev_token, const float* gate, const void* A, const void* B,
+               const int32_t* prev_token, const GateSrc& g, const void* A, const void* B,
                float* out_pair, const WalkArgs* w, int32_t* out_path, float* out_scores,
                hipStream_t stream) {
   pair_walk_kernel<kBf16, kWritePair, kWalk><<<dim3((unsigned)batch), dim3((unsigned)(kWave * L)),
                                                 0, stream>>>(
-      cand_idx, cand_val, prev_token, gate, A, B, (int)L, V, out_pair, w ? w->mode : 0,
-      w ? w->temperature : 1.0, w ? w->seed : 0ull, out_path, out_scores);
+      cand_idx, cand_val, prev_token, g.gate, g.splits, g.stride, A, B, (int)L, V, out_pair,
+      w ? w->mode : 0, w ? w->temperature : 1.0, w ? w->seed : 0ull, out_path, out_scores);
 }
 
 }  // namespace
 
+int pair_max_gate_splits() { return kMaxGateSplits; }
+
 hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
-                            const int32_t* prev_token, const float* gate, const void* A,
+                            const int32_t* prev_token, const GateSrc& gate, const void* A,
                             const void* B, bool bf16_tables, int64_t batch, int64_t L,
                             int64_t V, float* out_pair, const WalkArgs* walk, int32_t* out_path,
                             float* out_scores, hipStream_t stream) {
+  if (gate.splits < 1 || gate.splits > kMaxGateSplits) return hipErrorInvalidValue;
   const bool wp = out_pair != nullptr;
   const bool wk = walk != nullptr;
 #define DFS_PW(BF, WP, WK)                                                                      \

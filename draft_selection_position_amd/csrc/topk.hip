@@ -18,6 +18,7 @@
 // not depend on the order in which elements are seen.
 #include "dfs_device.h"
 #include "dfs_internal.h"
+#include "gate_pack.h"
 
 namespace dfs {
 namespace {
@@ -172,12 +173,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
                                                               int64_t V, int parts, int64_t chunk,
                                                               uint64_t* __restrict__ partial,
                                                               int32_t* __restrict__ out_idx,
-                                                              float* __restrict__ out_val) {
+                                                              float* __restrict__ out_val,
+                                                              int64_t ntopk, PackJob pack) {
   using T = typename Elems<kBf16>::T;
   constexpr int PV = Elems<kBf16>::per_vec;
   __shared__ uint64_t s_buf[kWaves][kCap];
   __shared__ uint64_t s_list[kWaves * kK];
   __shared__ uint32_t s_thr;
+  static_assert(sizeof(s_buf) >= kPackLdsBytes, "the packing job reuses the key buffers");
+
+  if (blockIdx.x >= ntopk) {  // workgroups past the top-16 jobs pack W_h (fused selector)
+    pack_w_slab(pack.W, pack.d, pack.Wp, (int64_t)(blockIdx.x - ntopk), threadIdx.x,
+                reinterpret_cast<uint16_t(*)[kPackPitch]>(&s_buf[0][0]));
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -339,15 +348,20 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int esize) {
 }
 
 hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
-                       float* out_val, void* ws, hipStream_t stream) {
+                       float* out_val, void* ws, hipStream_t stream, const PackJob* pack) {
+  static_assert(kThreads == kPackThreads, "packing jobs run on top-16 workgroups");
   uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
-  const dim3 grid((unsigned)(p.rows * p.parts));
+  const int64_t ntopk = p.rows * p.parts;
+  const PackJob job = pack ? *pack : PackJob{nullptr, 0, nullptr, 0};
+  // the packing jobs come last: they run in the tail of the pass, on CUs the last
+  // rows leave idle
+  const dim3 grid((unsigned)(ntopk + job.nslabs));
   if (bf16) {
     topk_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial,
-                                                           out_idx, out_val);
+                                                           out_idx, out_val, ntopk, job);
   } else {
     topk_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk,
-                                                            partial, out_idx, out_val);
+                                                            partial, out_idx, out_val, ntopk, job);
   }
   if (p.parts > 1) {
     topk_merge_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.parts, out_idx,

@@ -139,18 +139,12 @@ int dfs_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t 
 /* ---------------------------------------------------------------- fused selector
  * The whole selector: dfs_topk over logits [batch, L, V], dfs_gate over hidden
  * [batch, L, d] with W_h [d, 256], then pair scores and the walk fused in one
- * kernel (scores stay on chip).  Same results as calling the four steps in turn.
+ * kernel (scores stay on chip).  Same results, bit for bit, as calling the four
+ * steps in turn.  Everything is enqueued on `stream` alone.
  * prev_token [batch] int32; A, B [V, 256]; out_path [batch, L] int32; out_scores
  * [batch, L] fp32.  Alignment as in the step entry points; ws 256 bytes.
- * ws: dfs_select_workspace_bytes(shape) bytes of scratch (about 23 MB at batch 256,
- * L 16, V 151936, d 5120).
- * When the logits are 64 MiB or larger, the gate runs on a second stream of the
- * current device, concurrently with the top-16 pass: an event recorded on `stream`
- * starts it and `stream` waits on an event recorded after it, so ordering against
- * other work on `stream` (and HIP graph capture of `stream`) is as for one stream.
- * That stream and its two events are created on the first such call and kept for
- * the life of the process; the short host-side enqueue sequence is serialised
- * across threads.                                                                  */
+ * ws: dfs_select_workspace_bytes(shape) bytes of scratch (about 24 MB at batch 256,
+ * L 16, V 151936, d 5120).                                                        */
 size_t dfs_select_workspace_bytes(const dfs_shape_t* shape);
 int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
                const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
