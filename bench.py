@@ -25,7 +25,8 @@ METRIC = "draft blocks/sec through dfs_select; top-16 HBM GB/s as % of peak"
 HBM_PEAK_GBS = 8000.0
 # Sources of the top-16 kernel; HBM traffic figures taken with rocprofv3 counters
 # are reported only while these files hash to the value recorded with them.
-TOPK_SOURCES = ["draft_selection_position_amd/csrc/topk.hip", "draft_selection_position_amd/csrc/dfs_device.h"]
+TOPK_SOURCES = ["draft_selection_position_amd/csrc/topk.hip", "draft_selection_position_amd/csrc/dfs_device.h",
+                "draft_selection_position_amd/csrc/gate_pack.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_throughput_traffic.txt")
 
 
@@ -82,6 +83,52 @@ def summarize_rocprof(d: str) -> None:
         print("|---|---|---|---|---|")
         for (name, cn, g), v in sorted(agg.items()):
             print(f"| {name} | {cn} | {g} | {len(v)} | {sum(v) / len(v):.1f} |")
+
+
+def traffic_record(fetch_dir: str, write_dir: str, copy_mb: int, workload: str) -> None:
+    """Print the top-16 HBM traffic record (the format of TRAFFIC_FILE) from two rocprofv3
+    counter runs of `bench.py --calibrate-copy-mb copy_mb`: one with FETCH_SIZE, one with
+    WRITE_SIZE.  The calibration copies are the copy kernels whose WRITE_SIZE is exactly
+    copy_mb MiB; the top-16 launches are the standalone ones (grid = rows x 256 threads)."""
+    import csv
+    import glob
+
+    from workloads import config_by_name
+
+    cfg = config_by_name(workload)
+    rows = cfg.batch * cfg.L
+    esize = 2 if cfg.dtype == "bf16" else 4
+
+    def load(d, counter):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mb * 1024.0
+    cal_ids = {r["Dispatch_Id"] for r in write
+               if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) == copy_kib}
+    cal_f = [float(r["Counter_Value"]) for r in fetch if r["Dispatch_Id"] in cal_ids]
+    if not cal_ids or not cal_f:
+        raise SystemExit("no calibration copies found")
+    f_factor = sum(cal_f) / len(cal_f) / copy_kib
+    grid = str(rows * 256)
+    tk_f = [float(r["Counter_Value"]) for r in fetch if "topk_chunk" in r["Kernel_Name"] and r["Grid_Size"] == grid]
+    tk_w = [float(r["Counter_Value"]) for r in write if "topk_chunk" in r["Kernel_Name"] and r["Grid_Size"] == grid]
+    fk, wk = sum(tk_f) / len(tk_f), sum(tk_w) / len(tk_w)
+    fb, wb = fk * 1024 / f_factor, wk * 1024 / 1.0
+    print(f"workload: {workload}")
+    print(f"kernel_source_sha256_16: {topk_source_sha()}")
+    print(f"dispatches_fetch: {len(tk_f)}")
+    print(f"dispatches_write: {len(tk_w)}")
+    print(f"calibration_copies: {len(cal_f)} x {copy_mb} MiB")
+    print(f"fetch_size_kib_per_dispatch: {fk}")
+    print(f"write_size_kib_per_dispatch: {wk}")
+    print(f"copy_fetch_factor: {f_factor:.6f}")
+    print("copy_write_factor: 1.000000")
+    print(f"fetch_bytes_per_launch: {fb:.0f}")
+    print(f"write_bytes_per_launch: {wb:.0f}")
+    print(f"hbm_bytes_per_launch: {fb + wb:.0f}")
+    print(f"algorithmic_bytes_per_launch: {rows * cfg.V * esize}")
 
 
 def _affinity() -> int:
@@ -147,11 +194,16 @@ def main() -> int:
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run device-to-device copies of this size (counter calibration)")
     ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the top-16 traffic record from FETCH_SIZE / WRITE_SIZE counter runs and exit")
     ap.add_argument("--graph", action="store_true",
                     help="also time dfs_select replayed from a captured HIP graph (one launch per step)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return 0
+    if args.traffic_record:
+        traffic_record(*args.traffic_record, args.calibrate_copy_mb or 512, args.workload)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -180,40 +232,64 @@ def main() -> int:
     from tests.parity import upload
 
     dev = upload(inp)
+    # Copies of the whole input set at other addresses, rotated call by call, so that
+    # the 256 MB Infinity Cache cannot serve one call's reads from the previous
+    # call's (at least three sets and at least 512 MB in all).
+    names = ("logits", "hidden", "prev_token", "A", "B", "W_h")
+    set_bytes = sum(dev[k].numel() * dev[k].element_size() for k in names)
+    nsets = max(3, -(-(512 << 20) // set_bytes))
+    sets = [dev] + [{k: dev[k].clone() for k in names} for _ in range(nsets - 1)]
     torch.cuda.synchronize()
     sel = dfs.Selector(cfg.batch, cfg.L, cfg.V, cfg.d, mode=cfg.walk, temperature=cfg.temperature,
                        seed=cfg.walk_seed,
                        logits_dtype=dev["logits"].dtype, act_dtype=dev["hidden"].dtype,
                        table_dtype=dev["A"].dtype)
-    call = lambda: sel(dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])  # noqa
+    args_of = [tuple(st[k] for k in names) for st in sets]
 
-    print(f"[bench] warmup {args.warmup}, timed {args.steps} dfs_select steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        call()
+    def call(i=0):
+        return sel(*args_of[i % nsets])
+
+    print(f"[bench] {nsets} input sets of {set_bytes / 2**20:.0f} MiB; warmup {args.warmup}, "
+          f"timed {args.steps} dfs_select steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        call(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(args.steps):
-        call()
+    for i in range(args.steps):
+        call(i)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     blocks_per_s = cfg.batch / (ms_per_step * 1e-3)
-    path = sel.path.cpu().numpy()
+    path = sel.path.cpu().numpy()  # the last call's (every set holds the same values)
 
-    # The dominant kernel alone: the top-16 pass over [batch*L, V], same stream.
+    # Per-call spread: the same calls again, each between its own pair of events.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in evs])
+    pct = {f"p{q}": float(np.percentile(per_call, q)) for q in (10, 50, 90)}
+
+    # The dominant kernel alone: the top-16 pass over [batch*L, V], same stream,
+    # rotating over the input sets' logits like the calls above.
     logits2d = dev["logits"].view(-1, cfg.V)
+    all2d = [st["logits"].view(-1, cfg.V) for st in sets]
     rows = logits2d.shape[0]
     ws = torch.empty(max(1, dfs.topk_workspace_bytes(rows, cfg.V, logits2d.dtype)), dtype=torch.uint8,
                      device=logits2d.device)
-    for _ in range(5):
-        dfs.topk(logits2d, workspace=ws)
+    for i in range(5):
+        dfs.topk(all2d[i % nsets], workspace=ws)
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(args.steps):
-        dfs.topk(logits2d, workspace=ws)
+    for i in range(args.steps):
+        dfs.topk(all2d[i % nsets], workspace=ws)
     ev1.record()
     torch.cuda.synchronize()
     topk_ms = ev0.elapsed_time(ev1) / args.steps
@@ -293,10 +369,13 @@ def main() -> int:
                      "frac": topk_gbs / HBM_PEAK_GBS, "traffic": None if traffic is None else traffic[0],
                      "kernel": "topk_chunk_kernel", "bytes_per_launch": topk_bytes, "avg_ms": topk_ms},
         "step_ms": {"topk": topk_ms, "gate": gate_ms, "pair_scores": pair_ms, "select": ms_per_step},
+        "select_ms_per_call": pct,
+        "input_sets": nsets,
         "host_wall_s": wall,
     }
     if graph_ms is not None:
-        out["graph_replay"] = {"ms_per_step": graph_ms, "value": cfg.batch / (graph_ms * 1e-3)}
+        out["graph_replay"] = {"ms_per_step": graph_ms, "value": cfg.batch / (graph_ms * 1e-3),
+                               "input_sets": 1}
     if cpu is not None:
         paths = cpu.pop("_paths")
         mism = near = 0

@@ -14,6 +14,7 @@ using namespace dfs;
 namespace {
 
 constexpr int64_t kMaxV = 2147483647;  // token ids are int32
+constexpr int64_t kMaxD = DFS_MAX_D;    // the gate's 32-bit buffer offsets
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int esize(dfs_dtype_t t) { return t == DFS_BF16 ? 2 : 4; }
@@ -61,7 +62,7 @@ int check_gate_args(const void* hidden, const void* W_h, int dt, int64_t rows, i
   if (!hidden || !W_h || !out) return DFS_E_NULL;
   if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
   if (E != DFS_E) return DFS_E_UNSUPPORTED;
-  if (rows < 1 || d < 1) return DFS_E_SHAPE;
+  if (rows < 1 || d < 1 || d > kMaxD) return DFS_E_SHAPE;
   if (d % 8 != 0) return DFS_E_UNSUPPORTED;
   if (!aligned(hidden, 16) || !aligned(W_h, 16) || !aligned(out, 4)) return DFS_E_ALIGN;
   return DFS_OK;
@@ -105,7 +106,8 @@ int check_shape(const dfs_shape_t* s) {
   if (!s) return DFS_E_NULL;
   if (!valid_dtype(s->logits_dtype) || !valid_dtype(s->act_dtype) || !valid_dtype(s->table_dtype))
     return DFS_E_UNSUPPORTED;
-  if (s->batch < 1 || s->L < 1 || s->L > DFS_MAX_L || s->V < DFS_K || s->V > kMaxV || s->d < 1)
+  if (s->batch < 1 || s->L < 1 || s->L > DFS_MAX_L || s->V < DFS_K || s->V > kMaxV || s->d < 1 ||
+      s->d > kMaxD)
     return DFS_E_SHAPE;
   if (s->d % 8 != 0) return DFS_E_UNSUPPORTED;
   if (s->batch > (int64_t)1 << 30) return DFS_E_SHAPE;
@@ -152,7 +154,7 @@ int dfs_topk(const void* logits, dfs_dtype_t dt, int64_t rows, int64_t V, int k,
 }
 
 size_t dfs_gate_workspace_bytes(int64_t rows, int64_t d, dfs_dtype_t dt) {
-  if (rows < 1 || d < 1 || d % 8 != 0 || !valid_dtype(dt)) return 0;
+  if (rows < 1 || d < 1 || d > kMaxD || d % 8 != 0 || !valid_dtype(dt)) return 0;
   return plan_gate(rows, d, dt == DFS_BF16).ws_bytes;
 }
 

@@ -45,63 +45,58 @@ __global__ __launch_bounds__(kPackThreads) void pack_w_kernel(const uint16_t* __
 constexpr int kGemmThreads = 512;       // 8 waves, one per 32-column slice
 constexpr int kTileM = 64;              // rows per workgroup
 constexpr int kDepth = DFS_GATE_DEPTH;  // k steps in flight per thread (register ring)
-constexpr int kLdsPitch = kKB + 8;      // bf16 per LDS row of the H tile (+16 bytes)
 constexpr int kOutPitch = kE + 4;       // fp32 per LDS row of the output tile
 
-// H piece of thread tid (< 256) for k step kb: row m0 + tid / 4, k [32 kb + 8 (tid % 4), + 8).
-// Loads are never predicated (compiler-visible branches around loads make it wait
-// for every load in flight): a piece outside H is read from a clamped address and
-// zeroed when it is stored to LDS.
-__device__ __forceinline__ uint4 load_h_piece(const uint16_t* __restrict__ H, int64_t rows, int64_t d,
-                                              int64_t m0, int64_t kb, int tid) {
-  int64_t m = m0 + ((tid & 255) >> 2);
-  int64_t k = kb * kKB + 8 * (tid & 3);  // d % 8 == 0: the 8 values are all in or all out
-  m = m < rows ? m : rows - 1;
-  k = k < d ? k : d - 8;
-  return *reinterpret_cast<const uint4*>(H + m * d + k);
-}
-
-__device__ __forceinline__ bool h_piece_valid(int64_t rows, int64_t d, int64_t m0, int64_t kb,
-                                              int tid) {
-  return m0 + ((tid & 255) >> 2) < rows && kb * kKB + 8 * (tid & 3) < d;
-}
-
-// W_h operand of lane (r, q) for k step kb and output column n: the packed
-// slab holds column n's 32 k values contiguously, so this is one 16-byte load in
-// MFMA operand order.
-__device__ __forceinline__ uint4 load_w_frag(const uint16_t* __restrict__ Wp, int64_t kb, int n,
-                                             int q) {
-  return *reinterpret_cast<const uint4*>(Wp + (kb * kE + n) * kKB + 8 * q);
+// Buffer loads (base and range in scalar registers, a fixed 32-bit offset per
+// lane, the k step as a scalar offset): the per-step address work is scalar, and
+// the hardware range check returns zeros for H rows past the end of the matrix.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Z tile [64 rows x 256 columns] of one K split.  Wave w owns columns
 // [32 w, + 32) of all 64 rows: 8 MFMA tiles.  Per k step the H tile (64 x 32,
 // shared by all waves) goes through one of two LDS buffers with one barrier, and
 // each wave's W_h fragments (its own columns, fetched by no other wave) go straight
-// from memory to registers; both are loaded kDepth steps ahead of use.  The result is transposed through
-// LDS so that every row is stored as contiguous 16-byte pieces.
+// from memory to registers; both are loaded kDepth steps ahead of use.  The result
+// is transposed through LDS so that every row is stored as contiguous 16-byte pieces.
 __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t* __restrict__ H,
                                                                  const uint16_t* __restrict__ Wp,
                                                                  int64_t rows, int64_t d,
                                                                  int64_t kchunk, int splits,
                                                                  float* __restrict__ partial,
                                                                  float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kLdsPitch];
+  constexpr int kPitch = kKB + 16;  // bf16 per LDS row of the H tile (+32 bytes: fewest bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kPitch];
   __shared__ __attribute__((aligned(16))) float sOut[kTileM][kOutPitch];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int r = lane & 15;
   const int q = lane >> 4;
-  // Workgroup id -> (K split, row tile) with the split fastest: workgroups are
-  // dealt to the 8 XCDs round-robin, so with splits dividing 8 each XCD's L2 only
-  // ever holds one K slice of the packed W_h.
   const int s = (int)(blockIdx.x % (unsigned)splits);
   const int64_t m0 = (int64_t)(blockIdx.x / (unsigned)splits) * kTileM;
-  const int64_t KB = (d + kKB - 1) / kKB;
-  const int64_t kb0 = (int64_t)s * (kchunk / kKB);
-  int64_t kb1 = kb0 + kchunk / kKB;
+  const int KB = (int)((d + kKB - 1) / kKB);
+  const int kb0 = s * (int)(kchunk / kKB);
+  int kb1 = kb0 + (int)(kchunk / kKB);
   if (kb1 > KB) kb1 = KB;
+
+  // H: rows [m0, rows) of this tile; thread tid < 256 holds row tid / 4, k 8 (tid % 4) of a step
+  const int64_t tile_rows = rows - m0 < kTileM ? rows - m0 : kTileM;
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(H + m0 * d), (short)0, (int)(tile_rows * d * 2), kRawBufferWord3);
+  const int hk = 8 * (tid & 3);
+  const uint32_t hvoff = (uint32_t)((((tid & 255) >> 2) * d + hk) * 2);
+  const bool last_ok = (int64_t)(KB - 1) * kKB + hk < d;  // this piece of the last slab is inside d
+  // W_h: packed slabs [KB][256][32]
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Wp), (short)0, (int)((int64_t)KB * kE * kKB * 2), kRawBufferWord3);
+  const int nb = 32 * wave + r;
+  const uint32_t wvoff0 = (uint32_t)((nb * kKB + 8 * q) * 2);
+  const uint32_t wvoff1 = wvoff0 + 16 * kKB * 2;
 
   f32x4 acc[4][2];
 #pragma unroll
@@ -109,22 +104,20 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // register ring of kDepth k steps: H piece (threads < 256) and two W_h fragments
   uint4 ra[kDepth], rb0[kDepth], rb1[kDepth];
-  const int nb = 32 * wave + r;
-  auto fill = [&](int j, int64_t kb) {
-    ra[j] = load_h_piece(H, rows, d, m0, kb, tid);
-    rb0[j] = load_w_frag(Wp, kb, nb, q);
-    rb1[j] = load_w_frag(Wp, kb, nb + 16, q);
+  auto fill = [&](int j, int kb) {
+    ra[j] = bload(hrs, hvoff, (uint32_t)kb * kKB * 2);
+    rb0[j] = bload(wrs, wvoff0, (uint32_t)kb * kE * kKB * 2);
+    rb1[j] = bload(wrs, wvoff1, (uint32_t)kb * kE * kKB * 2);
   };
 #pragma unroll
   for (int j = 0; j < kDepth; ++j) fill(j, kb0 + j < kb1 ? kb0 + j : kb1 - 1);
 
-  auto step = [&](int64_t kb, uint4 a, uint4 b0, uint4 b1) {
-    const int st = (int)((kb - kb0) & 1);
+  auto step = [&](int kb, uint4 a, uint4 b0, uint4 b1) {
+    const int st = (kb - kb0) & 1;
     if (tid < 256) {
-      const uint32_t keep = h_piece_valid(rows, d, m0, kb, tid) ? 0xffffffffu : 0u;
-      *reinterpret_cast<uint4*>(&sA[st][tid >> 2][8 * (tid & 3)]) =
+      const uint32_t keep = (kb < KB - 1 || last_ok) ? 0xffffffffu : 0u;
+      *reinterpret_cast<uint4*>(&sA[st][tid >> 2][hk]) =
           make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep);
     }
     __syncthreads();
@@ -137,9 +130,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[nt], acc[mt][nt], 0, 0, 0);
     }
   };
-  // Full batches of kDepth steps, branch-free: each slot is consumed, then refilled
-  // with the step kDepth ahead (past the end: a harmless reload of the last step).
-  int64_t base = kb0;
+  int base = kb0;
   for (; base + kDepth <= kb1; base += kDepth) {
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) {
@@ -147,12 +138,10 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
       fill(j, base + j + kDepth < kb1 ? base + j + kDepth : kb1 - 1);
     }
   }
-  // The last (kb1 - base) < kDepth steps are already in slots 0, 1, ...
 #pragma unroll
   for (int j = 0; j < kDepth; ++j)
     if (base + j < kb1) step(base + j, ra[j], rb0[j], rb1[j]);
 
-  // lane holds D[4q + i][r] of each 16x16 tile -> LDS, then row-contiguous stores
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -161,7 +150,6 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
       for (int i = 0; i < 4; ++i)
         sOut[16 * mt + 4 * q + i][32 * wave + 16 * nt + r] = acc[mt][nt][i];
   __syncthreads();
-  // 64 rows x 64 float4: thread t stores float4 (t % 64) of rows t / 64, + 8, ...
   const int c4 = tid & 63;
 #pragma unroll
   for (int rr = tid >> 6; rr < kTileM; rr += kGemmThreads / 64) {

@@ -40,6 +40,10 @@ namespace {
 #ifndef DFS_TOPK_TARGET_BLOCKS
 #define DFS_TOPK_TARGET_BLOCKS 2048
 #endif
+// Where packing jobs riding along go in the grid: 1 = first, 0 = last (in the tail).
+#ifndef DFS_TOPK_PACK_FIRST
+#define DFS_TOPK_PACK_FIRST 0
+#endif
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -182,8 +186,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
   __shared__ uint32_t s_thr;
   static_assert(sizeof(s_buf) >= kPackLdsBytes, "the packing job reuses the key buffers");
 
-  if (blockIdx.x >= ntopk) {  // workgroups past the top-16 jobs pack W_h (fused selector)
-    pack_w_slab(pack.W, pack.d, pack.Wp, (int64_t)(blockIdx.x - ntopk), threadIdx.x,
+  // packing jobs (fused selector) ride in the same grid, after or before the rows
+  const int64_t job = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ntopk;
+  const int64_t bid = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x - pack.nslabs : (int64_t)blockIdx.x;
+  if (DFS_TOPK_PACK_FIRST ? job < pack.nslabs : job >= 0) {
+    pack_w_slab(pack.W, pack.d, pack.Wp, job, threadIdx.x,
                 reinterpret_cast<uint16_t(*)[kPackPitch]>(&s_buf[0][0]));
     return;
   }
@@ -191,8 +198,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int64_t row = blockIdx.x / parts;
-  const int part = blockIdx.x % parts;
+  const int64_t row = bid / parts;
+  const int part = (int)(bid % parts);
   const T* rowp = static_cast<const T*>(logits) + row * V;
   const int64_t beg = (int64_t)part * chunk;
   const int64_t end = beg + chunk < V ? beg + chunk : V;
@@ -353,8 +360,6 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
   uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
   const int64_t ntopk = p.rows * p.parts;
   const PackJob job = pack ? *pack : PackJob{nullptr, 0, nullptr, 0};
-  // the packing jobs come last: they run in the tail of the pass, on CUs the last
-  // rows leave idle
   const dim3 grid((unsigned)(ntopk + job.nslabs));
   if (bf16) {
     topk_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial,

@@ -50,11 +50,13 @@ extern "C" {
 #define DFS_K 16      /* candidates kept per block position */
 #define DFS_E 256     /* embedding and gate width */
 #define DFS_MAX_L 16  /* longest block handled; the post's blocks span 4 to 16 tokens */
+#define DFS_MAX_D (1 << 20) /* widest hidden state handled */
 
 typedef enum {
   DFS_OK = 0,
   DFS_E_NULL = 1,        /* a required pointer is NULL */
-  DFS_E_SHAPE = 2,       /* a size is out of range (batch, rows < 1; V < 16; L not in [1,16]; ...) */
+  DFS_E_SHAPE = 2,       /* a size is out of range (batch, rows < 1; V < 16; L not in [1,16];
+                            d not in [1, DFS_MAX_D]; ...) */
   DFS_E_UNSUPPORTED = 3, /* k != 16, E != 256, an unknown dtype or walk mode, or d not a multiple of 8 */
   DFS_E_WORKSPACE = 4,   /* workspace NULL or smaller than the matching *_workspace_bytes() */
   DFS_E_ALIGN = 5,       /* a pointer is not aligned as documented */
@@ -75,7 +77,7 @@ typedef struct {
   int64_t batch;             /* sequences, >= 1 */
   int64_t L;                 /* block positions per sequence, 1..16 */
   int64_t V;                 /* vocabulary size, 16..2^31-1 */
-  int64_t d;                 /* drafter hidden width, >= 8, multiple of 8 */
+  int64_t d;                 /* drafter hidden width, 8..DFS_MAX_D, multiple of 8 */
   dfs_dtype_t logits_dtype;  /* logits */
   dfs_dtype_t act_dtype;     /* hidden and W_h */
   dfs_dtype_t table_dtype;   /* A and B */

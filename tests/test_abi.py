@@ -77,6 +77,8 @@ def test_gate_validation(L):
     assert g(E=128) == E_UNSUP
     assert g(d=60) == E_UNSUP
     assert g(rows=0) == E_SHAPE
+    assert g(d=(1 << 20) + 8) == E_SHAPE  # wider than DFS_MAX_D
+    assert L.dfs_gate_workspace_bytes(4, (1 << 20) + 8, 1) == 0
     assert g(h=P + 8) == E_ALIGN
     assert g(ws=None, wsb=0) == E_WS
 
@@ -120,7 +122,7 @@ def test_select_validation(L):
     assert s(ws=P + 64) == E_ALIGN
     assert s(wsb=16) == E_WS
     assert s(ws=None) == E_WS
-    for bad in [dict(batch=0), dict(L=17), dict(V=3), dict(d=0)]:
+    for bad in [dict(batch=0), dict(L=17), dict(V=3), dict(d=0), dict(d=(1 << 20) + 8)]:
         sh = dfs._Shape(2, 4, 1000, 64, 1, 1, 1)
         for k_, v_ in bad.items():
             setattr(sh, k_, v_)
