@@ -15,6 +15,9 @@ Pinning status (what each function is checked against, in tests/):
   walk (greedy)  zero bilinear -> per-position top-1; planted chain; lexicographic
                  brute force over all 16^L paths for L <= 4
   walk (gumbel)  Gumbel-max frequencies vs softmax (chi-square); T -> 0 == greedy
+  viterbi        brute force (math.fsum) over all 16^L paths for L <= 4; zero
+                 bilinear -> per-position top-1; a planted path greedy misses;
+                 per-position shifts change nothing; all-equal scores -> slot 0
   philox4x32_10  rocRAND's header-only Philox4x32-10 compiled for the host
 """
 from .philox import gumbel, philox4x32_10, uniform_from_word
@@ -26,6 +29,7 @@ from .selector import (
     select_sequence,
     top16,
     top16_rows,
+    viterbi,
     walk,
     widen,
 )
@@ -41,6 +45,7 @@ __all__ = [
     "top16",
     "top16_rows",
     "uniform_from_word",
+    "viterbi",
     "walk",
     "widen",
 ]

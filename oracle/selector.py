@@ -119,12 +119,14 @@ def walk(S: np.ndarray, cand_idx: np.ndarray, mode: str = "greedy", temperature:
     """One walk over precomputed scores, from the last verified token.
 
     Greedy: at each step take the best successor of the previous pick (lowest
-    slot on ties).  Gumbel: take argmax_j S/T + g(seed, b, t, j), which draws the
+    slot on ties).  Viterbi: the path of largest total score (see ``viterbi``).  Gumbel: take argmax_j S/T + g(seed, b, t, j), which draws the
     successor from softmax(S/T) over the 16 candidates (wpnews.pro, "A Lightweight
     Path Selector": sampling uses the same scores).
     Returns (path int64 [L], scores fp64 [L], slots int64 [L], margins fp64 [L]);
     margins[t] is best minus second best of the (noised) row used at step t.
     """
+    if mode == "viterbi":
+        return viterbi(S, cand_idx)
     L = S.shape[0]
     path = np.empty(L, np.int64)
     scores = np.empty(L, np.float64)
@@ -149,6 +151,51 @@ def walk(S: np.ndarray, cand_idx: np.ndarray, mode: str = "greedy", temperature:
         scores[t] = row[j]
         slots[t] = j
         i = j
+    return path, scores, slots, margins
+
+
+def viterbi(S: np.ndarray, cand_idx: np.ndarray):
+    """The path whose summed pair scores are largest, by dynamic programming.
+
+    The post calls pairwise scoring the simplest selector and leaves better ones
+    open (wpnews.pro, "A Lightweight Path Selector"); the greedy walk takes the
+    best successor step by step, this takes the best whole path over the same
+    [L, 16, 16] scores.  best[0][j] = S_0(prev, j); best[t][j] =
+    max_i best[t-1][i] + S_t(i, j), keeping the lowest i among equal values; the
+    last slot is the lowest j of largest best[L-1][j]; the path is read back.
+    Returns (path, scores, slots, margins) like ``walk``; scores[t] is
+    S_t(slot[t-1], slot[t]) and margins holds the gap between the best and the
+    second best choice at every decision taken on the way back (final slot, then
+    each predecessor), so every other path totals at least min(margins) less.
+    """
+    L = S.shape[0]
+    best = S[0, 0].astype(np.float64).copy()
+    back = np.zeros((L, K), np.int64)
+    for t in range(1, L):
+        cand = best[:, None] + S[t]  # [i, j]: best path to i, then step i -> j
+        back[t] = np.argmax(cand, axis=0)  # first maximum -> lowest i
+        best = cand[back[t], np.arange(K)]
+    slots = np.empty(L, np.int64)
+    margins = np.empty(L, np.float64)
+
+    def gap(v):
+        srt = np.sort(v)
+        return srt[-1] - srt[-2]
+
+    slots[L - 1] = int(np.argmax(best))
+    margins[L - 1] = gap(best)
+    # recompute the DP tables to read the decision gaps on the way back
+    table = [S[0, 0].astype(np.float64).copy()]
+    for t in range(1, L):
+        table.append((table[-1][:, None] + S[t]).max(axis=0))
+    for t in range(L - 1, 0, -1):
+        slots[t - 1] = back[t, slots[t]]
+        margins[t - 1] = gap(table[t - 1] + S[t][:, slots[t]])
+    scores = np.empty(L, np.float64)
+    scores[0] = S[0, 0, slots[0]]
+    for t in range(1, L):
+        scores[t] = S[t, slots[t - 1], slots[t]]
+    path = np.array([cand_idx[t, slots[t]] for t in range(L)], np.int64)
     return path, scores, slots, margins
 
 

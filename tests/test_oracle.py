@@ -256,6 +256,84 @@ def test_greedy_walk_is_lexicographic_max_over_all_paths(L):
     np.testing.assert_array_equal(slots, best)
 
 
+def _viterbi_brute(S):
+    """Largest summed score over all 16^L slot paths (math.fsum), with its paths."""
+    L = S.shape[0]
+    totals = {}
+    for js in itertools.product(range(16), repeat=L):
+        terms, prev = [], 0
+        for t, j in enumerate(js):
+            terms.append(S[t, prev, j])
+            prev = j
+        totals[js] = math.fsum(terms)
+    top = max(totals.values())
+    return top, [js for js, v in totals.items() if v == top]
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_viterbi_is_the_best_total_over_all_paths(L):
+    S = RNG.standard_normal((L, 16, 16))
+    S[0] = S[0, 0][None, :]
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    path, scores, slots, margins = oracle.viterbi(S, cidx)
+    top, argtops = _viterbi_brute(S)
+    assert len(argtops) == 1  # continuous scores: one optimum
+    np.testing.assert_array_equal(slots, argtops[0])
+    assert abs(math.fsum(scores) - top) < 1e-12
+    np.testing.assert_array_equal(path, cidx[np.arange(L), slots])
+    # every other path totals at least min(margins) less
+    second = max(math.fsum(S[t, (0 if t == 0 else js[t - 1]), js[t]] for t in range(L))
+                 for js in itertools.product(range(16), repeat=L) if list(js) != list(slots)) \
+        if L <= 2 else None
+    if second is not None:
+        assert top - second >= margins.min() - 1e-12
+
+
+def test_viterbi_ties_take_lowest_slots():
+    L = 3
+    S = np.round(RNG.standard_normal((L, 16, 16)), 0)  # integer values: many equal totals
+    S[0] = S[0, 0][None, :]
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    _, _, slots, _ = oracle.viterbi(S, cidx)
+    top, argtops = _viterbi_brute(S)
+    assert tuple(slots) in argtops
+    # with every score equal the read-back takes slot 0 everywhere
+    _, _, slots0, margins0 = oracle.viterbi(np.zeros((L, 16, 16)), cidx)
+    np.testing.assert_array_equal(slots0, np.zeros(L, np.int64))
+    assert (margins0 == 0).all()
+
+
+def test_viterbi_zero_bilinear_is_per_position_top1():
+    L = 6
+    U = RNG.standard_normal((L, 16))
+    S = np.broadcast_to(U[:, None, :], (L, 16, 16)).copy()
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    _, _, slots, _ = oracle.viterbi(S, cidx)
+    np.testing.assert_array_equal(slots, U.argmax(axis=1))
+
+
+def test_viterbi_finds_the_path_greedy_misses():
+    # step 0 prefers slot 0 by 0.1, but only slot 1 leads to a +10 successor
+    S = np.zeros((2, 16, 16))
+    S[0, :, 0], S[0, :, 1] = 1.0, 0.9
+    S[1, 1, 5] = 10.0
+    cidx = np.stack([np.arange(16) + 100, np.arange(16) + 200])
+    g_path, *_ = oracle.walk(S, cidx)
+    v_path, v_scores, v_slots, _ = oracle.walk(S, cidx, "viterbi")
+    np.testing.assert_array_equal(g_path, [100, 200])
+    np.testing.assert_array_equal(v_path, [101, 205])
+    np.testing.assert_array_equal(v_scores, [0.9, 10.0])
+
+
+def test_viterbi_ignores_per_position_shifts():
+    L = 5
+    S = RNG.standard_normal((L, 16, 16))
+    S[0] = S[0, 0][None, :]
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    shifted = S + RNG.standard_normal(L)[:, None, None] * 10
+    np.testing.assert_array_equal(oracle.viterbi(S, cidx)[2], oracle.viterbi(shifted, cidx)[2])
+
+
 def test_gumbel_walk_tiny_temperature_is_greedy():
     L = 8
     S = RNG.permutation(L * 256).reshape(L, 16, 16) * 1e-3  # distinct, margins >= 1e-3
