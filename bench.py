@@ -145,20 +145,22 @@ def _oracle_worker(args):
     import oracle
     from workloads import make
 
-    name, seqs = args
+    name, walk, seqs = args
     with threadpool_limits(1):
-        inp = make(name, seqs=seqs, threads=1)
+        from workloads import variant
+
+        inp = make(variant(name, walk=walk, name=name), seqs=seqs, threads=1)
         t0 = time.perf_counter()
         res = oracle.select(inp)
         dt = time.perf_counter() - t0
     return [(int(s), r.path.tolist(), r.margins.tolist()) for s, r in zip(seqs, res)], dt
 
 
-def cpu_baseline(name: str, batch: int, target_cpu_s: float, workers: int) -> dict:
+def cpu_baseline(name: str, walk: str, batch: int, target_cpu_s: float, workers: int) -> dict:
     """Time the oracle on a bounded sample of the workload's sequences (no GPU touched)."""
     import multiprocessing as mp
 
-    probe, t1 = _oracle_worker((name, [0]))
+    probe, t1 = _oracle_worker((name, walk, [0]))
     per_seq = max(t1, 1e-3)
     nseq = int(min(batch, max(workers, round(target_cpu_s / per_seq))))
     seqs = list(range(nseq))
@@ -166,7 +168,7 @@ def cpu_baseline(name: str, batch: int, target_cpu_s: float, workers: int) -> di
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(len(chunks)) as pool:
-        parts = pool.map(_oracle_worker, [(name, c) for c in chunks])
+        parts = pool.map(_oracle_worker, [(name, walk, c) for c in chunks])
     wall = time.perf_counter() - t0
     rows = sorted([r for p, _ in parts for r in p])
     cpu_s = sum(dt for _, dt in parts)
@@ -189,6 +191,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="throughput")
+    ap.add_argument("--walk", choices=["greedy", "gumbel", "viterbi"],
+                    help="walk mode instead of the workload's own (its temperature and seed are kept)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU work of the baseline sample")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -217,6 +221,10 @@ def main() -> int:
     from workloads import config_by_name, make
 
     cfg = config_by_name(args.workload)
+    if args.walk and args.walk != cfg.walk:
+        from workloads import variant
+
+        cfg = variant(cfg, walk=args.walk, name=cfg.name)
     print(f"[bench] generating workload {cfg.name}: batch {cfg.batch} L {cfg.L} V {cfg.V} d {cfg.d}",
           file=sys.stderr, flush=True)
     inp = make(cfg)
@@ -224,7 +232,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (before the GPU is touched)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg.name, cfg.batch, args.cpu_seconds, max(1, min(16, _affinity())))
+        cpu = cpu_baseline(cfg.name, cfg.walk, cfg.batch, args.cpu_seconds, max(1, min(16, _affinity())))
 
     import torch
 

@@ -31,8 +31,8 @@ K = 16
 E = 256
 MAX_L = 16
 F32, BF16 = 0, 1
-GREEDY, GUMBEL = 0, 1
-_MODES = {"greedy": GREEDY, "gumbel": GUMBEL, "sampled": GUMBEL}
+GREEDY, GUMBEL, VITERBI = 0, 1, 2
+_MODES = {"greedy": GREEDY, "gumbel": GUMBEL, "sampled": GUMBEL, "viterbi": VITERBI}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

@@ -69,7 +69,8 @@ int check_gate_args(const void* hidden, const void* W_h, int dt, int64_t rows, i
 }
 
 int check_walk_mode(int mode, double temperature) {
-  if (mode != DFS_WALK_GREEDY && mode != DFS_WALK_GUMBEL) return DFS_E_UNSUPPORTED;
+  if (mode != DFS_WALK_GREEDY && mode != DFS_WALK_GUMBEL && mode != DFS_WALK_VITERBI)
+    return DFS_E_UNSUPPORTED;
   if (mode == DFS_WALK_GUMBEL && !(std::isfinite(temperature) && temperature > 0.0))
     return DFS_E_ARG;
   return DFS_OK;

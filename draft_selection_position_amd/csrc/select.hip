@@ -70,7 +70,7 @@ __device__ __forceinline__ double gumbel_noise(uint64_t seed, uint32_t b, uint32
 // itself: from slot 0 at t = 0 (every row of position 0 is the verified token's
 // row) follow the successor table, one dependent LDS read per step.
 struct WalkTables {
-  int32_t next[kMaxL][kK];  // successor slot of (t, a)
+  int32_t next[kMaxL][kK];  // successor slot of (t, a); best-path walk: best predecessor of (t, j)
   float best[kMaxL][kK];    // S_t(a, next) (the score without noise)
   int32_t cand[kMaxL][kK];  // token id of (t, slot)
 };
@@ -122,6 +122,56 @@ __device__ __forceinline__ void successors(const float (&s)[4], int t, int lane,
         w.next[t][4 * q + i] = j;
         w.best[t][4 * q + i] = raw;
       }
+    }
+  }
+}
+
+// The path of largest summed score (walk mode 2), by dynamic programming over
+// the whole [L, 16, 16] score tensor `sS` (in LDS), run by one wave: lane j keeps
+// best[j], the largest total of a path ending in slot j; a step takes
+// best[i] + S_t(i, j) over i with the lowest i among equal values (best[i] comes
+// from lane i through a scalar read) and stores the choice in `back`.  The last
+// slot is the lowest j of largest best (a DPP row reduction); one lane then reads
+// the path back.
+__device__ __forceinline__ void viterbi_walk(const float (*sS)[kK][kK], int32_t (*back)[kK],
+                                             const int32_t (*cand)[kK], int64_t b, int L, int lane,
+                                             int32_t* __restrict__ out_path,
+                                             float* __restrict__ out_scores) {
+  const int j = lane & 15;
+  float v = sS[0][0][j];
+  for (int t = 1; t < L; ++t) {
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) + sS[t][0][j];
+    int bi = 0;
+#pragma unroll
+    for (int i = 1; i < kK; ++i) {
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i)) + sS[t][i][j];
+      if (c > bv) {
+        bv = c;
+        bi = i;
+      }
+    }
+    if (lane < kK) back[t][j] = bi;
+    v = bv;
+  }
+  int fj = j;
+#pragma unroll
+  for (int m = 1; m < kK; m <<= 1) {
+    const float ov = __uint_as_float(xor_lanes(__float_as_uint(v), m, lane));
+    const int oj = (int)xor_lanes((uint32_t)fj, m, lane);
+    const bool take = ov > v || (ov == v && oj < fj);
+    v = take ? ov : v;
+    fj = take ? oj : fj;
+  }
+  // the back pointers were written by other lanes of this wave
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) {
+    int a = fj;
+    for (int t = L - 1; t >= 0; --t) {
+      const int pa = t > 0 ? back[t][a] : 0;
+      out_path[b * L + t] = cand[t][a];
+      out_scores[b * L + t] = sS[t][pa][a];
+      a = pa;
     }
   }
 }
@@ -180,6 +230,7 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
     int32_t* __restrict__ out_path, float* __restrict__ out_scores) {
   __shared__ WalkTables sW;
   __shared__ __attribute__((aligned(16))) float sG[kMaxL][kE];  // gate row of each position
+  __shared__ float sS[kWalk ? kMaxL : 1][kK][kK];                // whole tiles (best-path walk)
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;  // block position of this wave
   const int64_t b = blockIdx.x;
@@ -265,9 +316,16 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
     if constexpr (kWritePair) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
   }
   if constexpr (kWalk) {
-    successors(sc, t, lane, mode, temperature, seed, b, sW);
-    __syncthreads();
-    if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+    if (mode == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sS[t][4 * q + i][r] = sc[i];
+      __syncthreads();
+      if (t == 0) viterbi_walk(sS, sW.next, sW.cand, b, L, lane, out_path, out_scores);
+    } else {
+      successors(sc, t, lane, mode, temperature, seed, b, sW);
+      __syncthreads();
+      if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+    }
   }
 }
 
@@ -281,6 +339,7 @@ __global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __rest
                                                             int32_t* __restrict__ out_path,
                                                             float* __restrict__ out_scores) {
   __shared__ WalkTables sW;
+  __shared__ float sS[kMaxL][kK][kK];
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;
   const int64_t b = blockIdx.x;
@@ -291,9 +350,16 @@ __global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __rest
 #pragma unroll
   for (int i = 0; i < 4; ++i) sc[i] = pair[(row * kK + 4 * q + i) * kK + r];
   if (lane < kK) sW.cand[t][lane] = cand_idx[row * kK + lane];
-  successors(sc, t, lane, mode, temperature, seed, b, sW);
-  __syncthreads();
-  if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+  if (mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sS[t][4 * q + i][r] = sc[i];
+    __syncthreads();
+    if (t == 0) viterbi_walk(sS, sW.next, sW.cand, b, L, lane, out_path, out_scores);
+  } else {
+    successors(sc, t, lane, mode, temperature, seed, b, sW);
+    __syncthreads();
+    if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+  }
 }
 
 template <bool kBf16, bool kWritePair, bool kWalk>

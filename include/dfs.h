@@ -69,7 +69,8 @@ typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype_t;
 
 typedef enum {
   DFS_WALK_GREEDY = 0, /* argmax successor at each step, lowest candidate slot on ties */
-  DFS_WALK_GUMBEL = 1  /* Gumbel-max draw from softmax(S / temperature) over the 16 candidates */
+  DFS_WALK_GUMBEL = 1, /* Gumbel-max draw from softmax(S / temperature) over the 16 candidates */
+  DFS_WALK_VITERBI = 2 /* the path of largest summed score (dynamic programming), see dfs_walk */
 } dfs_walk_t;
 
 /* Shape of one dfs_select call. */
@@ -131,9 +132,16 @@ int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_
  *   gumbel:  j* = argmax_j pair[b,t,i,j] / temperature + g(seed, b, t, j), in fp64,
  *            g = -log(-log(u)), u = ((x >> 9) + 0.5) * 2^-23, x = word 0 of
  *            Philox4x32-10 with counter (j, t, b, 0) and key (seed low, seed high).
+ *   viterbi: the slot path maximising sum_t pair[b, t, j_{t-1}, j_t] (j_{-1} = 0), found
+ *            by dynamic programming in fp32: best_0[j] = pair[b,0,0,j], best_t[j] =
+ *            max_i best_{t-1}[i] + pair[b,t,i,j] keeping the lowest i on ties, last
+ *            slot the lowest j of largest best_{L-1}[j], read back from there.  The
+ *            pages leave better selectors than the greedy one open (blog post, section
+ *            "A Lightweight Path Selector"); this is the exact best path over the
+ *            same scores.
  *   out_path [batch, L] int32 = cand_idx[b, t, j*];
  *   out_scores [batch, L] fp32 = pair[b, t, i, j*] (un-noised, not divided by T).
- * temperature must be finite and > 0 in gumbel mode (ignored for greedy).          */
+ * temperature must be finite and > 0 in gumbel mode (ignored otherwise).          */
 int dfs_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L, int k,
              dfs_walk_t mode, double temperature, uint64_t seed, int32_t* out_path,
              float* out_scores, hipStream_t stream);

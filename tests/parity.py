@@ -57,6 +57,8 @@ def assert_scores(gpu, ref, what="scores"):
 def check_path(gpu_path, gpu_scores, res: "oracle.SequenceResult", mode="greedy", temperature=1.0, seed=0,
                b=0) -> dict:
     """Compare one sequence's GPU walk with the oracle's; returns a small report."""
+    if mode == "viterbi":
+        return check_best_path(gpu_path, gpu_scores, res, b)
     L = res.path.shape[0]
     near_ties = []
     conditional = False
@@ -84,3 +86,33 @@ def check_path(gpu_path, gpu_scores, res: "oracle.SequenceResult", mode="greedy"
             raise AssertionError(f"seq {b} step {t}: score {float(gpu_scores[t])!r} vs oracle {row[j]!r}")
         i_prev = j
     return {"near_ties": near_ties, "exact": not near_ties}
+
+
+def check_best_path(gpu_path, gpu_scores, res: "oracle.SequenceResult", b=0) -> dict:
+    """The GPU's best-total path against the oracle's (Viterbi): the same slots when the
+    oracle's optimum leads every other path by NEAR_TIE or more (its smallest decision gap);
+    otherwise the GPU path must total, on the oracle's fp64 scores, within NEAR_TIE of the
+    optimum.  Per-step scores within the score tolerance either way."""
+    L = res.path.shape[0]
+    slots, i_prev, total = [], 0, 0.0
+    for t in range(L):
+        hits = np.nonzero(res.cand_idx[t] == int(gpu_path[t]))[0]
+        if hits.size != 1:
+            raise AssertionError(f"seq {b} step {t}: GPU token {int(gpu_path[t])} is not a candidate")
+        j = int(hits[0])
+        s_ref = res.pair[t, i_prev, j]
+        if not scores_ok(gpu_scores[t], s_ref):
+            raise AssertionError(f"seq {b} step {t}: score {float(gpu_scores[t])!r} vs oracle {s_ref!r}")
+        total += s_ref
+        slots.append(j)
+        i_prev = j
+    best = float(np.sum(res.scores))
+    if res.margins.min() >= NEAR_TIE:
+        if not np.array_equal(np.asarray(slots), res.slots):
+            raise AssertionError(f"seq {b}: GPU best path {slots} != oracle {res.slots.tolist()} "
+                                 f"(oracle margin {res.margins.min():.3g})")
+        return {"near_ties": [], "exact": True}
+    if total < best - NEAR_TIE:
+        raise AssertionError(f"seq {b}: GPU path totals {total!r}, optimum {best!r}")
+    return {"near_ties": [] if slots == res.slots.tolist() else [int(np.argmin(res.margins))],
+            "exact": slots == res.slots.tolist()}

@@ -99,7 +99,7 @@ def test_pair_and_walk_validation(L):
         return L.dfs_walk(pair, ci, b, Lw, k, mode, T, seed, path, sc, None)
 
     assert w(pair=None) == E_NULL
-    assert w(mode=2) == E_UNSUP
+    assert w(mode=3) == E_UNSUP
     assert w(mode=1, T=0.0) == E_ARG
     assert w(mode=1, T=float("nan")) == E_ARG
     assert w(mode=1, T=float("inf")) == E_ARG

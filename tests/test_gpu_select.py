@@ -64,6 +64,12 @@ VARIANTS = [
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=256),
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=128),
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=64),
+    # the best-total-path walk
+    variant("tiny", emb_std=0.3, walk="viterbi"),
+    variant("tiny", emb_std=0.3, L=1, walk="viterbi"),
+    variant("single_stream", emb_std=0.3, batch=6, V=32001, d=512, walk="viterbi"),
+    variant("single_stream", emb_std=0.3, batch=4, L=7, tie_levels=16, d=256, walk="viterbi"),
+    variant("throughput", emb_std=0.3, batch=3, V=40000, d=1024, walk="viterbi"),
 ]
 
 
@@ -90,14 +96,16 @@ def test_select_equals_step_chain(cfg):
     import draft_selection_position_amd as dfs
 
     dev = upload(make(cfg))
-    path, scores = dfs.select(dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])
     idx, val = dfs.topk(dev["logits"])
     g = dfs.gate(dev["hidden"], dev["W_h"])
     pair = dfs.pair_scores(idx, val, dev["prev_token"], g, dev["A"], dev["B"])
-    p2, s2 = dfs.walk(pair, idx)
-    torch.cuda.synchronize()
-    assert torch.equal(path, p2)
-    assert torch.equal(scores, s2)
+    for mode, T, seed in (("greedy", 1.0, 0), ("gumbel", 0.8, 77), ("viterbi", 1.0, 0)):
+        path, scores = dfs.select(dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"],
+                                  dev["W_h"], mode=mode, temperature=T, seed=seed)
+        p2, s2 = dfs.walk(pair, idx, mode, T, seed)
+        torch.cuda.synchronize()
+        assert torch.equal(path, p2), mode
+        assert torch.equal(scores, s2), mode
 
 
 def test_select_is_deterministic(full_workload):
@@ -126,3 +134,26 @@ def test_select_equals_step_chain_full_size(name, full_workload):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(path, p2.cpu().numpy())
     np.testing.assert_array_equal(scores, s2.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", ["small_batch", "throughput"])
+def test_best_path_full_size(name, full_workload):
+    # the best-total-path walk at a full benchmark shape: sampled sequences against
+    # the oracle, every sequence's total at least the greedy walk's
+    import draft_selection_position_amd as dfs
+
+    inp, dev = full_workload(name)
+    cfg = variant(inp.config, walk="viterbi")
+    args = (dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])
+    vp, vs = dfs.select(*args, mode="viterbi")
+    gp, gs = dfs.select(*args, mode="greedy")
+    torch.cuda.synchronize()
+    vs64, gs64 = vs.cpu().double().sum(1), gs.cpu().double().sum(1)
+    assert bool((vs64 >= gs64 - 1e-3).all())
+    vp, vs = vp.cpu().numpy(), vs.cpu().numpy()
+    seqs = np.unique(np.r_[0, cfg.batch - 1, np.random.default_rng(5).choice(cfg.batch, 6, replace=False)])
+    for i in seqs:
+        res = oracle.select_sequence(inp, int(i))
+        path, scores, slots, margins = oracle.viterbi(res.pair, res.cand_idx)
+        res.path, res.scores, res.slots, res.margins = path, scores, slots, margins
+        check_path(vp[i], vs[i], res, "viterbi", b=int(inp.seq_ids[i]))

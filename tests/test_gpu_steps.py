@@ -104,7 +104,7 @@ def test_pair_scores_match_oracle(cfg):
 
 
 @pytest.mark.parametrize("cfg", PAIR_CASES, ids=lambda c: c.name)
-@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("gumbel", 1.0), ("gumbel", 0.7)])
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("gumbel", 1.0), ("gumbel", 0.7), ("viterbi", 1.0)])
 def test_walk_matches_oracle(cfg, mode, T):
     inp = make(variant(cfg, walk=mode, temperature=T, walk_seed=0xABCDEF123))
     res = _oracle_steps(inp)
@@ -115,3 +115,30 @@ def test_walk_matches_oracle(cfg, mode, T):
     path, scores = path.cpu().numpy(), scores.cpu().numpy()
     for i, r in enumerate(res):
         check_path(path[i], scores[i], r, mode, T, inp.walk_seed, int(inp.seq_ids[i]))
+
+
+def test_best_path_walk_on_planted_scores():
+    # a score tensor where the greedy walk and the best path part ways, and one
+    # where every score is equal (the read-back then takes slot 0 everywhere)
+    L, B = 5, 3
+    rng = np.random.default_rng(11)
+    S = rng.standard_normal((B, L, 16, 16)).astype(np.float32)
+    S[:, 0] = S[:, 0, :1]
+    S[0] = 0.0
+    S[1, 0, :, 0], S[1, 0, :, 1] = 3.0, 2.9
+    S[1, 1, 1, 7] = 40.0
+    cidx = np.stack([[rng.choice(5000, 16, replace=False) for _ in range(L)] for _ in range(B)])
+    pair = torch.from_numpy(S).cuda()
+    ci = torch.from_numpy(cidx.astype(np.int32)).cuda()
+    vp, vs = dfs_mod().walk(pair, ci, "viterbi")
+    gp, gs = dfs_mod().walk(pair, ci, "greedy")
+    torch.cuda.synchronize()
+    vp, vs, gp, gs = vp.cpu().numpy(), vs.cpu().numpy(), gp.cpu().numpy(), gs.cpu().numpy()
+    for b in range(B):
+        path, scores, slots, margins = oracle.viterbi(S[b].astype(np.float64), cidx[b])
+        np.testing.assert_array_equal(vp[b], path)
+        np.testing.assert_allclose(vs[b], scores, rtol=0, atol=1e-5)
+        assert vs[b].astype(np.float64).sum() >= gs[b].astype(np.float64).sum() - 1e-4
+    np.testing.assert_array_equal(vp[0], cidx[0, :, 0])
+    assert vp[1, 0] == cidx[1, 0, 1] and vp[1, 1] == cidx[1, 1, 7]
+    assert gp[1, 0] == cidx[1, 0, 0]

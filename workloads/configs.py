@@ -33,7 +33,7 @@ class Config:
     peak_margin_end: float = 0.0
     emb_std: float = 0.02  # std of A, B and W_h
     hidden_std: float = 1.0
-    walk: str = "greedy"  # "greedy" or "gumbel"
+    walk: str = "greedy"  # "greedy", "gumbel" or "viterbi"
     temperature: float = 1.0
     walk_seed: int = 0
     base_seed: int = 0xDF50
