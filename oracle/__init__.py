@@ -19,7 +19,9 @@ Pinning status (what each function is checked against, in tests/):
                  bilinear -> per-position top-1; a planted path greedy misses;
                  per-position shifts change nothing; all-equal scores -> slot 0
   philox4x32_10  rocRAND's header-only Philox4x32-10 compiled for the host
+  recall         hand-counted blocks (recall@k, accepted lengths, oracle selector)
 """
+from . import recall
 from .philox import gumbel, philox4x32_10, uniform_from_word
 from .selector import (
     SequenceResult,
@@ -40,6 +42,7 @@ __all__ = [
     "gumbel",
     "pair_scores",
     "philox4x32_10",
+    "recall",
     "select",
     "select_sequence",
     "top16",
