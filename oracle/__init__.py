@@ -20,8 +20,12 @@ Pinning status (what each function is checked against, in tests/):
                  per-position shifts change nothing; all-equal scores -> slot 0
   philox4x32_10  rocRAND's header-only Philox4x32-10 compiled for the host
   recall         hand-counted blocks (recall@k, accepted lengths, oracle selector)
+  verify         the speculative-sampling theorem (emitted tokens follow the target,
+                 chi-square), acceptance rate = sum min(p, q), q = p -> all accepted,
+                 target mass off the candidates -> rejected at once, inverse CDF by
+                 definition, draft_probs = scipy softmax
 """
-from . import recall
+from . import recall, verify
 from .philox import gumbel, philox4x32_10, uniform_from_word
 from .selector import (
     SequenceResult,
@@ -43,6 +47,7 @@ __all__ = [
     "pair_scores",
     "philox4x32_10",
     "recall",
+    "verify",
     "select",
     "select_sequence",
     "top16",
