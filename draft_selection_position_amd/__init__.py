@@ -81,6 +81,13 @@ def lib() -> ctypes.CDLL:
         L.dfs_select.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int, c_double,
                                  u64, vp, sz, i32p, f32p, vp]
         L.dfs_select.restype = c_int
+        L.dfs_select_draft.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int,
+                                       c_double, u64, vp, sz, i32p, f32p, f32p, i32p, vp]
+        L.dfs_select_draft.restype = c_int
+        L.dfs_verify_workspace_bytes.argtypes, L.dfs_verify_workspace_bytes.restype = [i64, i64, i64, c_int], sz
+        L.dfs_verify.argtypes = [vp, c_int, i64, i64, i64, i32p, i32p, f32p, c_int, c_double, u64, vp, sz,
+                                 i32p, i32p, vp]
+        L.dfs_verify.restype = c_int
         _lib = L
     return _lib
 
@@ -258,12 +265,14 @@ def select_workspace_bytes(batch: int, L: int, V: int, d: int, logits_dtype=torc
 
 def select(logits: torch.Tensor, hidden: torch.Tensor, prev_token: torch.Tensor, A: torch.Tensor,
            B: torch.Tensor, W_h: torch.Tensor, k: int = K, mode: str = "greedy", temperature: float = 1.0,
-           seed: int = 0, workspace: torch.Tensor | None = None, out=None):
+           seed: int = 0, workspace: torch.Tensor | None = None, out=None, draft: bool = False):
     """The whole selector on one draft block per sequence.
 
     logits [batch, L, V]; hidden [batch, L, d]; prev_token [batch] int32 (last
     verified token); A, B [V, 256]; W_h [d, 256].  Returns (path int32 [batch, L],
-    scores fp32 [batch, L]).  ``out`` may pass preallocated (path, scores).
+    scores fp32 [batch, L]).  ``out`` may pass preallocated (path, scores).  With
+    ``draft=True`` also the draft distributions q fp32 [batch, L, 16] and the
+    candidate ids int32 [batch, L, 16] (dfs_select_draft).
     """
     _dev(logits, "logits")
     _dev(hidden, "hidden")
@@ -286,11 +295,54 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, prev_token: torch.Tensor,
         scores = torch.empty((batch, L), dtype=torch.float32, device=logits.device)
     else:
         path, scores = out
-    _check(lib().dfs_select(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(),
-                            B.data_ptr(), W_h.data_ptr(), k, ctypes.byref(s), _MODES[mode], float(temperature),
-                            int(seed) & (2**64 - 1), _ptr(ws), nb, path.data_ptr(), scores.data_ptr(),
-                            _stream(logits.device)), "dfs_select")
-    return path, scores
+    if not draft:
+        _check(lib().dfs_select(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(),
+                                B.data_ptr(), W_h.data_ptr(), k, ctypes.byref(s), _MODES[mode],
+                                float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb, path.data_ptr(),
+                                scores.data_ptr(), _stream(logits.device)), "dfs_select")
+        return path, scores
+    q = torch.empty((batch, L, K), dtype=torch.float32, device=logits.device)
+    cand = torch.empty((batch, L, K), dtype=torch.int32, device=logits.device)
+    _check(lib().dfs_select_draft(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(),
+                                  B.data_ptr(), W_h.data_ptr(), k, ctypes.byref(s), _MODES[mode],
+                                  float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb, path.data_ptr(),
+                                  scores.data_ptr(), q.data_ptr(), cand.data_ptr(), _stream(logits.device)),
+           "dfs_select_draft")
+    return path, scores, q, cand
+
+
+def verify_workspace_bytes(batch: int, L: int, V: int, dtype: torch.dtype) -> int:
+    code = F32 if dtype == torch.float32 else BF16 if dtype == torch.bfloat16 else -1
+    return int(lib().dfs_verify_workspace_bytes(batch, L, V, code))
+
+
+def verify(target_logits: torch.Tensor, path: torch.Tensor, cand: torch.Tensor, q: torch.Tensor,
+           temperature: float = 1.0, seed: int = 0, workspace: torch.Tensor | None = None):
+    """Speculative-sampling verification of drafted blocks (see dfs_verify).
+
+    target_logits [batch, L + 1, V]; path [batch, L] int32; cand [batch, L, 16] int32 and
+    q [batch, L, 16] fp32 (``select(..., draft=True)``).  Returns (accepted int32 [batch],
+    token int32 [batch]): the number of draft tokens kept and the token drawn after them.
+    """
+    _dev(target_logits, "target_logits")
+    _dev(path, "path", torch.int32)
+    _dev(cand, "cand", torch.int32)
+    _dev(q, "q", torch.float32)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [batch, L + 1, V]")
+    batch, L1, V = target_logits.shape
+    L = L1 - 1
+    if path.shape != (batch, L) or cand.shape != (batch, L, K) or q.shape != (batch, L, K):
+        raise ValueError("path must be [batch, L], cand and q [batch, L, 16] with L + 1 target rows")
+    dt = _dtype_code(target_logits, "target_logits")
+    nb = int(lib().dfs_verify_workspace_bytes(batch, L, V, dt))
+    ws = _ws_arg(workspace, target_logits.device, nb)
+    accepted = torch.empty(batch, dtype=torch.int32, device=target_logits.device)
+    token = torch.empty(batch, dtype=torch.int32, device=target_logits.device)
+    _check(lib().dfs_verify(target_logits.data_ptr(), dt, batch, L, V, path.data_ptr(), cand.data_ptr(),
+                            q.data_ptr(), K, float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb,
+                            accepted.data_ptr(), token.data_ptr(), _stream(target_logits.device)), "dfs_verify")
+    return accepted, token
 
 
 class Selector:

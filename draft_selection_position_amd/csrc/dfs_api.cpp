@@ -117,6 +117,56 @@ int check_shape(const dfs_shape_t* s) {
 
 }  // namespace
 
+static int select_impl(const void* logits, const void* hidden, const int32_t* prev_token,
+                       const void* A, const void* B, const void* W_h, int k,
+                       const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
+                       uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+                       float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream) {
+  if (!logits || !hidden || !prev_token || !A || !B || !W_h || !out_path || !out_scores)
+    return DFS_E_NULL;
+  int st = check_shape(shape);
+  if (st != DFS_OK) return st;
+  if (k != DFS_K) return DFS_E_UNSUPPORTED;
+  if ((st = check_walk_mode(mode, temperature)) != DFS_OK) return st;
+  const dfs_shape_t s = *shape;
+  if (!aligned(logits, esize(s.logits_dtype)) || !aligned(hidden, 16) || !aligned(W_h, 16) ||
+      !aligned(A, 16) || !aligned(B, 16) || !aligned(prev_token, 4) || !aligned(out_path, 4) ||
+      !aligned(out_scores, 4))
+    return DFS_E_ALIGN;
+  const SelectLayout l = select_layout(s);
+  if (!ws || ws_bytes < l.total) return DFS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+
+  char* w = static_cast<char*>(ws);
+  int32_t* cand_idx = reinterpret_cast<int32_t*>(w + l.cand_idx_off);
+  float* cand_val = reinterpret_cast<float*>(w + l.cand_val_off);
+  float* gate = reinterpret_cast<float*>(w + l.gate_off);
+  // One stream, in order: the top-16 pass (the W_h packing slabs ride in its
+  // tail), the gate GEMM, the gate finish when the K split is wider than the pair
+  // kernel adds up itself, then pair scores and the walk in one kernel.
+  char* gws = w + l.gate_ws_off;
+  const PackJob job = gate_pack_job(l.gate, W_h, gws);
+  hipError_t e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
+                             w + l.topk_ws_off, stream, &job);
+  if (e != hipSuccess) return DFS_E_HIP;
+  if ((e = launch_gate_gemm(l.gate, hidden, W_h, gate, gws, stream)) != hipSuccess) return DFS_E_HIP;
+  GateSrc gs{gate, 1, 0};
+  if (l.gate.splits > 1) {
+    if (l.gate.splits <= pair_max_gate_splits()) {
+      gs = GateSrc{gate_partials(l.gate, gws), l.gate.splits, s.batch * s.L * DFS_E};
+    } else if ((e = launch_gate_finish(l.gate, gate, gws, stream)) != hipSuccess) {
+      return DFS_E_HIP;
+    }
+  }
+  const WalkArgs wa{(int)mode, temperature, seed, out_q, out_cand};
+  e = launch_pair_walk(cand_idx, cand_val, prev_token, gs, A, B, s.table_dtype == DFS_BF16,
+                       s.batch, s.L, s.V, nullptr, &wa, out_path, out_scores, stream);
+  return hip_status(e);
+}
+
+
 extern "C" {
 
 int dfs_abi_version(void) { return DFS_ABI_VERSION; }
@@ -216,48 +266,49 @@ int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token
                const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
                double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                float* out_scores, hipStream_t stream) {
-  if (!logits || !hidden || !prev_token || !A || !B || !W_h || !out_path || !out_scores)
-    return DFS_E_NULL;
-  int st = check_shape(shape);
-  if (st != DFS_OK) return st;
-  if (k != DFS_K) return DFS_E_UNSUPPORTED;
-  if ((st = check_walk_mode(mode, temperature)) != DFS_OK) return st;
-  const dfs_shape_t s = *shape;
-  if (!aligned(logits, esize(s.logits_dtype)) || !aligned(hidden, 16) || !aligned(W_h, 16) ||
-      !aligned(A, 16) || !aligned(B, 16) || !aligned(prev_token, 4) || !aligned(out_path, 4) ||
-      !aligned(out_scores, 4))
-    return DFS_E_ALIGN;
-  const SelectLayout l = select_layout(s);
-  if (!ws || ws_bytes < l.total) return DFS_E_WORKSPACE;
-  if (!aligned(ws, 256)) return DFS_E_ALIGN;
-  if ((st = check_device()) != DFS_OK) return st;
-  (void)hipGetLastError();
+  return select_impl(logits, hidden, prev_token, A, B, W_h, k, shape, mode, temperature, seed, ws,
+                     ws_bytes, out_path, out_scores, nullptr, nullptr, stream);
+}
 
-  char* w = static_cast<char*>(ws);
-  int32_t* cand_idx = reinterpret_cast<int32_t*>(w + l.cand_idx_off);
-  float* cand_val = reinterpret_cast<float*>(w + l.cand_val_off);
-  float* gate = reinterpret_cast<float*>(w + l.gate_off);
-  // One stream, in order: the top-16 pass (the W_h packing slabs ride in its
-  // tail), the gate GEMM, the gate finish when the K split is wider than the pair
-  // kernel adds up itself, then pair scores and the walk in one kernel.
-  char* gws = w + l.gate_ws_off;
-  const PackJob job = gate_pack_job(l.gate, W_h, gws);
-  hipError_t e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
-                             w + l.topk_ws_off, stream, &job);
-  if (e != hipSuccess) return DFS_E_HIP;
-  if ((e = launch_gate_gemm(l.gate, hidden, W_h, gate, gws, stream)) != hipSuccess) return DFS_E_HIP;
-  GateSrc gs{gate, 1, 0};
-  if (l.gate.splits > 1) {
-    if (l.gate.splits <= pair_max_gate_splits()) {
-      gs = GateSrc{gate_partials(l.gate, gws), l.gate.splits, s.batch * s.L * DFS_E};
-    } else if ((e = launch_gate_finish(l.gate, gate, gws, stream)) != hipSuccess) {
-      return DFS_E_HIP;
-    }
-  }
-  const WalkArgs wa{(int)mode, temperature, seed};
-  e = launch_pair_walk(cand_idx, cand_val, prev_token, gs, A, B, s.table_dtype == DFS_BF16,
-                       s.batch, s.L, s.V, nullptr, &wa, out_path, out_scores, stream);
-  return hip_status(e);
+int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev_token,
+                     const void* A, const void* B, const void* W_h, int k,
+                     const dfs_shape_t* shape, dfs_walk_t mode, double temperature, uint64_t seed,
+                     void* ws, size_t ws_bytes, int32_t* out_path, float* out_scores,
+                     float* out_q, int32_t* out_cand, hipStream_t stream) {
+  if (!out_q || !out_cand) return DFS_E_NULL;
+  if (!aligned(out_q, 4) || !aligned(out_cand, 4)) return DFS_E_ALIGN;
+  if (!(std::isfinite(temperature) && temperature > 0.0)) return DFS_E_ARG;
+  return select_impl(logits, hidden, prev_token, A, B, W_h, k, shape, mode, temperature, seed, ws,
+                     ws_bytes, out_path, out_scores, out_q, out_cand, stream);
+}
+
+size_t dfs_verify_workspace_bytes(int64_t batch, int64_t L, int64_t V, dfs_dtype_t dt) {
+  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K || V > kMaxV ||
+      !valid_dtype(dt))
+    return 0;
+  return plan_verify(batch, L, V, esize(dt)).ws_bytes;
+}
+
+int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t L, int64_t V,
+               const int32_t* path, const int32_t* cand, const float* q, int k, double temperature,
+               uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_accepted, int32_t* out_token,
+               hipStream_t stream) {
+  if (!target_logits || !path || !cand || !q || !out_accepted || !out_token || !ws)
+    return DFS_E_NULL;
+  if (!valid_dtype(dt) || k != DFS_K) return DFS_E_UNSUPPORTED;
+  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K || V > kMaxV)
+    return DFS_E_SHAPE;
+  if (!(std::isfinite(temperature) && temperature > 0.0)) return DFS_E_ARG;
+  if (!aligned(target_logits, esize(dt)) || !aligned(path, 4) || !aligned(cand, 4) ||
+      !aligned(q, 4) || !aligned(out_accepted, 4) || !aligned(out_token, 4) || !aligned(ws, 256))
+    return DFS_E_ALIGN;
+  const VerifyPlan p = plan_verify(batch, L, V, esize(dt));
+  if (ws_bytes < p.ws_bytes) return DFS_E_WORKSPACE;
+  int st = check_device();
+  if (st != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_verify(p, target_logits, dt == DFS_BF16, path, cand, q, temperature,
+                                  seed, ws, out_accepted, out_token, stream));
 }
 
 }  // extern "C"

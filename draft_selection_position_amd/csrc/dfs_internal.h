@@ -62,9 +62,11 @@ const float* gate_partials(const GatePlan& p, const void* ws);
 
 // ---------------------------------------------------------------- pair scores and walk
 struct WalkArgs {
-  int mode;  // 0 greedy, 1 gumbel
+  int mode;  // 0 greedy, 1 gumbel, 2 best path
   double temperature;
   uint64_t seed;
+  float* out_q = nullptr;       // optional [B, L, 16] draft distributions (fused walk only)
+  int32_t* out_cand = nullptr;  // with out_q: [B, L, 16] candidate ids
 };
 // Where the pair kernel finds the gate: the finished gate [rows, 256] (splits 1),
 // or up to pair_max_gate_splits() K-split partial sums [splits, rows, 256], `stride`
@@ -85,5 +87,18 @@ hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
 hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L,
                        const WalkArgs& walk, int32_t* out_path, float* out_scores,
                        hipStream_t stream);
+
+// ---------------------------------------------------------------- verification
+struct VerifyPlan {
+  int64_t batch, L, V;
+  int esize;       // bytes per target logit
+  int parts;       // chunks per target row in the log-sum-exp pass
+  int64_t chunk;   // elements per chunk
+  size_t ws_bytes; // (max, sum) pairs [batch * (L + 1), parts]
+};
+VerifyPlan plan_verify(int64_t batch, int64_t L, int64_t V, int esize);
+hipError_t launch_verify(const VerifyPlan& p, const void* logits, bool bf16, const int32_t* path,
+                         const int32_t* cand, const float* q, double temperature, uint64_t seed,
+                         void* ws, int32_t* out_accepted, int32_t* out_token, hipStream_t stream);
 
 }  // namespace dfs

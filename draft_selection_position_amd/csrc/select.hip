@@ -23,6 +23,7 @@
 // chain through LDS.
 #include "dfs_device.h"
 #include "dfs_internal.h"
+#include "philox.h"
 
 namespace dfs {
 namespace {
@@ -32,31 +33,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxL = 16;
 
-// ---------------------------------------------------------------- Philox4x32-10
-// Counter-based generator of Salmon, Moraes, Dror and Shaw (SC'11): ten rounds
-// of two 32x32->64 multiplies and xors, key advanced by two Weyl constants.
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-  return c0;
-}
-
 // Standard Gumbel noise for (sequence b, position t, slot j), fp64:
 // u = ((x >> 9) + 1/2) 2^-23 in (0, 1), g = -log(-log u).
 __device__ __forceinline__ double gumbel_noise(uint64_t seed, uint32_t b, uint32_t t, uint32_t j) {
-  const uint32_t x = philox_word0(j, t, b, 0u, (uint32_t)seed, (uint32_t)(seed >> 32));
-  const double u = ((double)(x >> 9) + 0.5) * 0x1p-23;
+  uint32_t w[4];
+  philox4x32_10(j, t, b, 0u, (uint32_t)seed, (uint32_t)(seed >> 32), w);
+  const uint32_t x = w[0];
+  const double u = uniform23(x);
   return -log(-log(u));
 }
 
@@ -73,6 +56,7 @@ struct WalkTables {
   int32_t next[kMaxL][kK];  // successor slot of (t, a); best-path walk: best predecessor of (t, j)
   float best[kMaxL][kK];    // S_t(a, next) (the score without noise)
   int32_t cand[kMaxL][kK];  // token id of (t, slot)
+  int32_t slot[kMaxL];      // the walk's slot at each position
 };
 
 __device__ __forceinline__ void successors(const float (&s)[4], int t, int lane, int mode,
@@ -134,8 +118,8 @@ __device__ __forceinline__ void successors(const float (&s)[4], int t, int lane,
 // slot is the lowest j of largest best (a DPP row reduction); one lane then reads
 // the path back.
 __device__ __forceinline__ void viterbi_walk(const float (*sS)[kK][kK], int32_t (*back)[kK],
-                                             const int32_t (*cand)[kK], int64_t b, int L, int lane,
-                                             int32_t* __restrict__ out_path,
+                                             const int32_t (*cand)[kK], int32_t* slot_out, int64_t b,
+                                             int L, int lane, int32_t* __restrict__ out_path,
                                              float* __restrict__ out_scores) {
   const int j = lane & 15;
   float v = sS[0][0][j];
@@ -169,6 +153,7 @@ __device__ __forceinline__ void viterbi_walk(const float (*sS)[kK][kK], int32_t 
     int a = fj;
     for (int t = L - 1; t >= 0; --t) {
       const int pa = t > 0 ? back[t][a] : 0;
+      slot_out[t] = a;
       out_path[b * L + t] = cand[t][a];
       out_scores[b * L + t] = sS[t][pa][a];
       a = pa;
@@ -176,15 +161,44 @@ __device__ __forceinline__ void viterbi_walk(const float (*sS)[kK][kK], int32_t 
   }
 }
 
-__device__ __forceinline__ void chase(const WalkTables& w, int64_t b, int L,
+__device__ __forceinline__ void chase(WalkTables& w, int64_t b, int L,
                                       int32_t* __restrict__ out_path,
                                       float* __restrict__ out_scores) {
   int a = 0;
   for (int t = 0; t < L; ++t) {
     const int j = w.next[t][a];
+    w.slot[t] = j;
     out_path[b * L + t] = w.cand[t][j];
     out_scores[b * L + t] = w.best[t][a];
     a = j;
+  }
+}
+
+// The draft distribution of position t given the walk's own predecessor: q =
+// softmax(S_t(slot[t-1], .) / T) over the 16 candidates (slot[-1] = 0, the verified
+// token's row), the distribution the Gumbel-max walk draws from; with the
+// candidate ids it is what speculative-sampling verification needs from the
+// drafter.  One wave per position; the 16 lanes of each DPP row hold the 16
+// candidates (all four rows the same), the row maximum and the sum are row
+// reductions, and every lane divides by lane 0's sum so the row is normalised
+// once.
+__device__ __forceinline__ void draft_q(const float (*sS)[kK][kK], const WalkTables& w, int t,
+                                        int lane, double temperature, int64_t row,
+                                        float* __restrict__ out_q, int32_t* __restrict__ out_cand) {
+  const int prev = t > 0 ? w.slot[t - 1] : 0;
+  const int j = lane & 15;
+  const float x = (float)((double)sS[t][prev][j] / temperature);
+  float m = x;
+#pragma unroll
+  for (int k = 1; k < kK; k <<= 1) m = fmaxf(m, __uint_as_float(xor_lanes(__float_as_uint(m), k, lane)));
+  const float e = expf(x - m);
+  float sum = e;
+#pragma unroll
+  for (int k = 1; k < kK; k <<= 1) sum += __uint_as_float(xor_lanes(__float_as_uint(sum), k, lane));
+  sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 0));
+  if (lane < kK) {
+    out_q[row * kK + j] = e / sum;
+    out_cand[row * kK + j] = w.cand[t][j];
   }
 }
 
@@ -227,7 +241,8 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
     const int32_t* __restrict__ prev_token, const float* __restrict__ gate, int gate_splits,
     int64_t gate_stride, const void* __restrict__ A_, const void* __restrict__ B_, int L,
     int64_t V, float* __restrict__ out_pair, int mode, double temperature, uint64_t seed,
-    int32_t* __restrict__ out_path, float* __restrict__ out_scores) {
+    int32_t* __restrict__ out_path, float* __restrict__ out_scores, float* __restrict__ out_q,
+    int32_t* __restrict__ out_cand) {
   __shared__ WalkTables sW;
   __shared__ __attribute__((aligned(16))) float sG[kMaxL][kE];  // gate row of each position
   __shared__ float sS[kWalk ? kMaxL : 1][kK][kK];                // whole tiles (best-path walk)
@@ -316,15 +331,21 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
     if constexpr (kWritePair) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
   }
   if constexpr (kWalk) {
-    if (mode == 2) {
+    if (mode == 2 || out_q != nullptr) {  // whole tiles kept for the best path or the draft rows
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[t][4 * q + i][r] = sc[i];
+    }
+    if (mode == 2) {
       __syncthreads();
-      if (t == 0) viterbi_walk(sS, sW.next, sW.cand, b, L, lane, out_path, out_scores);
+      if (t == 0) viterbi_walk(sS, sW.next, sW.cand, sW.slot, b, L, lane, out_path, out_scores);
     } else {
       successors(sc, t, lane, mode, temperature, seed, b, sW);
       __syncthreads();
       if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+    }
+    if (out_q != nullptr) {
+      __syncthreads();
+      draft_q(sS, sW, t, lane, temperature, row, out_q, out_cand);
     }
   }
 }
@@ -354,7 +375,7 @@ __global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) sS[t][4 * q + i][r] = sc[i];
     __syncthreads();
-    if (t == 0) viterbi_walk(sS, sW.next, sW.cand, b, L, lane, out_path, out_scores);
+    if (t == 0) viterbi_walk(sS, sW.next, sW.cand, sW.slot, b, L, lane, out_path, out_scores);
   } else {
     successors(sc, t, lane, mode, temperature, seed, b, sW);
     __syncthreads();
@@ -370,7 +391,8 @@ void launch_pw(int64_t batch, int64_t L, int64_t V, const int32_t* cand_idx, con
   pair_walk_kernel<kBf16, kWritePair, kWalk><<<dim3((unsigned)batch), dim3((unsigned)(kWave * L)),
                                                 0, stream>>>(
       cand_idx, cand_val, prev_token, g.gate, g.splits, g.stride, A, B, (int)L, V, out_pair,
-      w ? w->mode : 0, w ? w->temperature : 1.0, w ? w->seed : 0ull, out_path, out_scores);
+      w ? w->mode : 0, w ? w->temperature : 1.0, w ? w->seed : 0ull, out_path, out_scores,
+      w ? w->out_q : nullptr, w ? w->out_cand : nullptr);
 }
 
 }  // namespace

@@ -347,6 +347,9 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int esize) {
     if (parts > maxp) parts = maxp;
     if (parts > 64) parts = 64;
   }
+  // a chunk's byte range must fit the 32-bit range of its buffer resource
+  const int64_t min_parts = cdiv(V * esize, ((int64_t)1 << 31) - 256);
+  if (parts < min_parts) parts = min_parts;
   const int64_t chunk = (int64_t)align_up((size_t)cdiv(V, parts), (size_t)pv);
   p.parts = (int)cdiv(V, chunk);
   p.chunk = chunk;

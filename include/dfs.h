@@ -161,11 +161,49 @@ int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token
                double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                float* out_scores, hipStream_t stream);
 
+/* ---------------------------------------------------------------- draft distributions
+ * dfs_select plus the draft distribution the walk drew from at every position:
+ *   out_q [batch, L, 16] fp32: q[b, t, j] = softmax_j(S_t(slot[t-1], j) / temperature),
+ *     slot[-1] = 0 (the last verified token's row), over the 16 candidates of position
+ *     t; in gumbel mode this is exactly the distribution each step was drawn from.
+ *   out_cand [batch, L, 16] int32: the candidate ids (cand_idx of the top-16 step).
+ * temperature must be finite and > 0 in every mode here.  Together with out_path
+ * these are what speculative-sampling verification (dfs_verify) needs.            */
+int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev_token,
+                     const void* A, const void* B, const void* W_h, int k,
+                     const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
+                     uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+                     float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream);
+
+/* ---------------------------------------------------------------- verification
+ * Speculative-sampling verification of drafted blocks (Leviathan, Kalman and Matias,
+ * ICML 2023; Chen et al., 2023) against a target distribution p_t = softmax(z_t / T)
+ * over the vocabulary, z = target_logits [batch, L + 1, V] (dtype dt; row L is the
+ * target's next token after the whole block).  For block b and t = 0, 1, ...: the
+ * draft token x = path[b, t] with q_x = q[b, t, j] (cand[b, t, j] == x) is accepted
+ * when u < p_t(x) / q_x, u = ((w0 >> 9) + 0.5) 2^-23 from word w0 of Philox4x32-10
+ * counter (0, t, b, 1), key (seed low, seed high), ratio in fp64.  At the first
+ * rejection t = k (or k = L when all are accepted) one token is drawn by inverse CDF
+ * over the vocabulary, in id order, from weights max(0, p_k - q_k) (q_k zero off the
+ * candidates; k = L: p_L): the smallest v whose running weight reaches u2 times the
+ * total, u2 = ((w0 >> 9) 2^23 + (w1 >> 9) + 0.5) 2^-46 from counter (0, k, b, 2).
+ * Probabilities in fp32 against an fp32 log-sum-exp; running sums in fp64.
+ *   path [batch, L] int32, cand / q [batch, L, 16] (dfs_select_draft outputs);
+ *   out_accepted [batch] int32 = k; out_token [batch] int32 = the drawn token.
+ * temperature finite and > 0.  Alignment: target_logits to its element size, the
+ * int32 / fp32 arrays 4 bytes, ws 256 bytes.
+ * ws: dfs_verify_workspace_bytes(batch, L, V, dt) bytes of scratch (never 0).     */
+size_t dfs_verify_workspace_bytes(int64_t batch, int64_t L, int64_t V, dfs_dtype_t dt);
+int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t L, int64_t V,
+               const int32_t* path, const int32_t* cand, const float* q, int k, double temperature,
+               uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_accepted, int32_t* out_token,
+               hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* dfs_status_str(int status);
 
 /* ABI version of this header and library (major * 100 + minor). */
-#define DFS_ABI_VERSION 100
+#define DFS_ABI_VERSION 101
 int dfs_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.dfs_abi_version() == 100
+    assert L.dfs_abi_version() == 101
     for code in range(9):
         s = dfs.status_str(code)
         assert s.startswith("DFS_")
@@ -131,6 +131,40 @@ def test_select_validation(L):
     assert s(sh=ctypes.byref(sh)) == E_UNSUP
     sh = dfs._Shape(2, 4, 1000, 64, 1, 5, 1)
     assert s(sh=ctypes.byref(sh)) == E_UNSUP
+
+
+def test_select_draft_and_verify_validation(L):
+    shape = dfs._Shape(2, 4, 1000, 64, 1, 1, 1)
+
+    def sd(q=P, c=P, T=1.0, mode=0):
+        return L.dfs_select_draft(P, P, P, P, P, P, 16, ctypes.byref(shape), mode, T, 0, P, 1 << 26, P, P,
+                                  q, c, None)
+
+    assert sd(q=None) == E_NULL
+    assert sd(c=None) == E_NULL
+    assert sd(q=P + 2) == E_ALIGN
+    assert sd(T=0.0) == E_ARG  # the draft rows need a temperature in every mode
+    assert sd(T=float("inf")) == E_ARG
+
+    def v(tl=P, dt=1, b=2, Lv=4, V=1000, path=P, cand=P, q=P, k=16, T=1.0, ws=P, wsb=1 << 20, acc=P, tok=P):
+        return L.dfs_verify(tl, dt, b, Lv, V, path, cand, q, k, T, 0, ws, wsb, acc, tok, None)
+
+    assert v(tl=None) == E_NULL
+    assert v(ws=None) == E_NULL
+    assert v(tok=None) == E_NULL
+    assert v(k=8) == E_UNSUP
+    assert v(dt=3) == E_UNSUP
+    assert v(b=0) == E_SHAPE
+    assert v(Lv=0) == E_SHAPE
+    assert v(Lv=17) == E_SHAPE
+    assert v(V=15) == E_SHAPE
+    assert v(T=0.0) == E_ARG
+    assert v(T=float("nan")) == E_ARG
+    assert v(tl=P + 1) == E_ALIGN
+    assert v(ws=P + 64) == E_ALIGN
+    assert v(wsb=16) == E_WS
+    assert L.dfs_verify_workspace_bytes(2, 4, 1000, 1) >= 16
+    assert L.dfs_verify_workspace_bytes(2, 0, 1000, 1) == 0
 
 
 def test_valid_arguments_without_a_device_report_hip_error(L):
