@@ -200,6 +200,9 @@ def main() -> int:
     ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the top-16 traffic record from FETCH_SIZE / WRITE_SIZE counter runs and exit")
+    ap.add_argument("--verify", action="store_true",
+                    help="also time dfs_select_draft + dfs_verify against synthetic target logits "
+                         "[batch, L + 1, V] (the drafter's logits plus noise, one more random row)")
     ap.add_argument("--graph", action="store_true",
                     help="also time dfs_select replayed from a captured HIP graph (one launch per step)")
     args = ap.parse_args()
@@ -348,6 +351,34 @@ def main() -> int:
         if not torch.equal(sel.path.cpu(), torch.from_numpy(path)):
             raise RuntimeError("graph replay gave a different path than eager dfs_select")
 
+    verify_out = None
+    if args.verify:
+        # Speculative-sampling verification of the drafted blocks: the target's logits
+        # are synthetic (seeded, on the device): the drafter's logits plus N(0, 0.3)
+        # noise for the L block rows and N(0, 1.5) for the row after the block.
+        gen = torch.Generator(device=logits2d.device).manual_seed(0xDF5E)
+        lg = dev["logits"].float()
+        tgt = torch.empty((cfg.batch, cfg.L + 1, cfg.V), dtype=dev["logits"].dtype, device=logits2d.device)
+        tgt[:, :cfg.L] = (lg + 0.3 * torch.randn(lg.shape, generator=gen, device=lg.device)).to(tgt.dtype)
+        tgt[:, cfg.L] = (1.5 * torch.randn((cfg.batch, cfg.V), generator=gen, device=lg.device)).to(tgt.dtype)
+        del lg
+        T = cfg.temperature if cfg.walk == "gumbel" else 1.0
+        dargs = (dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])
+        dkw = dict(mode="gumbel", temperature=T, seed=cfg.walk_seed, draft=True)
+        vws = torch.empty(dfs.verify_workspace_bytes(cfg.batch, cfg.L, cfg.V, tgt.dtype), dtype=torch.uint8,
+                          device=tgt.device)
+        path_d, _, q_d, cand_d = dfs.select(*dargs, **dkw)
+        draft_ms = timed(lambda: dfs.select(*dargs, **dkw))
+        verify_ms = timed(lambda: dfs.verify(tgt, path_d, cand_d, q_d, 1.0, 7, workspace=vws))
+        acc, _ = dfs.verify(tgt, path_d, cand_d, q_d, 1.0, 7, workspace=vws)
+        tbytes = tgt.numel() * tgt.element_size()
+        verify_out = {"draft_ms": draft_ms, "verify_ms": verify_ms, "target_bytes": tbytes,
+                      "verify_GBps": tbytes / (verify_ms * 1e-3) / 1e9,
+                      "verify_frac_of_peak": tbytes / (verify_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "accepted_mean": float(acc.float().mean().item()), "target_temperature": 1.0,
+                      "draft_temperature": T}
+        del tgt
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device=logits2d.device).fill_(1)
@@ -381,6 +412,8 @@ def main() -> int:
         "input_sets": nsets,
         "host_wall_s": wall,
     }
+    if verify_out is not None:
+        out["verify"] = verify_out
     if graph_ms is not None:
         out["graph_replay"] = {"ms_per_step": graph_ms, "value": cfg.batch / (graph_ms * 1e-3),
                                "input_sets": 1}

@@ -283,8 +283,8 @@ int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev
 }
 
 size_t dfs_verify_workspace_bytes(int64_t batch, int64_t L, int64_t V, dfs_dtype_t dt) {
-  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K || V > kMaxV ||
-      !valid_dtype(dt))
+  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K ||
+      V > verify_max_vocab() || !valid_dtype(dt))
     return 0;
   return plan_verify(batch, L, V, esize(dt)).ws_bytes;
 }
@@ -296,7 +296,8 @@ int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t
   if (!target_logits || !path || !cand || !q || !out_accepted || !out_token || !ws)
     return DFS_E_NULL;
   if (!valid_dtype(dt) || k != DFS_K) return DFS_E_UNSUPPORTED;
-  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K || V > kMaxV)
+  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K ||
+      V > verify_max_vocab())
     return DFS_E_SHAPE;
   if (!(std::isfinite(temperature) && temperature > 0.0)) return DFS_E_ARG;
   if (!aligned(target_logits, esize(dt)) || !aligned(path, 4) || !aligned(cand, 4) ||

@@ -92,11 +92,12 @@ hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch
 struct VerifyPlan {
   int64_t batch, L, V;
   int esize;       // bytes per target logit
-  int parts;       // chunks per target row in the log-sum-exp pass
-  int64_t chunk;   // elements per chunk
-  size_t ws_bytes; // (max, sum) pairs [batch * (L + 1), parts]
+  int parts;       // workgroups per target row in the log-sum-exp pass
+  int64_t nseg;    // segment slots per row
+  size_t ws_bytes; // (max, sum) per segment [batch * (L + 1), nseg], fp64 pairs
 };
 VerifyPlan plan_verify(int64_t batch, int64_t L, int64_t V, int esize);
+int64_t verify_max_vocab();  // the draw keeps a row's segment masses in LDS
 hipError_t launch_verify(const VerifyPlan& p, const void* logits, bool bf16, const int32_t* path,
                          const int32_t* cand, const float* q, double temperature, uint64_t seed,
                          void* ws, int32_t* out_accepted, int32_t* out_token, hipStream_t stream);

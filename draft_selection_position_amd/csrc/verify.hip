@@ -11,17 +11,16 @@
 // p_t = softmax(z_t / T) over the vocabulary, z the target logits of row t.
 //
 // Design (gfx950): two kernels.  lse_kernel streams the target logits once (the
-// only vocabulary-wide pass): each workgroup keeps a running (max, sum of 2^(x -
-// max)) of x = z log2(e) / T per thread, merged across the wave with DPP and across
-// waves through LDS, for a row or a chunk of one.  verify_kernel takes one block per
-// workgroup: it merges the chunks into log2-sum-exp per row, runs the accept tests
-// (fp64 ratio against a 23-bit Philox uniform), and draws the output token by
-// inverse CDF with a 46-bit Philox uniform: every thread sums its contiguous share
-// of the row's weights (as 64 sub-ranges), thread 0 finds the share and the
-// sub-range the target mass falls in, and the exact token is found inside that
-// sub-range.  The 16 candidates' corrections min(p, q) are subtracted where they
-// fall, so the residual never needs a per-element candidate test outside the last
-// sub-range.
+// only vocabulary-wide pass) and leaves, for every run of 4096 tokens of every row
+// (a segment), the running (max, sum of 2^(x - max)) of x = z log2(e) / T, each
+// segment streamed by one wave with 16-byte non-temporal loads and reduced with
+// DPP.  verify_kernel takes one block per workgroup: it merges a row's segments
+// into its log2-sum-exp, runs the accept tests (fp64 ratio against a 23-bit Philox
+// uniform), and draws the output token by inverse CDF with a 46-bit Philox
+// uniform: the segments' masses (their pairs against the row's log-sum-exp, less
+// the 16 candidates' min(p, q) where the residual applies) locate the segment,
+// and only that segment is read again to find the token, each thread summing a
+// contiguous share of it in token order.
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "philox.h"
@@ -32,20 +31,22 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;           // 16-byte vectors per thread per iteration
-constexpr int kMinChunk = 4096;      // elements; below this a split does not pay
-constexpr int kSub = 64;             // sub-ranges per thread share (inverse CDF)
+constexpr int kSeg = 4096;           // tokens per segment of a target row
+constexpr int kMaxSeg = 1024;        // segments per row the draw holds in LDS (V <= 2^22)
 constexpr int kMaxL = 16;            // longest block
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Running maximum and sum of 2^(x - max).  An empty pair is (-inf, 0).
+// Running maximum and sum of 2^(x - max) (the sum in fp64, so that the mass of a
+// segment is good to ~1e-7 of the row's).  An empty pair is (-inf, 0).
 struct MS {
-  float m, s;
+  float m;
+  double s;
 };
 
 __device__ __forceinline__ MS ms_merge(MS a, MS b) {
   const float m = fmaxf(a.m, b.m);
-  if (m == -INFINITY) return MS{m, 0.0f};
-  return MS{m, a.s * exp2f(a.m - m) + b.s * exp2f(b.m - m)};
+  if (m == -INFINITY) return MS{m, 0.0};
+  return MS{m, a.s * (double)exp2f(a.m - m) + b.s * (double)exp2f(b.m - m)};
 }
 
 template <bool kBf16>
@@ -79,113 +80,140 @@ __device__ __forceinline__ void ms_add_vec(MS& a, uint4 d, float scale) {
   }
   const float m = fmaxf(a.m, vm);
   if (m == -INFINITY) return;
-  float s = a.s * exp2f(a.m - m);
+  float vs = 0.0f;  // the vector's own few terms in fp32, then into the fp64 sum
 #pragma unroll
-  for (int e = 0; e < PV; ++e) s += exp2f(x[e] - m);
-  a = MS{m, s};
+  for (int e = 0; e < PV; ++e) vs += exp2f(x[e] - m);
+  a = MS{m, (m == a.m ? a.s : a.s * (double)exp2f(a.m - m)) + (double)vs};
 }
 
 __device__ __forceinline__ void ms_add(MS& a, float z, float scale) {
   const float x = z * scale;
   const float m = fmaxf(a.m, x);
   if (m == -INFINITY) return;
-  a = MS{m, a.s * exp2f(a.m - m) + exp2f(x - m)};
+  a = MS{m, (m == a.m ? a.s : a.s * (double)exp2f(a.m - m)) + (double)exp2f(x - m)};
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer
 constexpr int kCacheNonTemporal = 2;
 
-// (max, sum) of x = z * scale over chunk `part` of row `row`, one pair per workgroup.
+// Segments of a target row, in token order: the row's 16-byte aligned middle
+// [vb, ve) is cut into runs of kSeg tokens from vb; segment 0 also takes the
+// unaligned head [0, vb) and the last segment the tail [ve, V).  Both kernels
+// derive the same cut from the row's address.
+struct RowCut {
+  int64_t vb, ve, nvec, nseg;
+};
+
+template <bool kBf16>
+__device__ __forceinline__ RowCut row_cut(const void* rowp, int64_t V) {
+  constexpr int esz = kBf16 ? 2 : 4;
+  constexpr int PV = 16 / esz;
+  RowCut c;
+  const uintptr_t a = (uintptr_t)rowp;
+  c.vb = (int64_t)(((16u - (a & 15u)) & 15u) / esz);
+  if (c.vb > V) c.vb = V;
+  c.nvec = (V - c.vb) / PV;
+  c.ve = c.vb + c.nvec * PV;
+  c.nseg = (c.nvec * PV + kSeg - 1) / kSeg;
+  if (c.nseg < 1) c.nseg = 1;
+  return c;
+}
+
+__device__ __forceinline__ void seg_range(const RowCut& c, int64_t V, int64_t s, int64_t& lo,
+                                          int64_t& hi) {
+  lo = s == 0 ? 0 : c.vb + s * kSeg;
+  hi = s == c.nseg - 1 ? V : c.vb + (s + 1) * kSeg;
+}
+
+// (max, sum) of x = z * scale for every segment of the rows: workgroup (row, part)
+// takes segments part, part + parts, ... of its row, one wave per segment at a
+// time, 16-byte non-temporal loads of the aligned middle.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void lse_kernel(const void* __restrict__ logits, int64_t V,
-                                                       int parts, int64_t chunk, float scale,
-                                                       float2* __restrict__ partial) {
+                                                       int parts, int64_t nseg_max, float scale,
+                                                       double2* __restrict__ seg_out) {
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
   constexpr int PV = kBf16 ? 8 : 4;
-  __shared__ MS s_w[kWaves];
+  constexpr int kSegVec = kSeg / PV;  // vectors per segment
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int64_t row = blockIdx.x / parts;
   const int part = (int)(blockIdx.x % parts);
   const T* rowp = static_cast<const T*>(logits) + row * V;
-  const int64_t beg = (int64_t)part * chunk;
-  const int64_t end = beg + chunk < V ? beg + chunk : V;
-
-  // [vb, ve): the 16-byte aligned middle of the chunk; the rest goes element by element
-  const uintptr_t a_beg = (uintptr_t)(rowp + beg);
-  int64_t vb = beg + (int64_t)(((16u - (a_beg & 15u)) & 15u) / sizeof(T));
-  if (vb > end) vb = end;
-  const int64_t nvec = (end - vb) / PV;
-  const int64_t ve = vb + nvec * PV;
-
-  MS acc{-INFINITY, 0.0f};
-  for (int64_t i = beg + tid; i < vb; i += kThreads) ms_add(acc, logit_at<kBf16>(rowp, i), scale);
-  for (int64_t i = ve + tid; i < end; i += kThreads) ms_add(acc, logit_at<kBf16>(rowp, i), scale);
-  if (nvec > 0) {
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(rowp + vb), (short)0, (int)(nvec * 16), kRawBufferWord3);
-    const int64_t step = (int64_t)kThreads * kUnroll;
-    for (int64_t base = 0; base < nvec; base += step) {
+  const RowCut c = row_cut<kBf16>(rowp, V);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(rowp + c.vb), (short)0, (int)(c.nvec * 16), kRawBufferWord3);
+  for (int64_t sg = (int64_t)part * kWaves + wave; sg < c.nseg; sg += (int64_t)parts * kWaves) {
+    MS acc{-INFINITY, 0.0};
+    if (sg == 0)
+      for (int64_t i = lane; i < c.vb; i += kWave) ms_add(acc, logit_at<kBf16>(rowp, i), scale);
+    if (sg == c.nseg - 1)
+      for (int64_t i = c.ve + lane; i < V; i += kWave) ms_add(acc, logit_at<kBf16>(rowp, i), scale);
+    const int64_t v0 = sg * kSegVec;
+    const int64_t v1 = v0 + kSegVec < c.nvec ? v0 + kSegVec : c.nvec;
+    for (int64_t base = v0; base < v1; base += (int64_t)kWave * kUnroll) {
       uint4 v[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t vid = (uint32_t)(base + u * kThreads + tid);
+        const uint32_t vid = (uint32_t)(base + u * kWave + lane);
         const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vid * 16u, 0, kCacheNonTemporal);
-        v[u] = make_uint4(w.x, w.y, w.z, w.w);  // past the end: zeros, skipped below
+        v[u] = make_uint4(w.x, w.y, w.z, w.w);  // past the row: zeros, skipped below
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (base + u * kThreads + tid < nvec) ms_add_vec<kBf16>(acc, v[u], scale);
+        if (base + u * kWave + lane < v1) ms_add_vec<kBf16>(acc, v[u], scale);
     }
-  }
-  // across the wave (lane 0's result), then across the waves in order
 #pragma unroll
-  for (int k = 1; k < kWave; k <<= 1) {
-    const MS o{__uint_as_float(xor_lanes(__float_as_uint(acc.m), k, lane)),
-               __uint_as_float(xor_lanes(__float_as_uint(acc.s), k, lane))};
-    acc = ms_merge(acc, o);
-  }
-  if (lane == 0) s_w[wave] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    MS r = s_w[0];
-    for (int w = 1; w < kWaves; ++w) r = ms_merge(r, s_w[w]);
-    partial[blockIdx.x] = make_float2(r.m, r.s);
+    for (int k = 1; k < kWave; k <<= 1) {
+      const uint64_t sb = (uint64_t)__double_as_longlong(acc.s);
+      const uint32_t lo = xor_lanes((uint32_t)sb, k, lane), hi = xor_lanes((uint32_t)(sb >> 32), k, lane);
+      const MS o{__uint_as_float(xor_lanes(__float_as_uint(acc.m), k, lane)),
+                 __longlong_as_double((long long)(((uint64_t)hi << 32) | lo))};
+      acc = ms_merge(acc, o);
+    }
+    if (lane == 0) seg_out[row * nseg_max + sg] = make_double2((double)acc.m, acc.s);
   }
 }
 
-// Target probability of token v in row `rowp`: 2^(x - log2-sum-exp), fp32 exp2 of
-// the fp32-scaled logit (the residual of a candidate subtracts min(p, q) from it).
+// Target probability of token v in row `rowp`: 2^(x - log2-sum-exp) in fp64, x the
+// fp32-scaled logit as the log-sum-exp pass saw it (the residual of a candidate
+// subtracts min(p, q) from it).
 template <bool kBf16>
 __device__ __forceinline__ double token_weight(const void* rowp, int64_t v, float scale, double lse2) {
-  return (double)exp2f((float)(logit_at<kBf16>(rowp, v) * scale - (float)lse2));
+  return exp2((double)(logit_at<kBf16>(rowp, v) * scale) - lse2);
 }
 
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void verify_kernel(
-    const void* __restrict__ logits, int64_t V, int L, int parts, float scale,
-    const float2* __restrict__ partial, const int32_t* __restrict__ path,
+    const void* __restrict__ logits, int64_t V, int L, int64_t nseg_max, float scale,
+    const double2* __restrict__ segs, const int32_t* __restrict__ path,
     const int32_t* __restrict__ cand, const float* __restrict__ q, uint64_t seed,
     int32_t* __restrict__ out_accepted, int32_t* __restrict__ out_token) {
   __shared__ double s_lse2[kMaxL + 1];
   __shared__ int32_t s_cand[kK];
   __shared__ double s_corr[kK];
+  __shared__ double s_mass[kMaxSeg];
   __shared__ double s_share[kThreads];
-  __shared__ double s_sub[kSub];
-  __shared__ int s_k, s_share_idx, s_sub_idx;
+  __shared__ int s_k, s_seg;
   __shared__ double s_rest;
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
 
-  // log2-sum-exp of rows (b, 0..L), chunks merged in order
+  // log2-sum-exp of rows (b, 0..L): the row's segments merged in order
   if (tid <= L) {
-    const float2* p = partial + ((b * (L + 1)) + tid) * parts;
-    MS r{-INFINITY, 0.0f};
-    for (int i = 0; i < parts; ++i) r = ms_merge(r, MS{p[i].x, p[i].y});
-    s_lse2[tid] = r.s > 0.0f ? (double)r.m + log2((double)r.s) : -INFINITY;
+    const int64_t row = b * (L + 1) + tid;
+    const void* rowp = kBf16 ? (const void*)(static_cast<const uint16_t*>(logits) + row * V)
+                             : (const void*)(static_cast<const float*>(logits) + row * V);
+    const RowCut c = row_cut<kBf16>(rowp, V);
+    MS r{-INFINITY, 0.0};
+    for (int64_t i = 0; i < c.nseg; ++i) {
+      const double2 p = segs[row * nseg_max + i];
+      r = ms_merge(r, MS{(float)p.x, p.y});
+    }
+    s_lse2[tid] = r.s > 0.0 ? (double)r.m + log2(r.s) : -INFINITY;
   }
   __syncthreads();
 
@@ -216,124 +244,115 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
   const void* rowp = kBf16 ? (const void*)(static_cast<const uint16_t*>(logits) + row * V)
                            : (const void*)(static_cast<const float*>(logits) + row * V);
   const double lse2 = s_lse2[k];
+  const RowCut c = row_cut<kBf16>(rowp, V);
   if (tid < kK) {
-    int32_t c = -1;
+    int32_t cd = -1;
     double corr = 0.0;
     if (k < L) {
-      c = cand[(b * L + k) * kK + tid];
-      const int32_t cc = c < 0 ? 0 : (c >= V ? (int32_t)(V - 1) : c);
+      cd = cand[(b * L + k) * kK + tid];
+      const int32_t cc = cd < 0 ? 0 : (cd >= V ? (int32_t)(V - 1) : cd);
       const double p = token_weight<kBf16>(rowp, cc, scale, lse2);
       const double qc = (double)q[(b * L + k) * kK + tid];
-      corr = p < qc ? p : qc;  // min(p, q): what the residual takes off token c
+      corr = p < qc ? p : qc;  // min(p, q): what the residual takes off token cd
     }
-    s_cand[tid] = c;
+    s_cand[tid] = cd;
     s_corr[tid] = corr;
   }
-  __syncthreads();
-
-  // Thread i's share [i R, (i + 1) R) as kSub sub-ranges of R2 tokens, summed in
-  // order; the same sums are rebuilt below for the share the draw falls in.
-  const int64_t R = (V + kThreads - 1) / kThreads;
-  const int64_t R2 = (R + kSub - 1) / kSub;
-  auto sub_sum = [&](int64_t lo, int64_t hi) {
-    double s = 0.0;
-    for (int64_t v = lo; v < hi; ++v) s += token_weight<kBf16>(rowp, v, scale, lse2);
-    for (int j = 0; j < kK; ++j) {
-      const int64_t c = s_cand[j];
-      if (c >= lo && c < hi) s -= s_corr[j];
-    }
-    return s;
-  };
-  {
-    const int64_t lo = tid * R;
-    double share = 0.0;
-    for (int u = 0; u < kSub; ++u) {
-      int64_t a = lo + u * R2, e = a + R2;
-      const int64_t hi_share = lo + R < V ? lo + R : V;
-      if (a > hi_share) a = hi_share;
-      if (e > hi_share) e = hi_share;
-      share += sub_sum(a, e);
-    }
-    s_share[tid] = share;
+  // the mass of every segment, from its (max, sum) pair
+  for (int64_t sg = tid; sg < c.nseg; sg += kThreads) {
+    const double2 p = segs[row * nseg_max + sg];
+    s_mass[sg] = p.y * exp2(p.x - lse2);
   }
   __syncthreads();
   if (tid == 0) {
+    for (int j = 0; j < kK; ++j) {  // the residual's corrections, where they fall
+      const int64_t cd = s_cand[j];
+      if (cd < 0 || cd >= V) continue;
+      const int64_t sg = cd < c.vb + kSeg ? 0 : (cd - c.vb) / kSeg < c.nseg ? (cd - c.vb) / kSeg
+                                                                                : c.nseg - 1;
+      s_mass[sg] -= s_corr[j];
+    }
     double total = 0.0;
-    for (int i = 0; i < kThreads; ++i) total += s_share[i];
+    for (int64_t sg = 0; sg < c.nseg; ++sg) total += s_mass[sg] > 0.0 ? s_mass[sg] : 0.0;
     uint32_t w[4];
     philox4x32_10(0u, (uint32_t)k, (uint32_t)b, 2u, k0, k1, w);
     const double u = ((double)(w[0] >> 9) * 0x1p23 + (double)(w[1] >> 9) + 0.5) * 0x1p-46;
-    double target = u * total, cum = 0.0;
-    int idx = -1;
-    for (int i = 0; i < kThreads; ++i) {
-      if (s_share[i] > 0.0 && cum + s_share[i] >= target) {
-        idx = i;
+    const double target = u * total;
+    double cum = 0.0;
+    int64_t pick = -1, last = 0;
+    for (int64_t sg = 0; sg < c.nseg; ++sg) {
+      const double m = s_mass[sg] > 0.0 ? s_mass[sg] : 0.0;
+      if (m <= 0.0) continue;
+      last = sg;
+      if (cum + m >= target) {
+        pick = sg;
         break;
       }
-      cum += s_share[i];
+      cum += m;
     }
-    if (idx < 0) {  // rounding past the end: the last share with weight
-      for (int i = kThreads - 1; i >= 0; --i)
-        if (s_share[i] > 0.0) {
-          idx = i;
-          break;
-        }
-      target = cum;
-      cum -= idx >= 0 ? s_share[idx] : 0.0;
+    if (pick < 0) {  // rounding past the end: the last segment with mass, from its end
+      pick = last;
+      cum = 1e300;
     }
-    s_share_idx = idx < 0 ? 0 : idx;
+    s_seg = (int)pick;
     s_rest = target - cum;
   }
   __syncthreads();
-  const int64_t lo = s_share_idx * R;
-  const int64_t hi_share = lo + R < V ? lo + R : V;
-  if (tid < kSub) {
-    int64_t a = lo + tid * R2, e = a + R2;
-    if (a > hi_share) a = hi_share;
-    if (e > hi_share) e = hi_share;
-    s_sub[tid] = sub_sum(a, e);
+  // the segment, exactly: thread i sums its contiguous share of it in order
+  int64_t lo, hi;
+  seg_range(c, V, s_seg, lo, hi);
+  const int64_t per = (hi - lo + kThreads - 1) / kThreads;
+  auto weight = [&](int64_t v) {
+    double wv = token_weight<kBf16>(rowp, v, scale, lse2);
+#pragma unroll
+    for (int j = 0; j < kK; ++j)
+      if (s_cand[j] == v) wv -= s_corr[j];
+    return wv > 0.0 ? wv : 0.0;
+  };
+  {
+    const int64_t a = lo + tid * per < hi ? lo + tid * per : hi;
+    const int64_t e = a + per < hi ? a + per : hi;
+    double sum = 0.0;
+    for (int64_t v = a; v < e; ++v) sum += weight(v);
+    s_share[tid] = sum;
   }
   __syncthreads();
   if (tid == 0) {
-    double rest = s_rest, cum = 0.0;
-    int idx = -1;
-    for (int u = 0; u < kSub; ++u) {
-      if (s_sub[u] > 0.0 && cum + s_sub[u] >= rest) {
-        idx = u;
-        break;
+    const double rest = s_rest;
+    double cum = 0.0;
+    int64_t pick = -1;
+    int last_share = -1;
+    for (int i = 0; i < kThreads && pick < 0; ++i) {
+      if (s_share[i] <= 0.0) continue;
+      last_share = i;
+      if (cum + s_share[i] < rest) {
+        cum += s_share[i];
+        continue;
       }
-      cum += s_sub[u];
-    }
-    if (idx < 0) {
-      for (int u = kSub - 1; u >= 0; --u)
-        if (s_sub[u] > 0.0) {
-          idx = u;
-          break;
-        }
-      if (idx < 0) idx = 0;
-      rest = 1e300;  // take the last token with weight in it
-      cum = 0.0;
-    }
-    int64_t a = lo + idx * R2, e = a + R2;
-    if (a > hi_share) a = hi_share;
-    if (e > hi_share) e = hi_share;
-    rest -= cum;
-    int64_t pick = -1, last = -1;
-    double run = 0.0;
-    for (int64_t v = a; v < e; ++v) {
-      double wv = token_weight<kBf16>(rowp, v, scale, lse2);
-      for (int j = 0; j < kK; ++j)
-        if (s_cand[j] == v) wv -= s_corr[j];
-      if (wv > 0.0) {
-        last = v;
-        run += wv;
-        if (run >= rest) {
+      const int64_t a = lo + i * per < hi ? lo + i * per : hi;
+      const int64_t e = a + per < hi ? a + per : hi;
+      for (int64_t v = a; v < e; ++v) {
+        const double wv = weight(v);
+        if (wv <= 0.0) continue;
+        cum += wv;
+        if (cum >= rest) {
           pick = v;
           break;
         }
       }
     }
-    if (pick < 0) pick = last >= 0 ? last : a;
+    if (pick < 0) {  // rounding past the end: the last token with weight
+      pick = lo;
+      if (last_share >= 0) {
+        const int64_t a = lo + last_share * per < hi ? lo + last_share * per : hi;
+        const int64_t e = a + per < hi ? a + per : hi;
+        for (int64_t v = e - 1; v >= a; --v)
+          if (weight(v) > 0.0) {
+            pick = v;
+            break;
+          }
+      }
+    }
     out_accepted[b] = k;
     out_token[b] = (int32_t)pick;
   }
@@ -348,40 +367,37 @@ VerifyPlan plan_verify(int64_t batch, int64_t L, int64_t V, int esize) {
   p.V = V;
   p.esize = esize;
   const int64_t rows = batch * (L + 1);
-  const int64_t pv = 16 / esize;
+  // segments per row (at most one more than the aligned middle needs)
+  p.nseg = cdiv(V, kSeg) + 1;
+  // workgroups per row: enough rows x parts to fill the chip, four segments apiece at least
   int64_t parts = 1;
   if (rows < kTargetBlocks) {
     parts = cdiv(kTargetBlocks, rows);
-    int64_t maxp = V / kMinChunk;
-    if (maxp < 1) maxp = 1;
+    const int64_t maxp = cdiv(p.nseg, kWaves);
     if (parts > maxp) parts = maxp;
-    if (parts > 64) parts = 64;
   }
-  // a chunk's byte range must fit the 32-bit range of its buffer resource
-  const int64_t min_parts = cdiv(V * esize, ((int64_t)1 << 31) - 256);
-  if (parts < min_parts) parts = min_parts;
-  const int64_t chunk = (int64_t)align_up((size_t)cdiv(V, parts), (size_t)pv);
-  p.parts = (int)cdiv(V, chunk);
-  p.chunk = chunk;
-  p.ws_bytes = align_up((size_t)rows * p.parts * sizeof(float2), 256);
+  p.parts = (int)parts;
+  p.ws_bytes = align_up((size_t)rows * p.nseg * sizeof(double2), 256);
   return p;
 }
+
+int64_t verify_max_vocab() { return (int64_t)(kMaxSeg - 1) * kSeg; }
 
 hipError_t launch_verify(const VerifyPlan& p, const void* logits, bool bf16, const int32_t* path,
                          const int32_t* cand, const float* q, double temperature, uint64_t seed,
                          void* ws, int32_t* out_accepted, int32_t* out_token, hipStream_t stream) {
-  float2* partial = static_cast<float2*>(ws);
+  double2* segs = static_cast<double2*>(ws);
   const float scale = (float)((double)kLog2e / temperature);
   const int64_t rows = p.batch * (p.L + 1);
   const dim3 grid((unsigned)(rows * p.parts));
   if (bf16) {
-    lse_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, scale, partial);
+    lse_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.nseg, scale, segs);
     verify_kernel<true><<<dim3((unsigned)p.batch), kThreads, 0, stream>>>(
-        logits, p.V, (int)p.L, p.parts, scale, partial, path, cand, q, seed, out_accepted, out_token);
+        logits, p.V, (int)p.L, p.nseg, scale, segs, path, cand, q, seed, out_accepted, out_token);
   } else {
-    lse_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, scale, partial);
+    lse_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.nseg, scale, segs);
     verify_kernel<false><<<dim3((unsigned)p.batch), kThreads, 0, stream>>>(
-        logits, p.V, (int)p.L, p.parts, scale, partial, path, cand, q, seed, out_accepted, out_token);
+        logits, p.V, (int)p.L, p.nseg, scale, segs, path, cand, q, seed, out_accepted, out_token);
   }
   return hipGetLastError();
 }

@@ -158,6 +158,7 @@ def test_select_draft_and_verify_validation(L):
     assert v(Lv=0) == E_SHAPE
     assert v(Lv=17) == E_SHAPE
     assert v(V=15) == E_SHAPE
+    assert v(V=4190209) == E_SHAPE  # the draw keeps at most 1023 segments of 4096 tokens
     assert v(T=0.0) == E_ARG
     assert v(T=float("nan")) == E_ARG
     assert v(tl=P + 1) == E_ALIGN
