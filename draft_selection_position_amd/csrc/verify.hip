@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 4;           // 16-byte vectors per thread per iteration
+constexpr int kUnroll = 2;           // 16-byte vectors per lane per step (two steps in flight)
 constexpr int kSeg = 4096;           // tokens per segment of a target row
 constexpr int kMaxSeg = 1024;        // segments per row the draw holds in LDS (V <= 2^22)
 constexpr int kMaxL = 16;            // longest block
@@ -43,10 +43,16 @@ struct MS {
   double s;
 };
 
+// 2^x by the hardware's v_exp_f32 (about 1 ulp; results below 2^-126, which no
+// sum here can feel next to its own maximum's term 1, may come back flushed).
+// The library exp2f wraps the same instruction in a denormal rescue that costs
+// five more instructions per element, which would make the pass ALU-bound.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ MS ms_merge(MS a, MS b) {
   const float m = fmaxf(a.m, b.m);
   if (m == -INFINITY) return MS{m, 0.0};
-  return MS{m, a.s * (double)exp2f(a.m - m) + b.s * (double)exp2f(b.m - m)};
+  return MS{m, a.s * (double)fast_exp2(a.m - m) + b.s * (double)fast_exp2(b.m - m)};
 }
 
 template <bool kBf16>
@@ -58,11 +64,9 @@ __device__ __forceinline__ float logit_at(const void* p, int64_t i) {
   }
 }
 
-// Add the values of one 16-byte vector (8 bf16 or 4 fp32) to a running pair.
+// The values of a 16-byte vector (8 bf16 or 4 fp32), widened to fp32.
 template <bool kBf16>
-__device__ __forceinline__ void ms_add_vec(MS& a, uint4 d, float scale) {
-  constexpr int PV = kBf16 ? 8 : 4;
-  float x[PV];
+__device__ __forceinline__ void unpack_vec(uint4 d, float* x) {
   if constexpr (kBf16) {
     x[0] = bf16_lo(d.x); x[1] = bf16_hi(d.x);
     x[2] = bf16_lo(d.y); x[3] = bf16_hi(d.y);
@@ -72,25 +76,43 @@ __device__ __forceinline__ void ms_add_vec(MS& a, uint4 d, float scale) {
     x[0] = __uint_as_float(d.x); x[1] = __uint_as_float(d.y);
     x[2] = __uint_as_float(d.z); x[3] = __uint_as_float(d.w);
   }
-  float vm = -INFINITY;
+}
+
+// Add N vectors of raw logits z to a running pair of x = z * scale (scale > 0, so
+// the largest z gives the largest x): one maximum and at most one rescale for the
+// lot, then one fma and one v_exp_f32 per value, summed in fp32 and added to the
+// fp64 sum once.
+template <bool kBf16, int N>
+__device__ __forceinline__ void ms_add_vecs(MS& a, const uint4* d, float scale) {
+  constexpr int PV = kBf16 ? 8 : 4;
+  float x[N][PV];
+  float zm = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < PV; ++e) {
-    x[e] *= scale;
-    vm = fmaxf(vm, x[e]);
+  for (int u = 0; u < N; ++u) {
+    unpack_vec<kBf16>(d[u], x[u]);
+#pragma unroll
+    for (int e = 0; e < PV; ++e) zm = fmaxf(zm, x[u][e]);
   }
-  const float m = fmaxf(a.m, vm);
-  if (m == -INFINITY) return;
-  float vs = 0.0f;  // the vector's own few terms in fp32, then into the fp64 sum
+  const float vm = zm * scale;
+  if (vm > a.m) {  // a new maximum (rare once a row is under way): rescale the sum
+    a.s = a.m == -INFINITY ? 0.0 : a.s * (double)fast_exp2(a.m - vm);
+    a.m = vm;
+  }
+  if (a.m == -INFINITY) return;
+  const float nm = -a.m;
+  float vs = 0.0f;
 #pragma unroll
-  for (int e = 0; e < PV; ++e) vs += exp2f(x[e] - m);
-  a = MS{m, (m == a.m ? a.s : a.s * (double)exp2f(a.m - m)) + (double)vs};
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int e = 0; e < PV; ++e) vs += fast_exp2(fmaf(x[u][e], scale, nm));
+  a.s += (double)vs;
 }
 
 __device__ __forceinline__ void ms_add(MS& a, float z, float scale) {
   const float x = z * scale;
   const float m = fmaxf(a.m, x);
   if (m == -INFINITY) return;
-  a = MS{m, (m == a.m ? a.s : a.s * (double)exp2f(a.m - m)) + (double)exp2f(x - m)};
+  a = MS{m, (m == a.m ? a.s : a.s * (double)fast_exp2(a.m - m)) + (double)fast_exp2(x - m)};
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -126,16 +148,33 @@ __device__ __forceinline__ void seg_range(const RowCut& c, int64_t V, int64_t s,
   hi = s == c.nseg - 1 ? V : c.vb + (s + 1) * kSeg;
 }
 
-// (max, sum) of x = z * scale for every segment of the rows: workgroup (row, part)
-// takes segments part, part + parts, ... of its row, one wave per segment at a
-// time, 16-byte non-temporal loads of the aligned middle.
+// Reduce a wave's running pair (lane 0 ends with the merge, in a fixed order).
+__device__ __forceinline__ MS wave_merge(MS acc, int lane) {
+#pragma unroll
+  for (int k = 1; k < kWave; k <<= 1) {
+    const uint64_t sb = (uint64_t)__double_as_longlong(acc.s);
+    const uint32_t lo = xor_lanes((uint32_t)sb, k, lane), hi = xor_lanes((uint32_t)(sb >> 32), k, lane);
+    const MS o{__uint_as_float(xor_lanes(__float_as_uint(acc.m), k, lane)),
+               __longlong_as_double((long long)(((uint64_t)hi << 32) | lo))};
+    acc = ms_merge(acc, o);
+  }
+  return acc;
+}
+
+// (max, sum) of x = z * scale for every segment of the rows.  Workgroup (row, part)
+// takes a contiguous run of the row's segments and each of its waves a contiguous
+// part of that; a wave streams its segments' vectors without a break (the next
+// step's 16-byte non-temporal loads in flight while the current ones are added),
+// and closes a segment every kSegVec vectors with one DPP reduction.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void lse_kernel(const void* __restrict__ logits, int64_t V,
                                                        int parts, int64_t nseg_max, float scale,
                                                        double2* __restrict__ seg_out) {
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
   constexpr int PV = kBf16 ? 8 : 4;
-  constexpr int kSegVec = kSeg / PV;  // vectors per segment
+  constexpr int kSegVec = kSeg / PV;            // vectors per segment
+  constexpr int kStep = kWave * kUnroll;        // vectors per wave step
+  static_assert(kSegVec % kStep == 0, "a step never straddles two segments");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -143,38 +182,70 @@ __global__ __launch_bounds__(kThreads) void lse_kernel(const void* __restrict__ 
   const int part = (int)(blockIdx.x % parts);
   const T* rowp = static_cast<const T*>(logits) + row * V;
   const RowCut c = row_cut<kBf16>(rowp, V);
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(rowp + c.vb), (short)0, (int)(c.nvec * 16), kRawBufferWord3);
-  for (int64_t sg = (int64_t)part * kWaves + wave; sg < c.nseg; sg += (int64_t)parts * kWaves) {
-    MS acc{-INFINITY, 0.0};
+  const int64_t per_wg = (c.nseg + parts - 1) / parts;
+  const int64_t sa = (int64_t)part * per_wg;
+  const int64_t sb = sa + per_wg < c.nseg ? sa + per_wg : c.nseg;
+  const int64_t per_wave = sb > sa ? (sb - sa + kWaves - 1) / kWaves : 0;
+  const int64_t wa = sa + wave * per_wave;
+  const int64_t wb = wa + per_wave < sb ? wa + per_wave : sb;
+  if (wa >= wb) return;
+
+  auto scalars = [&](MS& acc, int64_t sg) {
     if (sg == 0)
       for (int64_t i = lane; i < c.vb; i += kWave) ms_add(acc, logit_at<kBf16>(rowp, i), scale);
     if (sg == c.nseg - 1)
       for (int64_t i = c.ve + lane; i < V; i += kWave) ms_add(acc, logit_at<kBf16>(rowp, i), scale);
-    const int64_t v0 = sg * kSegVec;
-    const int64_t v1 = v0 + kSegVec < c.nvec ? v0 + kSegVec : c.nvec;
-    for (int64_t base = v0; base < v1; base += (int64_t)kWave * kUnroll) {
-      uint4 v[kUnroll];
+  };
+  auto emit = [&](MS acc, int64_t sg) {
+    acc = wave_merge(acc, lane);
+    if (lane == 0) seg_out[row * nseg_max + sg] = make_double2((double)acc.m, acc.s);
+  };
+  if (c.nvec == 0) {  // no aligned middle: the one segment is all scalars
+    MS acc{-INFINITY, 0.0};
+    scalars(acc, 0);
+    emit(acc, 0);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(rowp + c.vb), (short)0, (int)(c.nvec * 16), kRawBufferWord3);
+  auto load = [&](uint4* dst, int64_t base) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t vid = (uint32_t)(base + u * kWave + lane);
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vid * 16u, 0, kCacheNonTemporal);
-        v[u] = make_uint4(w.x, w.y, w.z, w.w);  // past the row: zeros, skipped below
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t vid = (uint32_t)(base + u * kWave + lane);
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vid * 16u, 0, kCacheNonTemporal);
+      dst[u] = make_uint4(w.x, w.y, w.z, w.w);  // past the row: zeros, skipped below
+    }
+  };
+  const int64_t v0 = wa * kSegVec;
+  const int64_t v1 = wb * kSegVec < c.nvec ? wb * kSegVec : c.nvec;
+  MS acc{-INFINITY, 0.0};
+  scalars(acc, wa);
+  auto add_step = [&](const uint4* src, int64_t base) {
+    if (base + kStep <= v1) {  // wave-uniform: every vector of the step is in the row
+      ms_add_vecs<kBf16, kUnroll>(acc, src, scale);
+    } else {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (base + u * kWave + lane < v1) ms_add_vec<kBf16>(acc, v[u], scale);
+        if (base + u * kWave + lane < v1) ms_add_vecs<kBf16, 1>(acc, src + u, scale);
     }
-#pragma unroll
-    for (int k = 1; k < kWave; k <<= 1) {
-      const uint64_t sb = (uint64_t)__double_as_longlong(acc.s);
-      const uint32_t lo = xor_lanes((uint32_t)sb, k, lane), hi = xor_lanes((uint32_t)(sb >> 32), k, lane);
-      const MS o{__uint_as_float(xor_lanes(__float_as_uint(acc.m), k, lane)),
-                 __longlong_as_double((long long)(((uint64_t)hi << 32) | lo))};
-      acc = ms_merge(acc, o);
+    const int64_t next = base + kStep;
+    if (next % kSegVec == 0 || next >= v1) {  // the step closed its segment
+      const int64_t sg = base / kSegVec;
+      emit(acc, sg);
+      acc = MS{-INFINITY, 0.0};
+      if (next < v1) scalars(acc, sg + 1);
     }
-    if (lane == 0) seg_out[row * nseg_max + sg] = make_double2((double)acc.m, acc.s);
+  };
+  uint4 bufA[kUnroll], bufB[kUnroll];
+  load(bufA, v0);
+  int64_t base = v0;
+  for (; base + kStep < v1; base += 2 * kStep) {  // the next step is always loaded ahead
+    load(bufB, base + kStep);
+    add_step(bufA, base);
+    load(bufA, base + 2 * kStep);
+    if (base + kStep < v1) add_step(bufB, base + kStep);
   }
+  if (base < v1) add_step(bufA, base);
 }
 
 // Target probability of token v in row `rowp`: 2^(x - log2-sum-exp) in fp64, x the
@@ -185,64 +256,121 @@ __device__ __forceinline__ double token_weight(const void* rowp, int64_t v, floa
   return exp2((double)(logit_at<kBf16>(rowp, v) * scale) - lse2);
 }
 
+// Inclusive prefix sum over the workgroup, in a fixed order (wave scans with
+// shuffles, then the wave totals in wave order); every thread passes one value.
+__device__ __forceinline__ double block_prefix(double v, double* s_wave, int tid) {
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = v;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  __syncthreads();
+  return base + v;
+}
+
+constexpr int kMaxPer = 17;  // tokens per thread in the rescanned segment (kSeg / 256 + 1)
+
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void verify_kernel(
     const void* __restrict__ logits, int64_t V, int L, int64_t nseg_max, float scale,
     const double2* __restrict__ segs, const int32_t* __restrict__ path,
     const int32_t* __restrict__ cand, const float* __restrict__ q, uint64_t seed,
     int32_t* __restrict__ out_accepted, int32_t* __restrict__ out_token) {
+  static_assert(kSeg / kThreads + 1 <= kMaxPer, "rescan share");
   __shared__ double s_lse2[kMaxL + 1];
   __shared__ int32_t s_cand[kK];
   __shared__ double s_corr[kK];
   __shared__ double s_mass[kMaxSeg];
-  __shared__ double s_share[kThreads];
-  __shared__ int s_k, s_seg;
+  __shared__ double s_wave[kWaves];
+  __shared__ int s_k, s_seg, s_pick, s_last;
   __shared__ double s_rest;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int64_t b = blockIdx.x;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  auto row_ptr = [&](int64_t row) {
+    return kBf16 ? (const void*)(static_cast<const uint16_t*>(logits) + row * V)
+                 : (const void*)(static_cast<const float*>(logits) + row * V);
+  };
 
-  // log2-sum-exp of rows (b, 0..L): the row's segments merged in order
-  if (tid <= L) {
-    const int64_t row = b * (L + 1) + tid;
-    const void* rowp = kBf16 ? (const void*)(static_cast<const uint16_t*>(logits) + row * V)
-                             : (const void*)(static_cast<const float*>(logits) + row * V);
-    const RowCut c = row_cut<kBf16>(rowp, V);
-    MS r{-INFINITY, 0.0};
-    for (int64_t i = 0; i < c.nseg; ++i) {
-      const double2 p = segs[row * nseg_max + i];
-      r = ms_merge(r, MS{(float)p.x, p.y});
+  // log2-sum-exp of rows (b, 0..L): wave w merges rows w, w + 4, ...; a lane loads
+  // segments lane, lane + 64, ... of each of its rows before any merge
+  {
+    constexpr int kRowsPerWave = (kMaxL + 1 + kWaves - 1) / kWaves;
+    constexpr int kSegPerLane = 2;  // segment pairs a lane holds per row before merging
+    double2 held[kRowsPerWave][kSegPerLane];
+    int64_t nseg_of[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int t = wave + i * kWaves;
+      const int64_t row = b * (L + 1) + (t <= L ? t : L);
+      nseg_of[i] = row_cut<kBf16>(row_ptr(row), V).nseg;
+#pragma unroll
+      for (int u = 0; u < kSegPerLane; ++u) {
+        const int64_t sg = lane + u * kWave;
+        held[i][u] = make_double2(-INFINITY, 0.0);
+        if (t <= L && sg < nseg_of[i]) held[i][u] = segs[row * nseg_max + sg];
+      }
     }
-    s_lse2[tid] = r.s > 0.0 ? (double)r.m + log2(r.s) : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int t = wave + i * kWaves;
+      const int64_t row = b * (L + 1) + (t <= L ? t : L);
+      MS r{-INFINITY, 0.0};
+#pragma unroll
+      for (int u = 0; u < kSegPerLane; ++u) r = ms_merge(r, MS{(float)held[i][u].x, held[i][u].y});
+      for (int64_t sg = lane + kSegPerLane * kWave; sg < nseg_of[i]; sg += kWave) {  // long rows
+        const double2 p = segs[row * nseg_max + sg];
+        r = ms_merge(r, MS{(float)p.x, p.y});
+      }
+      r = wave_merge(r, lane);
+      if (lane == 0 && t <= L) s_lse2[t] = r.s > 0.0 ? (double)r.m + log2(r.s) : -INFINITY;
+    }
   }
   __syncthreads();
 
-  // accept tests, in order, up to the first rejection
-  if (tid == 0) {
-    int k = L;
-    for (int t = 0; t < L; ++t) {
+  // accept tests of all positions at once (lane t of wave 0); the block keeps the
+  // draft tokens before the first rejection
+  if (tid < kWave) {
+    bool keep = false;  // lanes >= L stand for "past the block": rejected
+    if (tid < L) {
+      const int t = tid;
       const int64_t row = b * (L + 1) + t;
       int32_t x = path[b * L + t];
+      int32_t cj[kK];
+      float qj[kK];
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {  // every load issued before any compare
+        cj[j] = cand[(b * L + t) * kK + j];
+        qj[j] = q[(b * L + t) * kK + j];
+      }
       float qx = 0.0f;
-      for (int j = 0; j < kK; ++j)
-        if (cand[(b * L + t) * kK + j] == x) qx = q[(b * L + t) * kK + j];
+#pragma unroll
+      for (int j = 0; j < kK; ++j) qx = cj[j] == x ? qj[j] : qx;
       x = x < 0 ? 0 : (x >= V ? (int32_t)(V - 1) : x);
       const float xs = logit_at<kBf16>(logits, row * V + x) * scale;
       const double p = exp2((double)xs - s_lse2[t]);
       uint32_t w[4];
       philox4x32_10(0u, (uint32_t)t, (uint32_t)b, 1u, k0, k1, w);
-      if (!(uniform23(w[0]) < p / (double)qx)) {
-        k = t;
-        break;
-      }
+      keep = uniform23(w[0]) < p / (double)qx;
     }
-    s_k = k;
+    const uint64_t rejected = __ballot(!keep);  // bit L is always set (L <= 16 < 64)
+    if (tid == 0) {
+      const int k = (int)__builtin_ctzll(rejected);
+      s_k = k < L ? k : L;
+    }
   }
   __syncthreads();
   const int k = s_k;
   const int64_t row = b * (L + 1) + k;
-  const void* rowp = kBf16 ? (const void*)(static_cast<const uint16_t*>(logits) + row * V)
-                           : (const void*)(static_cast<const float*>(logits) + row * V);
+  const void* rowp = row_ptr(row);
   const double lse2 = s_lse2[k];
   const RowCut c = row_cut<kBf16>(rowp, V);
   if (tid < kK) {
@@ -263,98 +391,116 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     const double2 p = segs[row * nseg_max + sg];
     s_mass[sg] = p.y * exp2(p.x - lse2);
   }
-  __syncthreads();
   if (tid == 0) {
-    for (int j = 0; j < kK; ++j) {  // the residual's corrections, where they fall
+    s_last = -1;
+    s_seg = 0;  // (no segment with mass at all: the rescan below picks the segment's first token)
+  }
+  __syncthreads();
+  if (tid == 0) {  // the residual's corrections, where they fall (in candidate order)
+    for (int j = 0; j < kK; ++j) {
       const int64_t cd = s_cand[j];
       if (cd < 0 || cd >= V) continue;
-      const int64_t sg = cd < c.vb + kSeg ? 0 : (cd - c.vb) / kSeg < c.nseg ? (cd - c.vb) / kSeg
-                                                                                : c.nseg - 1;
+      const int64_t sg = cd < c.vb + kSeg ? 0 : ((cd - c.vb) / kSeg < c.nseg ? (cd - c.vb) / kSeg : c.nseg - 1);
       s_mass[sg] -= s_corr[j];
     }
-    double total = 0.0;
-    for (int64_t sg = 0; sg < c.nseg; ++sg) total += s_mass[sg] > 0.0 ? s_mass[sg] : 0.0;
+  }
+  __syncthreads();
+  // Which segment: thread i holds a group of g consecutive segments; a prefix sum
+  // over the groups gives the group the draw falls in, its thread walks it.
+  {
+    const int64_t g = (c.nseg + kThreads - 1) / kThreads;
+    const int64_t s0 = tid * g;
+    double gm = 0.0;
+    for (int64_t sg = s0; sg < s0 + g && sg < c.nseg; ++sg) gm += s_mass[sg] > 0.0 ? s_mass[sg] : 0.0;
+    const double incl = block_prefix(gm, s_wave, tid);
+    if (tid == kThreads - 1) s_rest = incl;  // the total mass
+    __syncthreads();
     uint32_t w[4];
     philox4x32_10(0u, (uint32_t)k, (uint32_t)b, 2u, k0, k1, w);
     const double u = ((double)(w[0] >> 9) * 0x1p23 + (double)(w[1] >> 9) + 0.5) * 0x1p-46;
-    const double target = u * total;
-    double cum = 0.0;
-    int64_t pick = -1, last = 0;
-    for (int64_t sg = 0; sg < c.nseg; ++sg) {
-      const double m = s_mass[sg] > 0.0 ? s_mass[sg] : 0.0;
-      if (m <= 0.0) continue;
-      last = sg;
-      if (cum + m >= target) {
-        pick = sg;
-        break;
+    const double target = u * s_rest;
+    const double excl = incl - gm;
+    if (gm > 0.0) atomicMax(&s_last, tid);
+    __syncthreads();
+    bool mine = gm > 0.0 && excl < target && target <= incl;
+    if (!mine && tid == s_last && target > incl) mine = true;  // rounding past the end
+    if (mine) {
+      double cum = excl;
+      int64_t pick = -1, lastpos = -1;
+      for (int64_t sg = s0; sg < s0 + g && sg < c.nseg; ++sg) {
+        const double m = s_mass[sg] > 0.0 ? s_mass[sg] : 0.0;
+        if (m <= 0.0) continue;
+        lastpos = sg;
+        if (cum + m >= target) {
+          pick = sg;
+          break;
+        }
+        cum += m;
       }
-      cum += m;
+      s_seg = (int)(pick >= 0 ? pick : lastpos);
+      // past the end by rounding: a rest beyond any sum takes the segment's last token
+      s_rest = pick >= 0 ? target - cum : 1e300;
     }
-    if (pick < 0) {  // rounding past the end: the last segment with mass, from its end
-      pick = last;
-      cum = 1e300;
-    }
-    s_seg = (int)pick;
-    s_rest = target - cum;
   }
   __syncthreads();
-  // the segment, exactly: thread i sums its contiguous share of it in order
+  // The segment, exactly: thread i weighs its contiguous share of it (candidates'
+  // corrections held in registers), a prefix sum over the shares gives the share
+  // the draw falls in, and its thread picks the token.
   int64_t lo, hi;
   seg_range(c, V, s_seg, lo, hi);
   const int64_t per = (hi - lo + kThreads - 1) / kThreads;
-  auto weight = [&](int64_t v) {
-    double wv = token_weight<kBf16>(rowp, v, scale, lse2);
+  int32_t cj[kK];
+  double dj[kK];
 #pragma unroll
-    for (int j = 0; j < kK; ++j)
-      if (s_cand[j] == v) wv -= s_corr[j];
-    return wv > 0.0 ? wv : 0.0;
-  };
-  {
-    const int64_t a = lo + tid * per < hi ? lo + tid * per : hi;
-    const int64_t e = a + per < hi ? a + per : hi;
-    double sum = 0.0;
-    for (int64_t v = a; v < e; ++v) sum += weight(v);
-    s_share[tid] = sum;
+  for (int j = 0; j < kK; ++j) {
+    cj[j] = s_cand[j];
+    dj[j] = s_corr[j];
+  }
+  const int64_t a0 = lo + tid * per < hi ? lo + tid * per : hi;
+  const int64_t e0 = a0 + per < hi ? a0 + per : hi;
+  double wv[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int64_t v = a0 + i;
+    double x = 0.0;
+    if (v < e0) {
+      x = token_weight<kBf16>(rowp, v, scale, lse2);
+#pragma unroll
+      for (int j = 0; j < kK; ++j) x = cj[j] == v ? x - dj[j] : x;
+      x = x > 0.0 ? x : 0.0;
+    }
+    wv[i] = x;
+  }
+  double share = 0.0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) share += wv[i];
+  if (tid == 0) {
+    s_pick = -1;
+    s_last = -1;
+  }
+  const double incl = block_prefix(share, s_wave, tid);  // (holds barriers)
+  const double excl = incl - share;
+  const double rest = s_rest;
+  if (share > 0.0) atomicMax(&s_last, tid);
+  __syncthreads();
+  bool mine = share > 0.0 && excl < rest && rest <= incl;
+  if (!mine && tid == s_last && rest > incl) mine = true;  // rounding past the end
+  if (mine) {
+    double cum = excl;
+    int64_t pick = -1, lastpos = a0;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (pick >= 0 || wv[i] <= 0.0) continue;
+      lastpos = a0 + i;
+      cum += wv[i];
+      if (cum >= rest) pick = a0 + i;
+    }
+    s_pick = (int)(pick >= 0 ? pick : lastpos);
   }
   __syncthreads();
   if (tid == 0) {
-    const double rest = s_rest;
-    double cum = 0.0;
-    int64_t pick = -1;
-    int last_share = -1;
-    for (int i = 0; i < kThreads && pick < 0; ++i) {
-      if (s_share[i] <= 0.0) continue;
-      last_share = i;
-      if (cum + s_share[i] < rest) {
-        cum += s_share[i];
-        continue;
-      }
-      const int64_t a = lo + i * per < hi ? lo + i * per : hi;
-      const int64_t e = a + per < hi ? a + per : hi;
-      for (int64_t v = a; v < e; ++v) {
-        const double wv = weight(v);
-        if (wv <= 0.0) continue;
-        cum += wv;
-        if (cum >= rest) {
-          pick = v;
-          break;
-        }
-      }
-    }
-    if (pick < 0) {  // rounding past the end: the last token with weight
-      pick = lo;
-      if (last_share >= 0) {
-        const int64_t a = lo + last_share * per < hi ? lo + last_share * per : hi;
-        const int64_t e = a + per < hi ? a + per : hi;
-        for (int64_t v = e - 1; v >= a; --v)
-          if (weight(v) > 0.0) {
-            pick = v;
-            break;
-          }
-      }
-    }
     out_accepted[b] = k;
-    out_token[b] = (int32_t)pick;
+    out_token[b] = s_pick >= 0 ? s_pick : (int32_t)lo;
   }
 }
 
@@ -369,13 +515,9 @@ VerifyPlan plan_verify(int64_t batch, int64_t L, int64_t V, int esize) {
   const int64_t rows = batch * (L + 1);
   // segments per row (at most one more than the aligned middle needs)
   p.nseg = cdiv(V, kSeg) + 1;
-  // workgroups per row: enough rows x parts to fill the chip, four segments apiece at least
-  int64_t parts = 1;
-  if (rows < kTargetBlocks) {
-    parts = cdiv(kTargetBlocks, rows);
-    const int64_t maxp = cdiv(p.nseg, kWaves);
-    if (parts > maxp) parts = maxp;
-  }
+  // workgroups per row: about two segments per wave, so that the launch is many
+  // short workgroups (a ragged last round of the chip's slots costs little)
+  const int64_t parts = cdiv(p.nseg, 2 * kWaves);
   p.parts = (int)parts;
   p.ws_bytes = align_up((size_t)rows * p.nseg * sizeof(double2), 256);
   return p;
