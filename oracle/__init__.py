@@ -24,8 +24,12 @@ Pinning status (what each function is checked against, in tests/):
                  chi-square), acceptance rate = sum min(p, q), q = p -> all accepted,
                  target mass off the candidates -> rejected at once, inverse CDF by
                  definition, draft_probs = scipy softmax
+  conv2          static kernel == numpy.convolve along the block; identity and shift
+                 kernels exact; a planted one-weight case fixes taps, groups and
+                 predecessors; one group's weights move exactly its 16 channels by
+                 a closed form; x_prev reaches position 0 only; scalar fsum loops
 """
-from . import recall, verify
+from . import conv, recall, verify
 from .philox import gumbel, philox4x32_10, uniform_from_word
 from .selector import (
     SequenceResult,
@@ -42,6 +46,7 @@ from .selector import (
 
 __all__ = [
     "SequenceResult",
+    "conv",
     "gate",
     "gumbel",
     "pair_scores",
