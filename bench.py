@@ -200,6 +200,8 @@ def main() -> int:
     ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the top-16 traffic record from FETCH_SIZE / WRITE_SIZE counter runs and exit")
+    ap.add_argument("--conv", action="store_true",
+                    help="also time dfs_conv2 (two-tap dynamic convolution) on x [batch, L, d] of the workload")
     ap.add_argument("--verify", action="store_true",
                     help="also time dfs_select_draft + dfs_verify against synthetic target logits "
                          "[batch, L + 1, V] (the drafter's logits plus noise, one more random row)")
@@ -379,6 +381,35 @@ def main() -> int:
                       "draft_temperature": T}
         del tgt
 
+    conv_out = None
+    if args.conv:
+        # One convolution site of the drafter at this workload's shape: x [batch, L, d].
+        from workloads.conv import make_conv
+        from tests.parity import to_dev
+
+        ci = make_conv(cfg)
+        cx = [to_dev(ci.x)]
+        cargs = (to_dev(ci.x_prev), to_dev(ci.base), to_dev(ci.W_c))
+        xb = cx[0].numel() * cx[0].element_size()
+        ncs = max(3, -(-(512 << 20) // xb))
+        cx += [cx[0].clone() for _ in range(ncs - 1)]
+        cy = torch.empty_like(cx[0])
+        cws = torch.empty(max(1, dfs.conv2_workspace_bytes(cfg.batch, cfg.L, cfg.d, cx[0].dtype)),
+                          dtype=torch.uint8, device=cy.device)
+        it = iter(range(1 << 30))
+        conv_ms = timed(lambda: dfs.conv2(cx[next(it) % ncs], *cargs, out=cy, workspace=cws),
+                        n=max(50, args.steps))
+        es = cx[0].element_size()
+        D, rows = cfg.d, cfg.batch * cfg.L
+        cbytes = 2 * rows * D * es + cfg.batch * D * es + 2 * D * es + (D // 8) * D * es
+        cflops = 2 * rows * D * (D // 8) + 4 * rows * D
+        conv_out = {"ms": conv_ms, "x_sets": ncs, "bytes_per_launch": cbytes, "flops_per_launch": cflops,
+                    "GBps": cbytes / (conv_ms * 1e-3) / 1e9,
+                    "hbm_frac": cbytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "TFLOPs": cflops / (conv_ms * 1e-3) / 1e12,
+                    "mfma_frac": cflops / (conv_ms * 1e-3) / 1e12 / (2500.0 if es == 2 else 157.3)}
+        del cx, cy
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device=logits2d.device).fill_(1)
@@ -414,6 +445,8 @@ def main() -> int:
     }
     if verify_out is not None:
         out["verify"] = verify_out
+    if conv_out is not None:
+        out["conv"] = conv_out
     if graph_ms is not None:
         out["graph_replay"] = {"ms_per_step": graph_ms, "value": cfg.batch / (graph_ms * 1e-3),
                                "input_sets": 1}

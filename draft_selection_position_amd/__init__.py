@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "DfsError", "K", "E", "MAX_L", "lib", "lib_path", "topk", "gate", "pair_scores", "walk",
     "select", "Selector", "select_workspace_bytes", "topk_workspace_bytes",
-    "gate_workspace_bytes", "status_str",
+    "gate_workspace_bytes", "status_str", "conv2", "conv2_workspace_bytes",
 ]
 
 K = 16
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.dfs_verify.argtypes = [vp, c_int, i64, i64, i64, i32p, i32p, f32p, c_int, c_double, u64, vp, sz,
                                  i32p, i32p, vp]
         L.dfs_verify.restype = c_int
+        L.dfs_conv2_workspace_bytes.argtypes, L.dfs_conv2_workspace_bytes.restype = [i64, i64, i64, c_int], sz
+        L.dfs_conv2.argtypes = [vp, vp, vp, vp, c_int, i64, i64, i64, vp, vp, sz, vp]
+        L.dfs_conv2.restype = c_int
         _lib = L
     return _lib
 
@@ -343,6 +346,40 @@ def verify(target_logits: torch.Tensor, path: torch.Tensor, cand: torch.Tensor, 
                             q.data_ptr(), K, float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb,
                             accepted.data_ptr(), token.data_ptr(), _stream(target_logits.device)), "dfs_verify")
     return accepted, token
+
+
+def conv2_workspace_bytes(batch: int, L: int, D: int, dtype: torch.dtype) -> int:
+    code = F32 if dtype == torch.float32 else BF16 if dtype == torch.bfloat16 else -1
+    return int(lib().dfs_conv2_workspace_bytes(batch, L, D, code))
+
+
+def conv2(x: torch.Tensor, x_prev: torch.Tensor, base: torch.Tensor, W_c: torch.Tensor,
+          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Two-tap dynamic depthwise convolution across block positions (see dfs_conv2).
+
+    x [batch, L, D], x_prev [batch, D], base [2, D], W_c [D/16, 2, D], all of one dtype
+    (bf16 or fp32).  Returns y [batch, L, D] (written into ``out`` when given)."""
+    _dev(x, "x")
+    dt = _dtype_code(x, "x")
+    _dev(x_prev, "x_prev", x.dtype)
+    _dev(base, "base", x.dtype)
+    _dev(W_c, "W_c", x.dtype)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, L, D]")
+    batch, L, D = x.shape
+    if x_prev.shape != (batch, D) or base.shape != (2, D) or W_c.shape != (D // 16, 2, D):
+        raise ValueError(f"x_prev must be [{batch}, {D}], base [2, {D}] and W_c [{D // 16}, 2, {D}]")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _dev(out, "out", x.dtype)
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    nb = int(lib().dfs_conv2_workspace_bytes(batch, L, D, dt))
+    ws = _ws_arg(workspace, x.device, nb)
+    _check(lib().dfs_conv2(x.data_ptr(), x_prev.data_ptr(), base.data_ptr(), W_c.data_ptr(), dt, batch, L, D,
+                           out.data_ptr(), _ptr(ws), nb, _stream(x.device)), "dfs_conv2")
+    return out
 
 
 class Selector:

@@ -177,12 +177,13 @@ const char* dfs_status_str(int status) {
     case DFS_E_NULL: return "DFS_E_NULL: a required pointer is NULL";
     case DFS_E_SHAPE: return "DFS_E_SHAPE: a size is out of range";
     case DFS_E_UNSUPPORTED:
-      return "DFS_E_UNSUPPORTED: k must be 16, E 256, d a multiple of 8, dtype and walk mode known";
+      return "DFS_E_UNSUPPORTED: k must be 16, E 256, d a multiple of 8 (convolution: 256), dtype and walk mode known";
     case DFS_E_WORKSPACE: return "DFS_E_WORKSPACE: workspace missing or too small";
     case DFS_E_ALIGN: return "DFS_E_ALIGN: a pointer is not aligned as required";
     case DFS_E_HIP: return "DFS_E_HIP: no usable HIP device, or a HIP launch failed";
     case DFS_E_ARCH: return "DFS_E_ARCH: the current device is not gfx950";
-    case DFS_E_ARG: return "DFS_E_ARG: invalid scalar argument (temperature must be finite and > 0)";
+    case DFS_E_ARG:
+      return "DFS_E_ARG: invalid argument (temperature must be finite and > 0; outputs must not overlap inputs)";
     default: return "unknown dfs status";
   }
 }
@@ -310,6 +311,47 @@ int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t
   (void)hipGetLastError();
   return hip_status(launch_verify(p, target_logits, dt == DFS_BF16, path, cand, q, temperature,
                                   seed, ws, out_accepted, out_token, stream));
+}
+
+// Rows and width the convolution takes; 0 when they are out of range.
+static int check_conv2_shape(int64_t batch, int64_t L, int64_t D, int dt) {
+  if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
+  if (batch < 1 || L < 1 || L > DFS_CONV_MAX_L || D < 256 || D > kMaxD) return DFS_E_SHAPE;
+  if (D % 256 != 0) return DFS_E_UNSUPPORTED;
+  if (batch > ((int64_t)1 << 31) / L) return DFS_E_SHAPE;
+  if (dt == DFS_F32 && batch * L * D > conv2_max_f32_elems()) return DFS_E_SHAPE;
+  return DFS_OK;
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+size_t dfs_conv2_workspace_bytes(int64_t batch, int64_t L, int64_t D, dfs_dtype_t dt) {
+  if (check_conv2_shape(batch, L, D, dt) != DFS_OK) return 0;
+  return conv2_workspace_bytes(batch * L, D, dt == DFS_BF16);
+}
+
+int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W_c, dfs_dtype_t dt,
+              int64_t batch, int64_t L, int64_t D, void* y, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  if (!x || !x_prev || !base || !W_c || !y) return DFS_E_NULL;
+  int st = check_conv2_shape(batch, L, D, dt);
+  if (st != DFS_OK) return st;
+  if (!aligned(x, 16) || !aligned(x_prev, 16) || !aligned(base, 16) || !aligned(W_c, 16) ||
+      !aligned(y, 16))
+    return DFS_E_ALIGN;
+  const size_t es = (size_t)esize(dt);
+  const size_t ybytes = (size_t)(batch * L * D) * es;
+  if (overlaps(y, ybytes, x, ybytes) || overlaps(y, ybytes, x_prev, (size_t)(batch * D) * es))
+    return DFS_E_ARG;
+  const size_t need = conv2_workspace_bytes(batch * L, D, dt == DFS_BF16);
+  if (need > 0 && (!ws || ws_bytes < need)) return DFS_E_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_conv2(x, x_prev, base, W_c, dt == DFS_BF16, batch, L, D, y, ws, stream));
 }
 
 }  // extern "C"

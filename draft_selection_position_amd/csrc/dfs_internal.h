@@ -102,4 +102,13 @@ hipError_t launch_verify(const VerifyPlan& p, const void* logits, bool bf16, con
                          const int32_t* cand, const float* q, double temperature, uint64_t seed,
                          void* ws, int32_t* out_accepted, int32_t* out_token, hipStream_t stream);
 
+// ---------------------------------------------------------------- two-tap convolution
+// bf16: one fused kernel (no workspace).  fp32: correction [rows, D/8] in `ws`, then
+// an elementwise kernel; its launches need rows * D below conv2_max_f32_elems().
+size_t conv2_workspace_bytes(int64_t rows, int64_t D, bool bf16);
+int64_t conv2_max_f32_elems();
+hipError_t launch_conv2(const void* x, const void* x_prev, const void* base, const void* W_c,
+                        bool bf16, int64_t batch, int64_t L, int64_t D, void* y, void* ws,
+                        hipStream_t stream);
+
 }  // namespace dfs

@@ -51,6 +51,7 @@ extern "C" {
 #define DFS_E 256     /* embedding and gate width */
 #define DFS_MAX_L 16  /* longest block handled; the post's blocks span 4 to 16 tokens */
 #define DFS_MAX_D (1 << 20) /* widest hidden state handled */
+#define DFS_CONV_MAX_L 65536 /* longest run of positions dfs_conv2 takes per sequence */
 
 typedef enum {
   DFS_OK = 0,
@@ -62,7 +63,8 @@ typedef enum {
   DFS_E_ALIGN = 5,       /* a pointer is not aligned as documented */
   DFS_E_HIP = 6,         /* no usable HIP device, or a HIP launch error */
   DFS_E_ARCH = 7,        /* the current device is not gfx950 */
-  DFS_E_ARG = 8          /* a scalar argument is invalid (e.g. temperature <= 0 for sampling) */
+  DFS_E_ARG = 8          /* an argument is invalid (temperature <= 0 for sampling; an output
+                            that overlaps an input) */
 } dfs_status_t;
 
 typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype_t;
@@ -199,11 +201,33 @@ int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t
                uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_accepted, int32_t* out_token,
                hipStream_t stream);
 
+/* ---------------------------------------------------------------- two-tap convolution
+ * The drafter's two-tap dynamic depthwise convolution across block positions (blog
+ * post "DFlash 2: Keep Drafting Parallel", section "A Lightweight Local
+ * Convolution"; its equation Conv_k(x)_t = k_{t,0} . x_t + k_{t,1} . x_{t-1}):
+ *   c_t[2g + tap]   = sum_i W_c[g, tap, i] x_t[i]          (one correction per 16 channels)
+ *   k_{t,tap}[ch]   = base[tap, ch] + c_t[2 (ch / 16) + tap]
+ *   y_t[ch]         = k_{t,0}[ch] x_t[ch] + k_{t,1}[ch] x_{t-1}[ch],  x_{-1} = x_prev
+ *   x [batch, L, D]   the sublayer input at every block position (row-major)
+ *   x_prev [batch, D] the last verified token's representation at the same site
+ *   base [2, D]       the learned base kernel (tap 0: current position, tap 1: predecessor)
+ *   W_c [D/16, 2, D]  correction weights, K-contiguous (row 2g + tap)
+ *   y [batch, L, D]   output, same dtype as the inputs; must not overlap x or x_prev
+ * All of dtype dt (bf16: correction on the matrix cores with fp32 sums, y rounded to
+ * nearest-even bf16; fp32: fp32 throughout).  D a multiple of 256 in [256, DFS_MAX_D],
+ * 1 <= L <= DFS_CONV_MAX_L, batch * L < 2^31 (fp32: batch * L * D <= 2^34).  Every
+ * pointer 16-byte aligned, ws 256-byte aligned.
+ * ws: dfs_conv2_workspace_bytes(batch, L, D, dt) bytes (0 for bf16: ws may be NULL). */
+size_t dfs_conv2_workspace_bytes(int64_t batch, int64_t L, int64_t D, dfs_dtype_t dt);
+int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W_c, dfs_dtype_t dt,
+              int64_t batch, int64_t L, int64_t D, void* y, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* dfs_status_str(int status);
 
 /* ABI version of this header and library (major * 100 + minor). */
-#define DFS_ABI_VERSION 101
+#define DFS_ABI_VERSION 102
 int dfs_abi_version(void);
 
 #ifdef __cplusplus

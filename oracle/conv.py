@@ -40,7 +40,7 @@ def correction(x: np.ndarray, W_c: np.ndarray) -> np.ndarray:
     G, taps, D = W.shape
     if taps != 2 or D != x.shape[-1] or G * GROUP != D:
         raise ValueError(f"W_c must be [D/16, 2, D] for D = {x.shape[-1]}, got {W.shape}")
-    return np.einsum("...k,gpk->...gp", x, W)
+    return (x @ W.reshape(G * taps, D).T).reshape(x.shape[:-1] + (G, taps))
 
 
 def coefficients(x: np.ndarray, base: np.ndarray, W_c: np.ndarray) -> np.ndarray:

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.dfs_abi_version() == 101
+    assert L.dfs_abi_version() == 102
     for code in range(9):
         s = dfs.status_str(code)
         assert s.startswith("DFS_")
@@ -174,3 +174,28 @@ def test_valid_arguments_without_a_device_report_hip_error(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _topk(L, rows=4096, V=151936) == E_HIP
+
+
+def _conv(L, x=P, xp=P + 0x100000, base=P + 0x200000, W=P + 0x300000, dt=1, batch=2, Lp=4, D=512,
+          y=P + 0x1000000, ws=None, wsb=0):
+    return L.dfs_conv2(x, xp, base, W, dt, batch, Lp, D, y, ws, wsb, None)
+
+
+def test_conv2_validation(L):
+    assert _conv(L, x=None) == E_NULL
+    assert _conv(L, y=None) == E_NULL
+    assert _conv(L, dt=7) == E_UNSUP
+    assert _conv(L, D=128) == E_SHAPE
+    assert _conv(L, D=768 + 16) == E_UNSUP  # not a multiple of 256
+    assert _conv(L, Lp=0) == E_SHAPE
+    assert _conv(L, batch=0) == E_SHAPE
+    assert _conv(L, x=P + 8) == E_ALIGN
+    assert _conv(L, y=P + 64) == E_ARG  # overlaps x
+    assert _conv(L, y=P + 0x100000) == E_ARG  # overlaps x_prev
+    # fp32 needs a workspace for the correction; bf16 needs none
+    assert L.dfs_conv2_workspace_bytes(2, 4, 512, 1) == 0
+    nb = L.dfs_conv2_workspace_bytes(2, 4, 512, 0)
+    assert nb >= 2 * 4 * 64 * 4
+    assert _conv(L, dt=0, ws=None, wsb=0) == E_WS
+    assert _conv(L, dt=0, ws=P + 0x3000000 + 1, wsb=nb) == E_ALIGN
+    assert L.dfs_conv2_workspace_bytes(2, 4, 500, 0) == 0
