@@ -393,12 +393,9 @@ def main() -> int:
         xb = cx[0].numel() * cx[0].element_size()
         ncs = max(3, -(-(512 << 20) // xb))
         cx += [cx[0].clone() for _ in range(ncs - 1)]
-        cy = torch.empty_like(cx[0])
-        cws = torch.empty(max(1, dfs.conv2_workspace_bytes(cfg.batch, cfg.L, cfg.d, cx[0].dtype)),
-                          dtype=torch.uint8, device=cy.device)
+        conv = dfs.Conv2(cfg.batch, cfg.L, cfg.d, dtype=cx[0].dtype)
         it = iter(range(1 << 30))
-        conv_ms = timed(lambda: dfs.conv2(cx[next(it) % ncs], *cargs, out=cy, workspace=cws),
-                        n=max(50, args.steps))
+        conv_ms = timed(lambda: conv(cx[next(it) % ncs], *cargs), n=max(50, args.steps))
         es = cx[0].element_size()
         D, rows = cfg.d, cfg.batch * cfg.L
         cbytes = 2 * rows * D * es + cfg.batch * D * es + 2 * D * es + (D // 8) * D * es
@@ -408,7 +405,7 @@ def main() -> int:
                     "hbm_frac": cbytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "TFLOPs": cflops / (conv_ms * 1e-3) / 1e12,
                     "mfma_frac": cflops / (conv_ms * 1e-3) / 1e12 / (2500.0 if es == 2 else 157.3)}
-        del cx, cy
+        del cx, conv
 
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20

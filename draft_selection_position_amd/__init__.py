@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "DfsError", "K", "E", "MAX_L", "lib", "lib_path", "topk", "gate", "pair_scores", "walk",
     "select", "Selector", "select_workspace_bytes", "topk_workspace_bytes",
-    "gate_workspace_bytes", "status_str", "conv2", "conv2_workspace_bytes",
+    "gate_workspace_bytes", "status_str", "conv2", "conv2_workspace_bytes", "Conv2",
 ]
 
 K = 16
@@ -424,3 +424,39 @@ class Selector:
                       torch.cuda.current_stream(self.device).cuda_stream)
         _check(rc, "dfs_select")
         return self.path, self.scores
+
+
+class Conv2:
+    """Fixed-shape two-tap convolution (dfs_conv2) with its own workspace and output.
+
+    Inputs are checked against the construction-time shape with one tuple
+    comparison each; the call then goes straight to dfs_conv2 and writes ``self.y``.
+    """
+
+    def __init__(self, batch: int, L: int, D: int, device="cuda", dtype=torch.bfloat16):
+        self.device = torch.device(device)
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self._dt = BF16 if dtype == torch.bfloat16 else F32
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("dtype must be bfloat16 or float32")
+        self._dims = (batch, L, D)
+        self._ws_bytes = int(lib().dfs_conv2_workspace_bytes(batch, L, D, self._dt))
+        if D % 256 or D < 256 or batch < 1 or L < 1:
+            raise ValueError("unsupported convolution shape")
+        self.workspace = torch.empty(max(1, self._ws_bytes), dtype=torch.uint8, device=self.device)
+        self.y = torch.empty((batch, L, D), dtype=dtype, device=self.device)
+        self._expect = (((batch, L, D), dtype), ((batch, D), dtype), ((2, D), dtype), ((D // 16, 2, D), dtype))
+        self._fn = lib().dfs_conv2
+
+    def __call__(self, x, x_prev, base, W_c):
+        args = (x, x_prev, base, W_c)
+        for t, (shape, dtype) in zip(args, self._expect):
+            if t.shape != shape or t.dtype != dtype or t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"convolution input must be a contiguous {dtype} tensor of shape {shape} "
+                                 f"on {self.device}")
+        rc = self._fn(x.data_ptr(), x_prev.data_ptr(), base.data_ptr(), W_c.data_ptr(), self._dt, *self._dims,
+                      self.y.data_ptr(), self.workspace.data_ptr(), self._ws_bytes,
+                      torch.cuda.current_stream(self.device).cuda_stream)
+        _check(rc, "dfs_conv2")
+        return self.y

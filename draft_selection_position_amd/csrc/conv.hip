@@ -11,39 +11,35 @@
 // reading: c_t = W_c x_t with W_c [D/16, 2, D] (row 2g + tap), and
 //     k_{t,tap}[ch] = base[tap, ch] + c_t[2 (ch / 16) + tap].
 //
-// bf16 path, one kernel: the correction is a [rows, D] x [D, D/8] product on the
-// matrix cores (V_MFMA_F32_16X16X32_BF16); a workgroup computes 64 rows x 128
-// correction columns (64 groups = 1024 channels), and its epilogue applies the
-// convolution to exactly those rows and channels, so the correction never
-// leaves the chip.  W_c is K-contiguous, which is the MFMA operand order already:
-// no repacking.  Per 64-wide k step a lane holds 16 consecutive k of its row (two
-// MFMAs, the same k permutation on both operands), so each W_c fragment is one
-// full 128-byte line per column.
+// bf16 path: the correction is a [rows, D] x [D, D/8] product on the matrix cores
+// (mfma_tile.h: 128 x 128 tiles staged through LDS); a workgroup's epilogue applies
+// the convolution to exactly its 128 rows and 1024 channels, so the correction
+// never leaves the chip.  W_c is K-contiguous, the operand order the tile wants: no
+// repacking.  Shapes too small to fill the chip split K; an elementwise kernel then
+// adds the split partial sums in split order and applies the convolution (a
+// device-wide fence per workgroup to let the last split do it in place writes
+// back the L2 of a multi-XCD part and measured three times slower).
 // fp32 path (small shapes): the correction by wave dot products into workspace,
 // then an elementwise kernel.
 #include "dfs_device.h"
 #include "dfs_internal.h"
+#include "mfma_tile.h"
 
 namespace dfs {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer
-constexpr int kThreads = 256;                 // 4 waves, one per 32 correction columns
-constexpr int kTileM = 64;                    // rows per workgroup
-constexpr int kTileN = 128;                   // correction columns per workgroup
-constexpr int kKStep = 64;                    // k per step (two MFMAs per tile)
-constexpr int kDepth = 3;                     // k steps in flight per thread
-constexpr int kPitchA = kKStep + 8;           // bf16 per LDS row of the x tile
+constexpr int kThreads = 256;                 // 4 waves
+constexpr int kTileM = tile::kTile;           // rows per workgroup
+constexpr int kTileN = tile::kTile;           // correction columns per workgroup (64 groups)
+constexpr int kKStep = tile::kKStep;
 constexpr int kPitchC = kTileN + 4;           // fp32 per LDS row of the correction tile
-
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+#ifndef DFS_CONV_DEPTH
+#define DFS_CONV_DEPTH 2
+#endif
+#ifndef DFS_CONV_XCD
+#define DFS_CONV_XCD 1
+#endif
+static_assert(kTileM * kPitchC * 4 <= tile::kLdsBytes, "the correction tile reuses the operand stages");
 
 // fp32 -> bf16 bits, round to nearest, ties to even (finite and infinite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -67,95 +63,75 @@ __device__ __forceinline__ uint4 conv8(uint4 xv, uint4 pv, uint4 b0, uint4 b1, f
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-__global__ __launch_bounds__(kThreads) void conv2_bf16_kernel(
+// Workgroup (row tile, column tile, K split): the correction tile on the matrix
+// cores (mfma_tile.h), then either the convolution of the tile's rows over its
+// 1024 channels (one split) or the split's partial sums to `partial`.
+#ifndef DFS_CONV_WAVES_PER_EU
+#define DFS_CONV_WAVES_PER_EU 2
+#endif
+__global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ xprev,
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ Wc, int64_t rows, int L,
-    int64_t D, int ntiles_n, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kPitchA];
-  __shared__ __attribute__((aligned(16))) float sC[kTileM][kPitchC];
+    int64_t D, int ntiles_n, int64_t mtiles, int splits, int ks_per_split,
+    float* __restrict__ partial, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[tile::kLdsBytes / 2];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int r = lane & 15;
   const int q = lane >> 4;
-  const int n_tile = (int)(blockIdx.x % (unsigned)ntiles_n);
-  const int64_t m0 = (int64_t)(blockIdx.x / (unsigned)ntiles_n) * kTileM;
+  const int split = (int)(blockIdx.x % (unsigned)splits);
+  const unsigned p = blockIdx.x / (unsigned)splits;
+#if DFS_CONV_XCD
+  // Workgroups go to the 8 XCDs round-robin: XCD p % 8 takes the row tiles congruent
+  // to it, all column tiles of each, so a row tile's x and the column tiles' W_c
+  // slices are shared through that XCD's L2.
+  const unsigned xcd = p % 8u, jj = p / 8u;
+  const int n_tile = (int)(jj % (unsigned)ntiles_n);
+  const int64_t mt = (int64_t)(jj / (unsigned)ntiles_n) * 8 + xcd;
+  if (mt >= mtiles) return;
+#else
+  const int n_tile = (int)(p % (unsigned)ntiles_n);
+  const int64_t mt = (int64_t)(p / (unsigned)ntiles_n);
+#endif
+  const int64_t m0 = mt * kTileM;
   const int64_t ncols_all = D / 8;
   const int64_t n0 = (int64_t)n_tile * kTileN;
   const int ncols = (int)(ncols_all - n0 < kTileN ? ncols_all - n0 : kTileN);  // a multiple of 32
-  const bool wave_on = 32 * wave < ncols;
   const int tile_rows = (int)(rows - m0 < kTileM ? rows - m0 : kTileM);
-
-  // x rows [m0, m0 + tile_rows): rows past the end read as zeros (range check)
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(x + m0 * D), (short)0, (int)((int64_t)tile_rows * D * 2), kRawBufferWord3);
-  const uint32_t a_voff = (uint32_t)((((int64_t)(tid >> 2)) * D + 16 * (tid & 3)) * 2);
-  // W_c rows [n0, n0 + ncols): this wave's are 32 wave + 16 nt + r
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Wc + n0 * D), (short)0, (int)((int64_t)ncols * D * 2), kRawBufferWord3);
-  const uint32_t b_voff0 = (uint32_t)(((int64_t)(32 * wave + r) * D + 16 * q) * 2);
-  const uint32_t b_voff1 = b_voff0 + (uint32_t)(16 * D * 2);
-
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int KS = (int)(D / kKStep);
-  uint4 ra[kDepth][2], rb[kDepth][2][2];
-  auto fill = [&](int j, int ks) {
-    const uint32_t so = (uint32_t)ks * kKStep * 2;
-    ra[j][0] = bload(xr, a_voff, so);
-    ra[j][1] = bload(xr, a_voff + 16, so);
-    rb[j][0][0] = bload(wr, b_voff0, so);
-    rb[j][0][1] = bload(wr, b_voff0 + 16, so);
-    rb[j][1][0] = bload(wr, b_voff1, so);
-    rb[j][1][1] = bload(wr, b_voff1 + 16, so);
-  };
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j) fill(j, j < KS ? j : KS - 1);
+  const int ks0 = split * ks_per_split;
+  const int ks1 = ks0 + ks_per_split < KS ? ks0 + ks_per_split : KS;
 
-  auto step = [&](int ks, int j) {
-    const int st = ks & 1;
-    *reinterpret_cast<uint4*>(&sA[st][tid >> 2][16 * (tid & 3)]) = ra[j][0];
-    *reinterpret_cast<uint4*>(&sA[st][tid >> 2][16 * (tid & 3) + 8]) = ra[j][1];
-    __syncthreads();
-    if (wave_on) {
-      const bf16x8 b00 = __builtin_bit_cast(bf16x8, rb[j][0][0]), b01 = __builtin_bit_cast(bf16x8, rb[j][0][1]);
-      const bf16x8 b10 = __builtin_bit_cast(bf16x8, rb[j][1][0]), b11 = __builtin_bit_cast(bf16x8, rb[j][1][1]);
+  tile::Acc acc;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sA[st][16 * mt + r][16 * q]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sA[st][16 * mt + r][16 * q + 8]);
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b00, acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b10, acc[mt][1], 0, 0, 0);
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b01, acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b11, acc[mt][1], 0, 0, 0);
-      }
-    }
-  };
-  int ks = 0;
-  for (; ks + kDepth <= KS; ks += kDepth) {
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      step(ks + j, j);
-      fill(j, ks + j + kDepth < KS ? ks + j + kDepth : KS - 1);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j)
-    if (ks + j < KS) step(ks + j, j);
+    for (int b = 0; b < 4; ++b) acc.v[a][b] = tile::f32x4{0.f, 0.f, 0.f, 0.f};
+  tile::mma_128x128<DFS_CONV_DEPTH>(tile::rows_rsrc(x + m0 * D, tile_rows, D),
+                                    tile::rows_rsrc(Wc + n0 * D, ncols, D), D, ks0, ks1, lds, acc);
 
-  if (wave_on) {
+  float* sC = reinterpret_cast<float*>(lds);  // [kTileM][kPitchC], after the loop's last barrier
+  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sC[16 * mt + 4 * q + i][32 * wave + 16 * nt + r] = acc[mt][nt][i];
-  }
+      for (int i = 0; i < 4; ++i)
+        sC[(64 * wm + 16 * a + 4 * q + i) * kPitchC + 64 * wn + 16 * b + r] = acc.v[a][b][i];
   __syncthreads();
+  if (splits > 1) {  // this split's partial sums [rows, D/8] of the tile; the epilogue kernel adds them
+    float* pp = partial + (int64_t)split * rows * ncols_all;
+    const int nv = ncols / 4;
+    for (int jb = tid; jb < tile_rows * nv; jb += kThreads) {
+      const int rr = jb / nv;
+      const int v = jb - rr * nv;
+      *reinterpret_cast<float4*>(pp + (m0 + rr) * ncols_all + n0 + 4 * v) =
+          *reinterpret_cast<const float4*>(&sC[rr * kPitchC + 4 * v]);
+    }
+    return;
+  }
 
   // The convolution of this tile's rows over its 8 * ncols channels, eight channels
   // (16 bytes) per job; column 2g + tap of the tile is group g's correction.
@@ -168,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void conv2_bf16_kernel(
     const int64_t ch = ch0 + 8 * v;
     const int64_t b = m / L;
     const int t = (int)(m - b * L);
-    const float c0 = sC[rr][2 * (v >> 1)];
-    const float c1 = sC[rr][2 * (v >> 1) + 1];
+    const float c0 = sC[rr * kPitchC + 2 * (v >> 1)];
+    const float c1 = sC[rr * kPitchC + 2 * (v >> 1) + 1];
     const uint4 xv = *reinterpret_cast<const uint4*>(x + m * D + ch);
     const uint4 pv = t > 0 ? *reinterpret_cast<const uint4*>(x + (m - 1) * D + ch)
                            : *reinterpret_cast<const uint4*>(xprev + b * D + ch);
@@ -177,6 +153,33 @@ __global__ __launch_bounds__(kThreads) void conv2_bf16_kernel(
     const uint4 b1 = *reinterpret_cast<const uint4*>(base + D + ch);
     *reinterpret_cast<uint4*>(y + m * D + ch) = conv8(xv, pv, b0, b1, c0, c1);
   }
+}
+
+// The convolution after a K-split correction: partial sums added in split order.
+__global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xprev,
+    const uint16_t* __restrict__ base, const float* __restrict__ partial, int splits, int64_t rows,
+    int L, int64_t D, uint16_t* __restrict__ y) {
+  const int64_t nvec = D / 8;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= rows * nvec) return;
+  const int64_t m = i / nvec;
+  const int64_t ch = 8 * (i - m * nvec);
+  const int64_t b = m / L;
+  const int t = (int)(m - b * L);
+  const int64_t col = m * nvec + 2 * (ch / 16);
+  float c0 = 0.0f, c1 = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const float2 v = *reinterpret_cast<const float2*>(partial + s * rows * nvec + col);
+    c0 += v.x;
+    c1 += v.y;
+  }
+  const uint4 xv = *reinterpret_cast<const uint4*>(x + m * D + ch);
+  const uint4 pv = t > 0 ? *reinterpret_cast<const uint4*>(x + (m - 1) * D + ch)
+                         : *reinterpret_cast<const uint4*>(xprev + b * D + ch);
+  const uint4 b0 = *reinterpret_cast<const uint4*>(base + ch);
+  const uint4 b1 = *reinterpret_cast<const uint4*>(base + D + ch);
+  *reinterpret_cast<uint4*>(y + m * D + ch) = conv8(xv, pv, b0, b1, c0, c1);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -239,8 +242,33 @@ __global__ __launch_bounds__(kThreads) void conv2_apply_f32_kernel(
 
 int64_t conv2_max_f32_elems() { return (int64_t)1 << 34; }
 
+#ifndef DFS_CONV_TARGET_WG
+#define DFS_CONV_TARGET_WG 512
+#endif
+// K splits of the bf16 correction (enough workgroups for the chip, at least 8 k steps
+// each) and k steps per split; every split gets at least one step.
+struct ConvSplit {
+  int splits, kps;
+};
+ConvSplit conv2_splits(int64_t rows, int64_t D) {
+  const int64_t ks = D / kKStep;
+#ifdef DFS_CONV_SPLITS
+  (void)rows;
+  int64_t s = DFS_CONV_SPLITS;
+#else
+  const int64_t tiles = cdiv(rows, kTileM) * cdiv(D / 8, kTileN);
+  int64_t s = DFS_CONV_TARGET_WG / tiles;
+#endif
+  if (s > ks / 8) s = ks / 8;
+  if (s < 1) s = 1;
+  const int64_t kps = cdiv(ks, s);
+  return ConvSplit{(int)cdiv(ks, kps), (int)kps};
+}
+
 size_t conv2_workspace_bytes(int64_t rows, int64_t D, bool bf16) {
-  return bf16 ? 0 : align_up((size_t)rows * (size_t)(D / 8) * sizeof(float), 256);
+  const int64_t splits = bf16 ? conv2_splits(rows, D).splits : 1;
+  if (bf16 && splits == 1) return 0;
+  return align_up((size_t)splits * (size_t)rows * (size_t)(D / 8) * sizeof(float), 256);
 }
 
 hipError_t launch_conv2(const void* x, const void* x_prev, const void* base, const void* W_c,
@@ -249,11 +277,20 @@ hipError_t launch_conv2(const void* x, const void* x_prev, const void* base, con
   const int64_t rows = batch * L;
   if (bf16) {
     const int ntn = (int)cdiv(D / 8, kTileN);
-    const dim3 grid((unsigned)(cdiv(rows, kTileM) * ntn));
+    const int64_t mtiles = cdiv(rows, kTileM);
+    const ConvSplit sp = conv2_splits(rows, D);
+    const int splits = sp.splits, kps = sp.kps;
+    const dim3 grid((unsigned)((DFS_CONV_XCD ? cdiv(mtiles, 8) * 8 : mtiles) * ntn * splits));
     conv2_bf16_kernel<<<grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x_prev),
         static_cast<const uint16_t*>(base), static_cast<const uint16_t*>(W_c), rows, (int)L, D, ntn,
-        static_cast<uint16_t*>(y));
+        mtiles, splits, kps, static_cast<float*>(ws), static_cast<uint16_t*>(y));
+    if (splits > 1) {
+      conv2_split_epilogue_kernel<<<dim3((unsigned)cdiv(rows * (D / 8), kThreads)), kThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x_prev),
+          static_cast<const uint16_t*>(base), static_cast<const float*>(ws), splits, rows, (int)L, D,
+          static_cast<uint16_t*>(y));
+    }
   } else {
     float* c = static_cast<float*>(ws);
     corr_f32_kernel<<<dim3((unsigned)(D / 8 * cdiv(rows, kF32Rows))), kWave, 0, stream>>>(

@@ -114,3 +114,14 @@ def test_conv2_is_deterministic_and_writes_out():
     torch.cuda.synchronize()
     assert y2.data_ptr() == out.data_ptr()
     assert torch.equal(y1, y2)
+
+
+def test_conv2_fixed_shape_object_matches_function():
+    ci = make_conv(variant("throughput", batch=3, L=16, d=1024), corr_std=0.02)
+    args = (to_dev(ci.x), to_dev(ci.x_prev), to_dev(ci.base), to_dev(ci.W_c))
+    c = dfs_mod().Conv2(3, 16, 1024)
+    y = c(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y, dfs_mod().conv2(*args))
+    with pytest.raises(ValueError):
+        c(args[0][:, :8].contiguous(), *args[1:])
