@@ -28,8 +28,10 @@ Pinning status (what each function is checked against, in tests/):
                  kernels exact; a planted one-weight case fixes taps, groups and
                  predecessors; one group's weights move exactly its 16 channels by
                  a closed form; x_prev reaches position 0 only; scalar fsum loops
+  lmhead         one-hot hidden states select a weight column (closed form); scalar
+                 fsum dot products; top-16 == heapq.nlargest of the brute-force logits
 """
-from . import conv, recall, verify
+from . import conv, lmhead, recall, verify
 from .philox import gumbel, philox4x32_10, uniform_from_word
 from .selector import (
     SequenceResult,
@@ -49,6 +51,7 @@ __all__ = [
     "conv",
     "gate",
     "gumbel",
+    "lmhead",
     "pair_scores",
     "philox4x32_10",
     "recall",
