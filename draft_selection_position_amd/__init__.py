@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "DfsError", "K", "E", "MAX_L", "lib", "lib_path", "topk", "gate", "pair_scores", "walk",
     "select", "Selector", "select_workspace_bytes", "topk_workspace_bytes",
-    "gate_workspace_bytes", "status_str", "conv2", "conv2_workspace_bytes", "Conv2",
+    "gate_workspace_bytes", "status_str", "conv2", "conv2_workspace_bytes", "Conv2", "lmhead_topk", "lmhead_logits",
+    "lmhead_topk_workspace_bytes",
 ]
 
 K = 16
@@ -91,6 +92,12 @@ def lib() -> ctypes.CDLL:
         L.dfs_conv2_workspace_bytes.argtypes, L.dfs_conv2_workspace_bytes.restype = [i64, i64, i64, c_int], sz
         L.dfs_conv2.argtypes = [vp, vp, vp, vp, c_int, i64, i64, i64, vp, vp, sz, vp]
         L.dfs_conv2.restype = c_int
+        L.dfs_lmhead_topk_workspace_bytes.argtypes = [i64, i64, i64]
+        L.dfs_lmhead_topk_workspace_bytes.restype = sz
+        L.dfs_lmhead_topk.argtypes = [vp, vp, c_int, i64, i64, i64, c_int, i32p, f32p, vp, sz, vp]
+        L.dfs_lmhead_topk.restype = c_int
+        L.dfs_lmhead_logits.argtypes = [vp, vp, c_int, i64, i64, i64, f32p, vp]
+        L.dfs_lmhead_logits.restype = c_int
         _lib = L
     return _lib
 
@@ -379,6 +386,45 @@ def conv2(x: torch.Tensor, x_prev: torch.Tensor, base: torch.Tensor, W_c: torch.
     ws = _ws_arg(workspace, x.device, nb)
     _check(lib().dfs_conv2(x.data_ptr(), x_prev.data_ptr(), base.data_ptr(), W_c.data_ptr(), dt, batch, L, D,
                            out.data_ptr(), _ptr(ws), nb, _stream(x.device)), "dfs_conv2")
+    return out
+
+
+def _lmhead_args(hidden, W_lm):
+    _dev(hidden, "hidden", torch.bfloat16)
+    _dev(W_lm, "W_lm", torch.bfloat16)
+    d = hidden.shape[-1]
+    if W_lm.dim() != 2 or W_lm.shape[1] != d:
+        raise ValueError(f"W_lm must be [V, {d}], got {tuple(W_lm.shape)}")
+    return hidden.numel() // d, W_lm.shape[0], d
+
+
+def lmhead_topk_workspace_bytes(rows: int, V: int, d: int) -> int:
+    return int(lib().dfs_lmhead_topk_workspace_bytes(rows, V, d))
+
+
+def lmhead_topk(hidden: torch.Tensor, W_lm: torch.Tensor, workspace: torch.Tensor | None = None):
+    """Top-16 of U = hidden @ W_lm.T per row without writing U (see dfs_lmhead_topk).
+
+    hidden [..., d] and W_lm [V, d], bf16.  Returns (ids int32 [..., 16], values fp32 [..., 16])."""
+    rows, V, d = _lmhead_args(hidden, W_lm)
+    lead = tuple(hidden.shape[:-1])
+    idx = torch.empty(lead + (K,), dtype=torch.int32, device=hidden.device)
+    val = torch.empty(lead + (K,), dtype=torch.float32, device=hidden.device)
+    nb = lmhead_topk_workspace_bytes(rows, V, d)
+    ws = _ws_arg(workspace, hidden.device, nb)
+    _check(lib().dfs_lmhead_topk(hidden.data_ptr(), W_lm.data_ptr(), BF16, rows, V, d, K, idx.data_ptr(),
+                                 val.data_ptr(), _ptr(ws), nb, _stream(hidden.device)), "dfs_lmhead_topk")
+    return idx, val
+
+
+def lmhead_logits(hidden: torch.Tensor, W_lm: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """U = hidden @ W_lm.T in fp32 by the same product as lmhead_topk: [..., V]."""
+    rows, V, d = _lmhead_args(hidden, W_lm)
+    if out is None:
+        out = torch.empty(tuple(hidden.shape[:-1]) + (V,), dtype=torch.float32, device=hidden.device)
+    _dev(out, "out", torch.float32)
+    _check(lib().dfs_lmhead_logits(hidden.data_ptr(), W_lm.data_ptr(), BF16, rows, V, d, out.data_ptr(),
+                                   _stream(hidden.device)), "dfs_lmhead_logits")
     return out
 
 

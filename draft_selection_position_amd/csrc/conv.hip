@@ -28,9 +28,10 @@
 namespace dfs {
 namespace {
 
-constexpr int kThreads = 256;                 // 4 waves
-constexpr int kTileM = tile::kTile;           // rows per workgroup
-constexpr int kTileN = tile::kTile;           // correction columns per workgroup (64 groups)
+using CT = tile::Shape<2, 2, 4, 4>;           // 128 x 128 tiles, 64 x 64 per wave
+constexpr int kThreads = tile::kThreads;      // 4 waves
+constexpr int kTileM = CT::BM;                // rows per workgroup
+constexpr int kTileN = CT::BN;                // correction columns per workgroup (64 groups)
 constexpr int kKStep = tile::kKStep;
 constexpr int kPitchC = kTileN + 4;           // fp32 per LDS row of the correction tile
 #ifndef DFS_CONV_DEPTH
@@ -39,7 +40,7 @@ constexpr int kPitchC = kTileN + 4;           // fp32 per LDS row of the correct
 #ifndef DFS_CONV_XCD
 #define DFS_CONV_XCD 1
 #endif
-static_assert(kTileM * kPitchC * 4 <= tile::kLdsBytes, "the correction tile reuses the operand stages");
+static_assert(kTileM * kPitchC * 4 <= CT::kLdsBytes, "the correction tile reuses the operand stages");
 
 // fp32 -> bf16 bits, round to nearest, ties to even (finite and infinite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_ke
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ Wc, int64_t rows, int L,
     int64_t D, int ntiles_n, int64_t mtiles, int splits, int ks_per_split,
     float* __restrict__ partial, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[tile::kLdsBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[CT::kLdsBytes / 2];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -103,13 +104,10 @@ __global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_ke
   const int ks0 = split * ks_per_split;
   const int ks1 = ks0 + ks_per_split < KS ? ks0 + ks_per_split : KS;
 
-  tile::Acc acc;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc.v[a][b] = tile::f32x4{0.f, 0.f, 0.f, 0.f};
-  tile::mma_128x128<DFS_CONV_DEPTH>(tile::rows_rsrc(x + m0 * D, tile_rows, D),
-                                    tile::rows_rsrc(Wc + n0 * D, ncols, D), D, ks0, ks1, lds, acc);
+  CT::Acc acc;
+  tile::zero<2, 2, 4, 4>(acc);
+  tile::mma<2, 2, 4, 4, DFS_CONV_DEPTH>(tile::rows_rsrc(x + m0 * D, tile_rows, D),
+                                        tile::rows_rsrc(Wc + n0 * D, ncols, D), D, ks0, ks1, lds, acc);
 
   float* sC = reinterpret_cast<float*>(lds);  // [kTileM][kPitchC], after the loop's last barrier
   const int wm = wave >> 1, wn = wave & 1;

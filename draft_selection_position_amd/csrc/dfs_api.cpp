@@ -354,4 +354,46 @@ int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W
   return hip_status(launch_conv2(x, x_prev, base, W_c, dt == DFS_BF16, batch, L, D, y, ws, stream));
 }
 
+static int check_lmhead(const void* hidden, const void* W_lm, dfs_dtype_t dt, int64_t rows, int64_t V,
+                        int64_t d) {
+  if (!hidden || !W_lm) return DFS_E_NULL;
+  if (dt != DFS_BF16) return DFS_E_UNSUPPORTED;
+  if (rows < 1 || rows > ((int64_t)1 << 30) || V < DFS_K || V > kMaxV || d < 64 || d > kMaxD)
+    return DFS_E_SHAPE;
+  if (d % 64 != 0) return DFS_E_UNSUPPORTED;
+  if (!aligned(hidden, 16) || !aligned(W_lm, 16)) return DFS_E_ALIGN;
+  return DFS_OK;
+}
+
+size_t dfs_lmhead_topk_workspace_bytes(int64_t rows, int64_t V, int64_t d) {
+  if (rows < 1 || rows > ((int64_t)1 << 30) || V < DFS_K || V > kMaxV || d < 64 || d > kMaxD || d % 64)
+    return 0;
+  return lmhead_workspace_bytes(rows, V, d);
+}
+
+int dfs_lmhead_topk(const void* hidden, const void* W_lm, dfs_dtype_t dt, int64_t rows, int64_t V,
+                    int64_t d, int k, int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_lmhead(hidden, W_lm, dt, rows, V, d);
+  if (st != DFS_OK) return st;
+  if (!out_idx || !out_val || !ws) return DFS_E_NULL;
+  if (k != DFS_K) return DFS_E_UNSUPPORTED;
+  if (!aligned(out_idx, 4) || !aligned(out_val, 4) || !aligned(ws, 256)) return DFS_E_ALIGN;
+  if (ws_bytes < lmhead_workspace_bytes(rows, V, d)) return DFS_E_WORKSPACE;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_lmhead_topk(hidden, W_lm, rows, V, d, out_idx, out_val, ws, stream));
+}
+
+int dfs_lmhead_logits(const void* hidden, const void* W_lm, dfs_dtype_t dt, int64_t rows, int64_t V,
+                      int64_t d, float* out_logits, hipStream_t stream) {
+  int st = check_lmhead(hidden, W_lm, dt, rows, V, d);
+  if (st != DFS_OK) return st;
+  if (!out_logits) return DFS_E_NULL;
+  if (!aligned(out_logits, 4)) return DFS_E_ALIGN;
+  if ((st = check_device()) != DFS_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(launch_lmhead_logits(hidden, W_lm, rows, V, d, out_logits, stream));
+}
+
 }  // extern "C"

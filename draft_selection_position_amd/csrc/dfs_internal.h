@@ -35,6 +35,10 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
                        float* out_val, void* ws, hipStream_t stream,
                        const PackJob* pack = nullptr);
 
+// Merge of per-row partial top-16 lists [rows, parts, 16] (64-bit keys, 0 = empty).
+hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, int32_t* out_idx,
+                             float* out_val, hipStream_t stream);
+
 // ---------------------------------------------------------------- gate
 struct GatePlan {
   int64_t rows, d;
@@ -110,5 +114,13 @@ int64_t conv2_max_f32_elems();
 hipError_t launch_conv2(const void* x, const void* x_prev, const void* base, const void* W_c,
                         bool bf16, int64_t batch, int64_t L, int64_t D, void* y, void* ws,
                         hipStream_t stream);
+
+// ---------------------------------------------------------------- LM head -> top-16
+// bf16 hidden [rows, d] and W_lm [V, d], d a multiple of 64.
+size_t lmhead_workspace_bytes(int64_t rows, int64_t V, int64_t d);
+hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows, int64_t V, int64_t d,
+                              int32_t* out_idx, float* out_val, void* ws, hipStream_t stream);
+hipError_t launch_lmhead_logits(const void* hidden, const void* W_lm, int64_t rows, int64_t V, int64_t d,
+                                float* out, hipStream_t stream);
 
 }  // namespace dfs

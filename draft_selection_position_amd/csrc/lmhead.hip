@@ -1,0 +1,240 @@
+// Top-16 candidates straight from the drafter's hidden state, through its LM head.
+//
+// The selector reads the drafter's vocabulary logits U_t and makes no extra LM-head
+// pass (blog post "DFlash 2: Keep Drafting Parallel", section "A Lightweight Path
+// Selector"); the logits are the drafter's LM head applied to its hidden state.
+// Here the head's product U = h W_lm^T (h [rows, d], W_lm [V, d], bf16, fp32 sums on
+// the matrix cores) and the top-16 selection (section "The Right Tokens Are Already
+// There") run in one kernel: each workgroup walks a stripe of 128- (or 256-) column
+// tiles of U and folds every tile into running per-row top-16 lists, so U never
+// reaches HBM.  Keys and order are those of the top-16 pass (value descending, then
+// the lower token id), on the fp32 sums.  A merge pass then combines the stripes'
+// lists per row.  The same product can be written out (lmhead_logits_kernel): the
+// fused result equals the top-16 pass run on those logits, bit for bit.
+//
+// Tiles: 128 x 128 (four waves of 64 x 64) for many rows; 16 x 256 (four waves of
+// 16 x 64) for a few rows, where the pass streams W_lm once and the matrix cores
+// idle.  Workgroups are numbered so that each XCD runs 8 row tiles x 8 stripes at
+// a time (64 workgroups, two per CU): the 8 stripes' W_lm tiles and the 8 row
+// tiles' h are then shared through the XCD's L2 while their k loops advance
+// together.
+#include "dfs_device.h"
+#include "dfs_internal.h"
+#include "mfma_tile.h"
+
+namespace dfs {
+namespace {
+
+constexpr int kThreads = tile::kThreads;
+constexpr int kGroup = 64;  // workgroups an XCD runs at a time (two per CU)
+#ifndef DFS_LM_DEPTH
+#define DFS_LM_DEPTH 2
+#endif
+
+struct Grid {
+  int64_t rows, V, d;
+  int mtiles;
+  int64_t ntiles;
+  int nstripes, tps;   // stripes of tps column tiles
+  int gm, gs;          // row tiles x stripes per group (gm * gs = kGroup)
+  int mgroups, groups; // groups along the rows, all groups
+};
+
+// Workgroup -> (row tile, stripe); false for the padding of the last round.
+__device__ __forceinline__ bool place(const Grid& g, int& mt, int& stripe) {
+  const unsigned xcd = blockIdx.x % 8u, j = blockIdx.x / 8u;
+  const int gi = (int)(j / kGroup) * 8 + (int)xcd;
+  const int local = (int)(j % kGroup);
+  if (gi >= g.groups) return false;
+  mt = (gi % g.mgroups) * g.gm + local % g.gm;
+  stripe = (gi / g.mgroups) * g.gs + local / g.gm;
+  return mt < g.mtiles && stripe < g.nstripes;
+}
+
+template <int WMW, int WNW, int TM, int TN>
+__global__ __launch_bounds__(kThreads, 2) void lmhead_topk_kernel(const uint16_t* __restrict__ h,
+                                                                  const uint16_t* __restrict__ W, Grid g,
+                                                                  uint64_t* __restrict__ partial) {
+  using S = tile::Shape<WMW, WNW, TM, TN>;
+  constexpr int BM = S::BM, BN = S::BN, CAP = BN / WNW;
+  static_assert(BM * CAP * 8 <= S::kLdsBytes, "candidates reuse the operand stages");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::kLdsBytes / 2];
+  __shared__ uint64_t s_thr[BM];
+  __shared__ int s_cnt[BM];
+  __shared__ int s_has[BM];
+  int mt, stripe;
+  if (!place(g, mt, stripe)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int tile_rows = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
+  for (int i = tid; i < BM; i += kThreads) {
+    s_thr[i] = 0;
+    s_cnt[i] = 0;
+    s_has[i] = 0;
+  }
+  const int64_t row_stride = (int64_t)g.nstripes * kK;
+  uint64_t* plist = partial + (int64_t)stripe * kK;  // row m's list at plist[m * row_stride]
+  uint64_t* cand = reinterpret_cast<uint64_t*>(lds);  // [BM][CAP], after each product
+  const __amdgpu_buffer_rsrc_t ra = tile::rows_rsrc(h + m0 * g.d, tile_rows, g.d);
+  const int KS = (int)(g.d / tile::kKStep);
+  const int64_t t0 = (int64_t)stripe * g.tps;
+  const int64_t t1 = t0 + g.tps < g.ntiles ? t0 + g.tps : g.ntiles;
+  for (int64_t nt_ = t0; nt_ < t1; ++nt_) {
+    const int64_t n0 = nt_ * BN;
+    const int64_t ncols = g.V - n0 < BN ? g.V - n0 : BN;
+    typename S::Acc acc;
+    tile::zero<WMW, WNW, TM, TN>(acc);
+    tile::mma<WMW, WNW, TM, TN, DFS_LM_DEPTH>(ra, tile::rows_rsrc(W + n0 * g.d, ncols, g.d), g.d, 0, KS,
+                                              lds, acc);
+    // Fold the tile into the row lists, one wave column at a time (CAP columns).
+    for (int ph = 0; ph < WNW; ++ph) {
+      if (wn == ph) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
+            if (lr >= tile_rows) continue;
+            const uint64_t thr = s_thr[lr];
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+              const int lc = 16 * TN * wn + 16 * b + r;
+              if (lc >= ncols) continue;
+              const uint64_t key = make_key(acc.v[a][b][i], (uint32_t)(n0 + lc));
+              if (key > thr) cand[lr * CAP + atomicAdd(&s_cnt[lr], 1)] = key;
+            }
+          }
+      }
+      __syncthreads();
+      for (int lr = wave; lr < tile_rows; lr += 4) {  // row lr always merges on wave lr % 4
+        const int cnt = s_cnt[lr];
+        if (cnt == 0) continue;
+        uint64_t* gl = plist + (m0 + lr) * row_stride;
+        uint64_t cur = 0;
+        if (lane < kK && s_has[lr]) cur = gl[lane];  // this lane wrote it at an earlier merge
+        for (int c0 = 0; c0 < cnt; c0 += kWave - kK) {
+          const int ci = c0 + lane - kK;
+          uint64_t x = lane < kK ? cur : (ci < cnt ? cand[lr * CAP + ci] : 0);
+          x = wave_sort_desc(x, lane);
+          cur = lane < kK ? x : 0;
+        }
+        if (lane < kK) gl[lane] = cur;
+        const uint64_t thr = lane_u64(cur, kK - 1);
+        if (lane == 0) {
+          s_thr[lr] = thr;
+          s_cnt[lr] = 0;
+          s_has[lr] = 1;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// U [rows, V] fp32 written out: the same product, for checks and the unfused chain.
+template <int WMW, int WNW, int TM, int TN>
+__global__ __launch_bounds__(kThreads, 2) void lmhead_logits_kernel(const uint16_t* __restrict__ h,
+                                                                    const uint16_t* __restrict__ W,
+                                                                    int64_t rows, int64_t V, int64_t d,
+                                                                    int64_t ntiles, float* __restrict__ U) {
+  using S = tile::Shape<WMW, WNW, TM, TN>;
+  constexpr int BM = S::BM, BN = S::BN;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::kLdsBytes / 2];
+  const int64_t nt_ = (int64_t)blockIdx.x % ntiles;
+  const int64_t m0 = (int64_t)blockIdx.x / ntiles * BM;
+  const int64_t n0 = nt_ * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int tile_rows = (int)(rows - m0 < BM ? rows - m0 : BM);
+  const int64_t ncols = V - n0 < BN ? V - n0 : BN;
+  typename S::Acc acc;
+  tile::zero<WMW, WNW, TM, TN>(acc);
+  tile::mma<WMW, WNW, TM, TN, DFS_LM_DEPTH>(tile::rows_rsrc(h + m0 * d, tile_rows, d),
+                                            tile::rows_rsrc(W + n0 * d, ncols, d), d, 0,
+                                            (int)(d / tile::kKStep), lds, acc);
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
+      if (lr >= tile_rows) continue;
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int lc = 16 * TN * wn + 16 * b + r;
+        if (lc < ncols) U[(m0 + lr) * V + n0 + lc] = acc.v[a][b][i];
+      }
+    }
+}
+
+// Tile shapes: few rows -> 16 x 256 (W_lm streamed once); otherwise 128 x 128.
+constexpr int64_t kSmallRows = 32;
+
+Grid make_grid(int64_t rows, int64_t V, int64_t d) {
+  Grid g{};
+  g.rows = rows;
+  g.V = V;
+  g.d = d;
+  const bool small = rows <= kSmallRows;
+  const int BM = small ? 16 : 128, BN = small ? 256 : 128;
+  g.mtiles = (int)cdiv(rows, BM);
+  g.ntiles = cdiv(V, BN);
+  // about 2048 workgroups, at least two column tiles per stripe where there are enough
+  int64_t ns = cdiv(2048, g.mtiles);
+  if (ns > g.ntiles / 2) ns = g.ntiles / 2;
+  if (ns > 1024) ns = 1024;
+  if (ns < 1) ns = 1;
+  g.tps = (int)cdiv(g.ntiles, ns);
+  g.nstripes = (int)cdiv(g.ntiles, g.tps);
+  g.gm = g.mtiles < 8 ? g.mtiles : 8;
+  while (kGroup % g.gm) --g.gm;
+  g.gs = kGroup / g.gm;
+  g.mgroups = (int)cdiv(g.mtiles, g.gm);
+  g.groups = g.mgroups * (int)cdiv(g.nstripes, g.gs);
+  return g;
+}
+
+}  // namespace
+
+size_t lmhead_workspace_bytes(int64_t rows, int64_t V, int64_t d) {
+  const Grid g = make_grid(rows, V, d);
+  return align_up((size_t)rows * g.nstripes * kK * sizeof(uint64_t), 256);
+}
+
+hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows, int64_t V, int64_t d,
+                              int32_t* out_idx, float* out_val, void* ws, hipStream_t stream) {
+  const Grid g = make_grid(rows, V, d);
+  uint64_t* partial = static_cast<uint64_t*>(ws);
+  const dim3 grid((unsigned)(8 * kGroup * cdiv(g.groups, 8)));
+  const uint16_t* hp = static_cast<const uint16_t*>(hidden);
+  const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
+  if (rows <= kSmallRows)
+    lmhead_topk_kernel<1, 4, 1, 4><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+  else
+    lmhead_topk_kernel<2, 2, 4, 4><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_merge(partial, rows, g.nstripes, out_idx, out_val, stream);
+}
+
+hipError_t launch_lmhead_logits(const void* hidden, const void* W_lm, int64_t rows, int64_t V, int64_t d,
+                                float* out, hipStream_t stream) {
+  const uint16_t* hp = static_cast<const uint16_t*>(hidden);
+  const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
+  if (rows <= kSmallRows) {
+    const int64_t nt = cdiv(V, 256);
+    lmhead_logits_kernel<1, 4, 1, 4><<<dim3((unsigned)(cdiv(rows, 16) * nt)), kThreads, 0, stream>>>(
+        hp, wp, rows, V, d, nt, out);
+  } else {
+    const int64_t nt = cdiv(V, 128);
+    lmhead_logits_kernel<2, 2, 4, 4><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
+        hp, wp, rows, V, d, nt, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfs

@@ -378,4 +378,10 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
   return hipGetLastError();
 }
 
+hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, int32_t* out_idx,
+                             float* out_val, hipStream_t stream) {
+  topk_merge_kernel<<<dim3((unsigned)rows), kThreads, 0, stream>>>(partial, parts, out_idx, out_val);
+  return hipGetLastError();
+}
+
 }  // namespace dfs

@@ -223,11 +223,34 @@ int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W
               int64_t batch, int64_t L, int64_t D, void* y, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* ---------------------------------------------------------------- LM head -> top-16
+ * The candidates straight from the drafter's hidden state: the selector reads the
+ * drafter's logits and needs no extra LM-head pass (blog post "DFlash 2: Keep
+ * Drafting Parallel", section "A Lightweight Path Selector"); the logits are
+ * U = h W_lm^T, and the 16 largest per row are the candidates (section "The Right
+ * Tokens Are Already There").  dfs_lmhead_topk computes the product on the matrix
+ * cores (fp32 sums) and keeps only the running top-16 per row: U is never written.
+ *   hidden [rows, d] bf16 (row-major), W_lm [V, d] bf16 (one row per token)
+ *   out_idx [rows, 16] int32, out_val [rows, 16] fp32: value descending, then the
+ *     lower id, on the fp32 sums -- exactly dfs_topk run on dfs_lmhead_logits' U.
+ * dt must be DFS_BF16; d a multiple of 64 in [64, DFS_MAX_D]; 16 <= V < 2^31;
+ * 1 <= rows <= 2^30.  hidden and W_lm 16-byte aligned, outputs 4, ws 256.
+ * ws: dfs_lmhead_topk_workspace_bytes(rows, V, d) bytes (never 0): per-row lists of
+ * the column stripes, merged at the end.  Finite inputs whose sums stay finite. */
+size_t dfs_lmhead_topk_workspace_bytes(int64_t rows, int64_t V, int64_t d);
+int dfs_lmhead_topk(const void* hidden, const void* W_lm, dfs_dtype_t dt, int64_t rows, int64_t V,
+                    int64_t d, int k, int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+/* The same product written out: out_logits [rows, V] fp32 (the unfused chain's first
+ * step, and the reference the fused result is checked against). */
+int dfs_lmhead_logits(const void* hidden, const void* W_lm, dfs_dtype_t dt, int64_t rows, int64_t V,
+                      int64_t d, float* out_logits, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* dfs_status_str(int status);
 
 /* ABI version of this header and library (major * 100 + minor). */
-#define DFS_ABI_VERSION 102
+#define DFS_ABI_VERSION 103
 int dfs_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.dfs_abi_version() == 102
+    assert L.dfs_abi_version() == 103
     for code in range(9):
         s = dfs.status_str(code)
         assert s.startswith("DFS_")
@@ -199,3 +199,24 @@ def test_conv2_validation(L):
     assert _conv(L, dt=0, ws=None, wsb=0) == E_WS
     assert _conv(L, dt=0, ws=P + 0x3000000 + 1, wsb=nb) == E_ALIGN
     assert L.dfs_conv2_workspace_bytes(2, 4, 500, 0) == 0
+
+
+def test_lmhead_validation(L):
+    f = lambda **kw: L.dfs_lmhead_topk(kw.get("h", P), kw.get("W", P + 0x100000), kw.get("dt", 1),  # noqa: E731
+                                       kw.get("rows", 16), kw.get("V", 1000), kw.get("d", 512), kw.get("k", 16),
+                                       kw.get("idx", P), kw.get("val", P), kw.get("ws", P), kw.get("wsb", 1 << 30),
+                                       None)
+    assert f(h=None) == E_NULL
+    assert f(ws=None) == E_NULL
+    assert f(dt=0) == E_UNSUP
+    assert f(d=100) == E_SHAPE or f(d=100) == E_UNSUP
+    assert f(d=96) == E_UNSUP
+    assert f(V=15) == E_SHAPE
+    assert f(rows=0) == E_SHAPE
+    assert f(k=8) == E_UNSUP
+    assert f(h=P + 4) == E_ALIGN
+    assert f(wsb=16) == E_WS
+    nb = L.dfs_lmhead_topk_workspace_bytes(16, 151936, 5120)
+    assert 0 < nb < 1 << 24
+    assert L.dfs_lmhead_topk_workspace_bytes(16, 151936, 5100) == 0
+    assert L.dfs_lmhead_logits(P, P, 0, 16, 1000, 512, P, None) == E_UNSUP

@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from .configs import Config, config_by_name
-from .gen import _rng, _store, _workers
+from .gen import _rng, _sequence_hidden, _store, _workers
 
 TAG_WLM = 30
 BLOCK_ROWS = 4096
@@ -46,4 +46,20 @@ def make_lm_head(cfg: Config | str, std: float = 0.02, V: int | None = None,
     else:
         for i in range(nb):
             block(i)
+    return out
+
+
+def make_hidden(cfg: Config | str, seqs=None) -> np.ndarray:
+    """The workload's hidden states h [nseq, L, d] alone (identical to ``gen.make``'s)."""
+    if isinstance(cfg, str):
+        cfg = config_by_name(cfg)
+    seqs = range(cfg.batch) if seqs is None else [int(b) for b in seqs]
+    seqs = list(seqs)
+    out = np.empty((len(seqs), cfg.L, cfg.d), np.uint16 if cfg.dtype == "bf16" else np.float32)
+
+    def one(i: int) -> None:
+        out[i] = _sequence_hidden(cfg, seqs[i])
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(seqs))))
     return out
