@@ -202,6 +202,9 @@ def main() -> int:
                     help="print the top-16 traffic record from FETCH_SIZE / WRITE_SIZE counter runs and exit")
     ap.add_argument("--conv", action="store_true",
                     help="also time dfs_conv2 (two-tap dynamic convolution) on x [batch, L, d] of the workload")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="also time dfs_lmhead_topk (top-16 straight from the hidden states through a "
+                         "synthetic [V, d] LM head) against the unfused dfs_lmhead_logits + dfs_topk")
     ap.add_argument("--verify", action="store_true",
                     help="also time dfs_select_draft + dfs_verify against synthetic target logits "
                          "[batch, L + 1, V] (the drafter's logits plus noise, one more random row)")
@@ -407,6 +410,39 @@ def main() -> int:
                     "mfma_frac": cflops / (conv_ms * 1e-3) / 1e12 / (2500.0 if es == 2 else 157.3)}
         del cx, conv
 
+    lm_out = None
+    if args.lmhead and cfg.dtype != "bf16":
+        lm_out = {"skipped": "the fused LM head takes bf16 hidden states and weights"}
+    elif args.lmhead:
+        # The drafter's LM head on the workload's own hidden states: W_lm [V, d] ~ N(0, 0.02).
+        from workloads.lmhead import make_lm_head
+
+        from tests.parity import to_dev as _to_dev
+
+        W_lm = _to_dev(make_lm_head(cfg))
+        rows = cfg.batch * cfg.L
+        lws = torch.empty(dfs.lmhead_topk_workspace_bytes(rows, cfg.V, cfg.d), dtype=torch.uint8,
+                          device=W_lm.device)
+        n_lm = max(5, min(args.steps, 50)) if rows <= 512 else 5
+        fused_ms = timed(lambda: dfs.lmhead_topk(hidden2d, W_lm, workspace=lws), n=n_lm)
+        i1, v1 = dfs.lmhead_topk(hidden2d, W_lm, workspace=lws)
+        U = torch.empty((rows, cfg.V), dtype=torch.float32, device=W_lm.device)
+        logits_ms = timed(lambda: dfs.lmhead_logits(hidden2d, W_lm, out=U), n=n_lm)
+        uws = torch.empty(max(1, dfs.topk_workspace_bytes(rows, cfg.V, torch.float32)), dtype=torch.uint8,
+                          device=W_lm.device)
+        topk32_ms = timed(lambda: dfs.topk(U, workspace=uws), n=n_lm)
+        i2, v2 = dfs.topk(U, workspace=uws)
+        flops = 2 * rows * cfg.V * cfg.d
+        wbytes = cfg.V * cfg.d * 2 + rows * cfg.d * 2
+        lm_out = {"fused_ms": fused_ms, "logits_ms": logits_ms, "topk_fp32_ms": topk32_ms,
+                  "chain_ms": logits_ms + topk32_ms, "flops": flops, "weight_bytes": wbytes,
+                  "fused_TFLOPs": flops / (fused_ms * 1e-3) / 1e12,
+                  "fused_mfma_frac": flops / (fused_ms * 1e-3) / 1e12 / 2500.0,
+                  "fused_GBps": wbytes / (fused_ms * 1e-3) / 1e9,
+                  "fused_hbm_frac": wbytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "fused_equals_chain": bool(torch.equal(i1, i2) and torch.equal(v1, v2))}
+        del W_lm, U
+
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device=logits2d.device).fill_(1)
@@ -444,6 +480,8 @@ def main() -> int:
         out["verify"] = verify_out
     if conv_out is not None:
         out["conv"] = conv_out
+    if lm_out is not None:
+        out["lmhead"] = lm_out
     if graph_ms is not None:
         out["graph_replay"] = {"ms_per_step": graph_ms, "value": cfg.batch / (graph_ms * 1e-3),
                                "input_sets": 1}

@@ -18,15 +18,23 @@
 // a time (64 workgroups, two per CU): the 8 stripes' W_lm tiles and the 8 row
 // tiles' h are then shared through the XCD's L2 while their k loops advance
 // together.
+#include <type_traits>
+
 #include "dfs_device.h"
 #include "dfs_internal.h"
+#include "mfma_big.h"
 #include "mfma_tile.h"
 
 namespace dfs {
 namespace {
 
 constexpr int kThreads = tile::kThreads;
-constexpr int kGroup = 64;  // workgroups an XCD runs at a time (two per CU)
+#ifndef DFS_LM_BIG_ROWS
+#define DFS_LM_BIG_ROWS 256
+#endif
+#ifndef DFS_LM_BIG_TILE
+#define DFS_LM_BIG_TILE 0
+#endif
 #ifndef DFS_LM_DEPTH
 #define DFS_LM_DEPTH 2
 #endif
@@ -36,19 +44,95 @@ struct Grid {
   int mtiles;
   int64_t ntiles;
   int nstripes, tps;   // stripes of tps column tiles
-  int gm, gs;          // row tiles x stripes per group (gm * gs = kGroup)
+  int group;           // workgroups an XCD runs at a time
+  int gm, gs;          // row tiles x stripes per group (gm * gs = group)
   int mgroups, groups; // groups along the rows, all groups
 };
 
 // Workgroup -> (row tile, stripe); false for the padding of the last round.
 __device__ __forceinline__ bool place(const Grid& g, int& mt, int& stripe) {
   const unsigned xcd = blockIdx.x % 8u, j = blockIdx.x / 8u;
-  const int gi = (int)(j / kGroup) * 8 + (int)xcd;
-  const int local = (int)(j % kGroup);
+  const int gi = (int)(j / (unsigned)g.group) * 8 + (int)xcd;
+  const int local = (int)(j % (unsigned)g.group);
   if (gi >= g.groups) return false;
   mt = (gi % g.mgroups) * g.gm + local % g.gm;
   stripe = (gi / g.mgroups) * g.gs + local / g.gm;
   return mt < g.mtiles && stripe < g.nstripes;
+}
+
+// Fold one product tile into the running row lists.  The wave holding rows
+// 16 TM wm + ... and columns 16 TN wn + ... of the tile offers every value whose key
+// beats its row's current 16th (s_thr); the offers of a phase (CAP columns of one
+// wave column) are appended to the row's candidates in LDS, then each row with
+// offers is merged into its list (kept in `partial`) by a 64-lane sort, always on
+// wave row % 4 and lanes 0-15 so that each list slot is read back by the lane that
+// wrote it.  cand_row(lr) gives row lr's candidate array (CAP keys).
+template <int TM, int TN, int WNW, class CandRow>
+__device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int tile_rows, int64_t n0,
+                                          int64_t ncols, uint64_t* s_thr, int* s_cnt, int* s_has,
+                                          CandRow cand_row, uint64_t* plist, int64_t m0,
+                                          int64_t row_stride) {
+  constexpr int BPH = TN < 4 ? TN : 4;  // column tiles of a wave folded per phase
+  constexpr int NPH = WNW * (TN / BPH);
+  static_assert(TN / BPH <= 2 && TN % BPH == 0, "one or two phases per wave column");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int wm = wave / WNW, wn = wave % WNW;
+  // The offers of column tiles b0 .. b0 + BPH - 1 (b0 a compile-time constant, so the
+  // accumulators are indexed statically).
+  auto offer = [&](auto b0c) {
+    constexpr int b0 = decltype(b0c)::value;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
+        if (lr >= tile_rows) continue;
+        const uint64_t thr = s_thr[lr];
+#pragma unroll
+        for (int bb = 0; bb < BPH; ++bb) {
+          const int lc = 16 * TN * wn + 16 * (b0 + bb) + r;
+          if (lc >= ncols) continue;
+          const uint64_t key = make_key(v[a][b0 + bb][i], (uint32_t)(n0 + lc));
+          if (key > thr) cand_row(lr)[atomicAdd(&s_cnt[lr], 1)] = key;
+        }
+        // one row's offers at a time: keeps the scheduler from hoisting every key
+        // of the tile into registers at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  for (int ph = 0; ph < NPH; ++ph) {
+    if (wn == ph / (TN / BPH)) {
+      if (TN / BPH == 1 || ph % (TN / BPH) == 0)
+        offer(std::integral_constant<int, 0>{});
+      else
+        offer(std::integral_constant<int, (TN / BPH > 1 ? BPH : 0)>{});
+    }
+    __syncthreads();
+    for (int lr = wave; lr < tile_rows; lr += 4) {
+      const int cnt = s_cnt[lr];
+      if (cnt == 0) continue;
+      uint64_t* gl = plist + (m0 + lr) * row_stride;
+      const uint64_t* cr = cand_row(lr);
+      uint64_t cur = 0;
+      if (lane < kK && s_has[lr]) cur = gl[lane];
+      for (int c0 = 0; c0 < cnt; c0 += kWave - kK) {
+        const int ci = c0 + lane - kK;
+        uint64_t x = lane < kK ? cur : (ci < cnt ? cr[ci] : 0);
+        x = wave_sort_desc(x, lane);
+        cur = lane < kK ? x : 0;
+      }
+      if (lane < kK) gl[lane] = cur;
+      const uint64_t thr = lane_u64(cur, kK - 1);
+      if (lane == 0) {
+        s_thr[lr] = thr;
+        s_cnt[lr] = 0;
+        s_has[lr] = 1;
+      }
+    }
+    __syncthreads();
+  }
 }
 
 template <int WMW, int WNW, int TM, int TN>
@@ -56,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_topk_kernel(const uint16_t
                                                                   const uint16_t* __restrict__ W, Grid g,
                                                                   uint64_t* __restrict__ partial) {
   using S = tile::Shape<WMW, WNW, TM, TN>;
-  constexpr int BM = S::BM, BN = S::BN, CAP = BN / WNW;
+  constexpr int BM = S::BM, BN = S::BN, CAP = 16 * (TN < 4 ? TN : 4);
   static_assert(BM * CAP * 8 <= S::kLdsBytes, "candidates reuse the operand stages");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::kLdsBytes / 2];
   __shared__ uint64_t s_thr[BM];
@@ -65,9 +149,6 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_topk_kernel(const uint16_t
   int mt, stripe;
   if (!place(g, mt, stripe)) return;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, q = lane >> 4;
-  const int wm = wave / WNW, wn = wave % WNW;
   const int64_t m0 = (int64_t)mt * BM;
   const int tile_rows = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
   for (int i = tid; i < BM; i += kThreads) {
@@ -89,54 +170,57 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_topk_kernel(const uint16_t
     tile::zero<WMW, WNW, TM, TN>(acc);
     tile::mma<WMW, WNW, TM, TN, DFS_LM_DEPTH>(ra, tile::rows_rsrc(W + n0 * g.d, ncols, g.d), g.d, 0, KS,
                                               lds, acc);
-    // Fold the tile into the row lists, one wave column at a time (CAP columns).
-    for (int ph = 0; ph < WNW; ++ph) {
-      if (wn == ph) {
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
-            if (lr >= tile_rows) continue;
-            const uint64_t thr = s_thr[lr];
-#pragma unroll
-            for (int b = 0; b < TN; ++b) {
-              const int lc = 16 * TN * wn + 16 * b + r;
-              if (lc >= ncols) continue;
-              const uint64_t key = make_key(acc.v[a][b][i], (uint32_t)(n0 + lc));
-              if (key > thr) cand[lr * CAP + atomicAdd(&s_cnt[lr], 1)] = key;
-            }
-          }
-      }
-      __syncthreads();
-      for (int lr = wave; lr < tile_rows; lr += 4) {  // row lr always merges on wave lr % 4
-        const int cnt = s_cnt[lr];
-        if (cnt == 0) continue;
-        uint64_t* gl = plist + (m0 + lr) * row_stride;
-        uint64_t cur = 0;
-        if (lane < kK && s_has[lr]) cur = gl[lane];  // this lane wrote it at an earlier merge
-        for (int c0 = 0; c0 < cnt; c0 += kWave - kK) {
-          const int ci = c0 + lane - kK;
-          uint64_t x = lane < kK ? cur : (ci < cnt ? cand[lr * CAP + ci] : 0);
-          x = wave_sort_desc(x, lane);
-          cur = lane < kK ? x : 0;
-        }
-        if (lane < kK) gl[lane] = cur;
-        const uint64_t thr = lane_u64(cur, kK - 1);
-        if (lane == 0) {
-          s_thr[lr] = thr;
-          s_cnt[lr] = 0;
-          s_has[lr] = 1;
-        }
-      }
-      __syncthreads();
-    }
+    fold_tile<TM, TN, WNW>(acc.v, tile_rows, n0, ncols, s_thr, s_cnt, s_has,
+                           [&](int lr) { return cand + lr * CAP; }, plist, m0, row_stride);
+  }
+}
+
+// The same on the LDS-DMA tiles of mfma_big.h (TM = TN = 4: 128 x 128, two
+// workgroups per CU; 8: 256 x 256, one).
+template <int TM, int TN, int kMinWG>
+__global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const uint16_t* __restrict__ h,
+                                                                           const uint16_t* __restrict__ W,
+                                                                           Grid g,
+                                                                           uint64_t* __restrict__ partial) {
+  using C = big::Cfg<TM, TN>;
+  constexpr int BM = C::BM, BN = C::BN, CAP = 16 * (TN < 4 ? TN : 4);
+  __shared__ __attribute__((aligned(1024))) char lds[C::kLdsBytes];
+  __shared__ uint64_t s_thr[BM];
+  __shared__ int s_cnt[BM];
+  __shared__ int s_has[BM];
+  static_assert(BM * CAP * 8 <= C::kLdsBytes, "candidates reuse the operand stages");
+  int mt, stripe;
+  if (!place(g, mt, stripe)) return;
+  const int tid = threadIdx.x;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int tile_rows = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
+  for (int i = tid; i < BM; i += kThreads) {
+    s_thr[i] = 0;
+    s_cnt[i] = 0;
+    s_has[i] = 0;
+  }
+  const int64_t row_stride = (int64_t)g.nstripes * kK;
+  uint64_t* plist = partial + (int64_t)stripe * kK;
+  const big::rsrc_t ra = big::rows_rsrc(h + m0 * g.d, tile_rows, g.d);
+  const int KS = (int)(g.d / big::kK);
+  const int64_t t0 = (int64_t)stripe * g.tps;
+  const int64_t t1 = t0 + g.tps < g.ntiles ? t0 + g.tps : g.ntiles;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(lds);  // [BM][CAP], after each product
+  auto cand_row = [&](int lr) { return cand + lr * CAP; };
+  for (int64_t nt_ = t0; nt_ < t1; ++nt_) {
+    const int64_t n0 = nt_ * BN;
+    const int64_t ncols = g.V - n0 < BN ? g.V - n0 : BN;
+    typename C::Acc acc;
+    C::zero(acc);
+    big::mma<C>(ra, big::rows_rsrc(W + n0 * g.d, ncols, g.d), g.d, 0, KS, lds, acc);
+    fold_tile<TM, TN, 2>(acc.v, tile_rows, n0, ncols, s_thr, s_cnt, s_has, cand_row, plist, m0,
+                         row_stride);
   }
 }
 
 // U [rows, V] fp32 written out: the same product, for checks and the unfused chain.
 template <int WMW, int WNW, int TM, int TN>
-__global__ __launch_bounds__(kThreads, 2) void lmhead_logits_kernel(const uint16_t* __restrict__ h,
+__global__ __launch_bounds__(kThreads, (TM * TN > 16 ? 1 : 2)) void lmhead_logits_kernel(const uint16_t* __restrict__ h,
                                                                     const uint16_t* __restrict__ W,
                                                                     int64_t rows, int64_t V, int64_t d,
                                                                     int64_t ntiles, float* __restrict__ U) {
@@ -171,28 +255,73 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_logits_kernel(const uint16
     }
 }
 
-// Tile shapes: few rows -> 16 x 256 (W_lm streamed once); otherwise 128 x 128.
+template <int TM, int TN, int kMinWG>
+__global__ __launch_bounds__(kThreads, kMinWG) void lmhead_logits_dma_kernel(const uint16_t* __restrict__ h,
+                                                                             const uint16_t* __restrict__ W,
+                                                                             int64_t rows, int64_t V, int64_t d,
+                                                                             int64_t ntiles, float* __restrict__ U) {
+  using C = big::Cfg<TM, TN>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::kLdsBytes];
+  const int64_t nt_ = (int64_t)blockIdx.x % ntiles;
+  const int64_t m0 = (int64_t)blockIdx.x / ntiles * C::BM;
+  const int64_t n0 = nt_ * C::BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tile_rows = (int)(rows - m0 < C::BM ? rows - m0 : C::BM);
+  const int64_t ncols = V - n0 < C::BN ? V - n0 : C::BN;
+  typename C::Acc acc;
+  C::zero(acc);
+  big::mma<C>(big::rows_rsrc(h + m0 * d, tile_rows, d), big::rows_rsrc(W + n0 * d, ncols, d), d, 0,
+              (int)(d / big::kK), lds, acc);
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
+      if (lr >= tile_rows) continue;
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int lc = 16 * TN * wn + 16 * b + r;
+        if (lc < ncols) U[(m0 + lr) * V + n0 + lc] = acc.v[a][b][i];
+      }
+    }
+}
+
+// Tile shapes: few rows -> 16 x 256 (W_lm streamed once); up to DFS_LM_BIG_ROWS ->
+// 128 x 128; more -> 256 x 256 (one workgroup per CU).
 constexpr int64_t kSmallRows = 32;
+enum TileKind { kSmallTile = 0, kMidTile = 1, kBigTile = 2 };
+TileKind tile_kind(int64_t rows) {
+  return rows <= kSmallRows ? kSmallTile : rows < DFS_LM_BIG_ROWS ? kMidTile : kBigTile;
+}
 
 Grid make_grid(int64_t rows, int64_t V, int64_t d) {
   Grid g{};
   g.rows = rows;
   g.V = V;
   g.d = d;
-  const bool small = rows <= kSmallRows;
-  const int BM = small ? 16 : 128, BN = small ? 256 : 128;
+  const TileKind kind = tile_kind(rows);
+  const bool big = kind == kBigTile && DFS_LM_BIG_TILE;
+  const int BM = kind == kSmallTile ? 16 : big ? 256 : 128;
+  const int BN = kind == kSmallTile || big ? 256 : 128;
+  g.group = big ? 32 : 64;  // one or two workgroups per CU, 32 CUs per XCD
   g.mtiles = (int)cdiv(rows, BM);
   g.ntiles = cdiv(V, BN);
-  // about 2048 workgroups, at least two column tiles per stripe where there are enough
-  int64_t ns = cdiv(2048, g.mtiles);
-  if (ns > g.ntiles / 2) ns = g.ntiles / 2;
-  if (ns > 1024) ns = 1024;
+  // about four rounds of the chip's workgroup slots, at least two column tiles per
+  // stripe where there are enough
+  int64_t ns = cdiv(4 * 8 * g.group, g.mtiles);
+  // few rows: one column tile per workgroup (the pass streams W_lm; parallelism
+  // matters more than the merge of more lists)
+  if (ns > (kind == kSmallTile ? g.ntiles : g.ntiles / 2)) ns = kind == kSmallTile ? g.ntiles : g.ntiles / 2;
+  if (ns > 2048) ns = 2048;
   if (ns < 1) ns = 1;
   g.tps = (int)cdiv(g.ntiles, ns);
   g.nstripes = (int)cdiv(g.ntiles, g.tps);
   g.gm = g.mtiles < 8 ? g.mtiles : 8;
-  while (kGroup % g.gm) --g.gm;
-  g.gs = kGroup / g.gm;
+  while (g.group % g.gm) --g.gm;
+  g.gs = g.group / g.gm;
   g.mgroups = (int)cdiv(g.mtiles, g.gm);
   g.groups = g.mgroups * (int)cdiv(g.nstripes, g.gs);
   return g;
@@ -209,13 +338,23 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows
                               int32_t* out_idx, float* out_val, void* ws, hipStream_t stream) {
   const Grid g = make_grid(rows, V, d);
   uint64_t* partial = static_cast<uint64_t*>(ws);
-  const dim3 grid((unsigned)(8 * kGroup * cdiv(g.groups, 8)));
+  const dim3 grid((unsigned)(8 * g.group * cdiv(g.groups, 8)));
   const uint16_t* hp = static_cast<const uint16_t*>(hidden);
   const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
-  if (rows <= kSmallRows)
-    lmhead_topk_kernel<1, 4, 1, 4><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
-  else
-    lmhead_topk_kernel<2, 2, 4, 4><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+  switch (tile_kind(rows)) {
+    case kSmallTile:
+      lmhead_topk_kernel<1, 4, 1, 4><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+      break;
+    case kMidTile:
+      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+      break;
+    default:
+#if DFS_LM_BIG_TILE
+      lmhead_topk_dma_kernel<8, 8, 1><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+#else
+      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+#endif
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_merge(partial, rows, g.nstripes, out_idx, out_val, stream);
@@ -225,14 +364,30 @@ hipError_t launch_lmhead_logits(const void* hidden, const void* W_lm, int64_t ro
                                 float* out, hipStream_t stream) {
   const uint16_t* hp = static_cast<const uint16_t*>(hidden);
   const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
-  if (rows <= kSmallRows) {
-    const int64_t nt = cdiv(V, 256);
-    lmhead_logits_kernel<1, 4, 1, 4><<<dim3((unsigned)(cdiv(rows, 16) * nt)), kThreads, 0, stream>>>(
-        hp, wp, rows, V, d, nt, out);
-  } else {
-    const int64_t nt = cdiv(V, 128);
-    lmhead_logits_kernel<2, 2, 4, 4><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
-        hp, wp, rows, V, d, nt, out);
+  switch (tile_kind(rows)) {
+    case kSmallTile: {
+      const int64_t nt = cdiv(V, 256);
+      lmhead_logits_kernel<1, 4, 1, 4><<<dim3((unsigned)(cdiv(rows, 16) * nt)), kThreads, 0, stream>>>(
+          hp, wp, rows, V, d, nt, out);
+      break;
+    }
+    case kMidTile: {
+      const int64_t nt = cdiv(V, 128);
+      lmhead_logits_dma_kernel<4, 4, 2><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
+          hp, wp, rows, V, d, nt, out);
+      break;
+    }
+    default: {
+#if DFS_LM_BIG_TILE
+      const int64_t nt = cdiv(V, 256);
+      lmhead_logits_dma_kernel<8, 8, 1><<<dim3((unsigned)(cdiv(rows, 256) * nt)), kThreads, 0, stream>>>(
+          hp, wp, rows, V, d, nt, out);
+#else
+      const int64_t nt = cdiv(V, 128);
+      lmhead_logits_dma_kernel<4, 4, 2><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
+          hp, wp, rows, V, d, nt, out);
+#endif
+    }
   }
   return hipGetLastError();
 }

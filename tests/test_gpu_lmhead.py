@@ -76,6 +76,8 @@ SHAPES = [
     # ragged column tiles; a single stripe; many stripes
     (1, 1000, 64), (16, 20001, 256), (29, 4099, 512), (33, 20000, 256), (200, 50000, 128),
     (130, 777, 1024), (1, 16, 64),
+    # 256 x 256 tiles: exact tiles; ragged rows and columns; one column tile; deep K
+    (256, 4096, 256), (300, 20001, 512), (513, 777, 128), (257, 70000, 64), (1024, 5000, 2048),
 ]
 
 
