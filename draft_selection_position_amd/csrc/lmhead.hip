@@ -35,6 +35,9 @@ constexpr int kThreads = tile::kThreads;
 #ifndef DFS_LM_BIG_TILE
 #define DFS_LM_BIG_TILE 0
 #endif
+#ifndef DFS_LM_ROUNDS
+#define DFS_LM_ROUNDS 1
+#endif
 #ifndef DFS_LM_DEPTH
 #define DFS_LM_DEPTH 2
 #endif
@@ -116,8 +119,16 @@ __device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int ti
       uint64_t* gl = plist + (m0 + lr) * row_stride;
       const uint64_t* cr = cand_row(lr);
       uint64_t cur = 0;
-      if (lane < kK && s_has[lr]) cur = gl[lane];
-      for (int c0 = 0; c0 < cnt; c0 += kWave - kK) {
+      int c0 = 0;
+      if (s_has[lr]) {
+        if (lane < kK) cur = gl[lane];
+      } else {  // the row's first offers: sort them alone (no list to merge yet)
+        uint64_t x = lane < cnt ? cr[lane] : 0;
+        x = wave_sort_desc(x, lane);
+        cur = lane < kK ? x : 0;
+        c0 = kWave;
+      }
+      for (; c0 < cnt; c0 += kWave - kK) {
         const int ci = c0 + lane - kK;
         uint64_t x = lane < kK ? cur : (ci < cnt ? cr[ci] : 0);
         x = wave_sort_desc(x, lane);
@@ -311,7 +322,9 @@ Grid make_grid(int64_t rows, int64_t V, int64_t d) {
   g.ntiles = cdiv(V, BN);
   // about four rounds of the chip's workgroup slots, at least two column tiles per
   // stripe where there are enough
-  int64_t ns = cdiv(4 * 8 * g.group, g.mtiles);
+  // one round of the chip's workgroup slots: long stripes, so that few tiles are a
+  // stripe's first (whose fold sees every value as a candidate)
+  int64_t ns = cdiv(DFS_LM_ROUNDS * 8 * g.group, g.mtiles);
   // few rows: one column tile per workgroup (the pass streams W_lm; parallelism
   // matters more than the merge of more lists)
   if (ns > (kind == kSmallTile ? g.ntiles : g.ntiles / 2)) ns = kind == kSmallTile ? g.ntiles : g.ntiles / 2;
