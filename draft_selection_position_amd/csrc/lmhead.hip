@@ -12,9 +12,9 @@
 // lists per row.  The same product can be written out (lmhead_logits_kernel): the
 // fused result equals the top-16 pass run on those logits, bit for bit.
 //
-// Tiles: 128 x 128 (four waves of 64 x 64) for many rows; 16 x 256 (four waves of
-// 16 x 64) for a few rows, where the pass streams W_lm once and the matrix cores
-// idle.  Workgroups are numbered so that each XCD runs 8 row tiles x 8 stripes at
+// Tiles: 128 x 128 (four waves of 64 x 64) for many rows; for at most 32 rows the
+// product (16 x 256 tiles: the pass streams W_lm once and the matrix cores idle) is
+// written to the workspace and the top-16 pass runs over it, which is faster there.  Workgroups are numbered so that each XCD runs 8 row tiles x 8 stripes at
 // a time (64 workgroups, two per CU): the 8 stripes' W_lm tiles and the 8 row
 // tiles' h are then shared through the XCD's L2 while their k loops advance
 // together.
@@ -146,48 +146,9 @@ __device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int ti
   }
 }
 
-template <int WMW, int WNW, int TM, int TN>
-__global__ __launch_bounds__(kThreads, 2) void lmhead_topk_kernel(const uint16_t* __restrict__ h,
-                                                                  const uint16_t* __restrict__ W, Grid g,
-                                                                  uint64_t* __restrict__ partial) {
-  using S = tile::Shape<WMW, WNW, TM, TN>;
-  constexpr int BM = S::BM, BN = S::BN, CAP = 16 * (TN < 4 ? TN : 4);
-  static_assert(BM * CAP * 8 <= S::kLdsBytes, "candidates reuse the operand stages");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[S::kLdsBytes / 2];
-  __shared__ uint64_t s_thr[BM];
-  __shared__ int s_cnt[BM];
-  __shared__ int s_has[BM];
-  int mt, stripe;
-  if (!place(g, mt, stripe)) return;
-  const int tid = threadIdx.x;
-  const int64_t m0 = (int64_t)mt * BM;
-  const int tile_rows = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
-  for (int i = tid; i < BM; i += kThreads) {
-    s_thr[i] = 0;
-    s_cnt[i] = 0;
-    s_has[i] = 0;
-  }
-  const int64_t row_stride = (int64_t)g.nstripes * kK;
-  uint64_t* plist = partial + (int64_t)stripe * kK;  // row m's list at plist[m * row_stride]
-  uint64_t* cand = reinterpret_cast<uint64_t*>(lds);  // [BM][CAP], after each product
-  const __amdgpu_buffer_rsrc_t ra = tile::rows_rsrc(h + m0 * g.d, tile_rows, g.d);
-  const int KS = (int)(g.d / tile::kKStep);
-  const int64_t t0 = (int64_t)stripe * g.tps;
-  const int64_t t1 = t0 + g.tps < g.ntiles ? t0 + g.tps : g.ntiles;
-  for (int64_t nt_ = t0; nt_ < t1; ++nt_) {
-    const int64_t n0 = nt_ * BN;
-    const int64_t ncols = g.V - n0 < BN ? g.V - n0 : BN;
-    typename S::Acc acc;
-    tile::zero<WMW, WNW, TM, TN>(acc);
-    tile::mma<WMW, WNW, TM, TN, DFS_LM_DEPTH>(ra, tile::rows_rsrc(W + n0 * g.d, ncols, g.d), g.d, 0, KS,
-                                              lds, acc);
-    fold_tile<TM, TN, WNW>(acc.v, tile_rows, n0, ncols, s_thr, s_cnt, s_has,
-                           [&](int lr) { return cand + lr * CAP; }, plist, m0, row_stride);
-  }
-}
-
-// The same on the LDS-DMA tiles of mfma_big.h (TM = TN = 4: 128 x 128, two
-// workgroups per CU; 8: 256 x 256, one).
+// Workgroup (row tile, stripe): the product tile by tile on the LDS-DMA mainloop of
+// mfma_big.h (TM = TN = 4: 128 x 128, two workgroups per CU; 8: 256 x 256, one),
+// each tile folded into the stripe's row lists.
 template <int TM, int TN, int kMinWG>
 __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const uint16_t* __restrict__ h,
                                                                            const uint16_t* __restrict__ W,
@@ -325,9 +286,7 @@ Grid make_grid(int64_t rows, int64_t V, int64_t d) {
   // one round of the chip's workgroup slots: long stripes, so that few tiles are a
   // stripe's first (whose fold sees every value as a candidate)
   int64_t ns = cdiv(DFS_LM_ROUNDS * 8 * g.group, g.mtiles);
-  // few rows: one column tile per workgroup (the pass streams W_lm; parallelism
-  // matters more than the merge of more lists)
-  if (ns > (kind == kSmallTile ? g.ntiles : g.ntiles / 2)) ns = kind == kSmallTile ? g.ntiles : g.ntiles / 2;
+  if (ns > g.ntiles / 2) ns = g.ntiles / 2;
   if (ns > 2048) ns = 2048;
   if (ns < 1) ns = 1;
   g.tps = (int)cdiv(g.ntiles, ns);
@@ -342,22 +301,37 @@ Grid make_grid(int64_t rows, int64_t V, int64_t d) {
 
 }  // namespace
 
+// Few rows: the logits are small (at most 32 x V fp32) and writing them, then one
+// top-16 pass over them, beats folding every tile of a one-tile stripe (the two
+// kernels stream W_lm at the same rate); the logits then live in the workspace.
+static bool lmhead_two_pass(int64_t rows) { return rows <= kSmallRows; }
+
+static size_t lmhead_logits_bytes(int64_t rows, int64_t V) {
+  return align_up((size_t)rows * (size_t)V * sizeof(float), 256);
+}
+
 size_t lmhead_workspace_bytes(int64_t rows, int64_t V, int64_t d) {
+  if (lmhead_two_pass(rows)) return lmhead_logits_bytes(rows, V) + plan_topk(rows, V, 4).ws_bytes;
   const Grid g = make_grid(rows, V, d);
   return align_up((size_t)rows * g.nstripes * kK * sizeof(uint64_t), 256);
 }
 
 hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows, int64_t V, int64_t d,
                               int32_t* out_idx, float* out_val, void* ws, hipStream_t stream) {
+  if (lmhead_two_pass(rows)) {
+    float* U = static_cast<float*>(ws);
+    hipError_t e = launch_lmhead_logits(hidden, W_lm, rows, V, d, U, stream);
+    if (e != hipSuccess) return e;
+    const TopkPlan tp = plan_topk(rows, V, 4);
+    return launch_topk(tp, U, false, out_idx, out_val, static_cast<char*>(ws) + lmhead_logits_bytes(rows, V),
+                       stream);
+  }
   const Grid g = make_grid(rows, V, d);
   uint64_t* partial = static_cast<uint64_t*>(ws);
   const dim3 grid((unsigned)(8 * g.group * cdiv(g.groups, 8)));
   const uint16_t* hp = static_cast<const uint16_t*>(hidden);
   const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
-  switch (tile_kind(rows)) {
-    case kSmallTile:
-      lmhead_topk_kernel<1, 4, 1, 4><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
-      break;
+  switch (tile_kind(rows)) {  // (few rows took the two-pass way above)
     case kMidTile:
       lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
       break;

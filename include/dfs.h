@@ -229,14 +229,17 @@ int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W
  * Drafting Parallel", section "A Lightweight Path Selector"); the logits are
  * U = h W_lm^T, and the 16 largest per row are the candidates (section "The Right
  * Tokens Are Already There").  dfs_lmhead_topk computes the product on the matrix
- * cores (fp32 sums) and keeps only the running top-16 per row: U is never written.
+ * cores (fp32 sums) and keeps only the running top-16 per row: U is not written
+ * (for at most 32 rows, where U is small, it goes through the workspace and the
+ * top-16 pass, the faster way there; the result is the same).
  *   hidden [rows, d] bf16 (row-major), W_lm [V, d] bf16 (one row per token)
  *   out_idx [rows, 16] int32, out_val [rows, 16] fp32: value descending, then the
  *     lower id, on the fp32 sums -- exactly dfs_topk run on dfs_lmhead_logits' U.
  * dt must be DFS_BF16; d a multiple of 64 in [64, DFS_MAX_D]; 16 <= V < 2^31;
  * 1 <= rows <= 2^30.  hidden and W_lm 16-byte aligned, outputs 4, ws 256.
  * ws: dfs_lmhead_topk_workspace_bytes(rows, V, d) bytes (never 0): per-row lists of
- * the column stripes, merged at the end.  Finite inputs whose sums stay finite. */
+ * the column stripes, merged at the end (for <= 32 rows: U and the top-16 pass's
+ * lists).  Finite inputs whose sums stay finite. */
 size_t dfs_lmhead_topk_workspace_bytes(int64_t rows, int64_t V, int64_t d);
 int dfs_lmhead_topk(const void* hidden, const void* W_lm, dfs_dtype_t dt, int64_t rows, int64_t V,
                     int64_t d, int k, int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
