@@ -38,6 +38,9 @@ constexpr int kThreads = tile::kThreads;
 #ifndef DFS_LM_ROUNDS
 #define DFS_LM_ROUNDS 1
 #endif
+#ifndef DFS_LM_GM
+#define DFS_LM_GM 8  // row tiles per XCD group (the rest of the group: stripes)
+#endif
 #ifndef DFS_LM_DEPTH
 #define DFS_LM_DEPTH 2
 #endif
@@ -291,7 +294,7 @@ Grid make_grid(int64_t rows, int64_t V, int64_t d) {
   if (ns < 1) ns = 1;
   g.tps = (int)cdiv(g.ntiles, ns);
   g.nstripes = (int)cdiv(g.ntiles, g.tps);
-  g.gm = g.mtiles < 8 ? g.mtiles : 8;
+  g.gm = g.mtiles < DFS_LM_GM ? g.mtiles : DFS_LM_GM;
   while (g.group % g.gm) --g.gm;
   g.gs = g.group / g.gm;
   g.mgroups = (int)cdiv(g.mtiles, g.gm);

@@ -105,31 +105,45 @@ __device__ __forceinline__ void load_step(char* stage, rsrc_t ra, rsrc_t rb, int
 }
 
 template <class C>
-__device__ __forceinline__ void compute_step(const char* stage, int wm, int wn, int r, int q,
-                                             typename C::Acc& acc) {
-  constexpr int TM = C::TM, TN = C::TN;
+struct Frags {
+  bf16x8 a[C::TM], b[C::TN];
+};
+
+// This wave's operand fragments of one step, from its stage.
+template <class C>
+__device__ __forceinline__ void read_frags(const char* stage, int wm, int wn, int r, int q, Frags<C>& f) {
   const int sw = (q ^ ((r >> 1) & 3)) * 16;
-  const char* a = stage + (16 * TM * wm + r) * kRowBytes + sw;
-  const char* b = stage + C::BM * kRowBytes + (16 * TN * wn + r) * kRowBytes + sw;
-  bf16x8 af[TM], bfr[TN];
+  const char* a = stage + (16 * C::TM * wm + r) * kRowBytes + sw;
+  const char* b = stage + C::BM * kRowBytes + (16 * C::TN * wn + r) * kRowBytes + sw;
 #pragma unroll
-  for (int t = 0; t < TM; ++t) af[t] = *reinterpret_cast<const bf16x8*>(a + 16 * t * kRowBytes);
+  for (int t = 0; t < C::TM; ++t) f.a[t] = *reinterpret_cast<const bf16x8*>(a + 16 * t * kRowBytes);
 #pragma unroll
-  for (int t = 0; t < TN; ++t) bfr[t] = *reinterpret_cast<const bf16x8*>(b + 16 * t * kRowBytes);
+  for (int t = 0; t < C::TN; ++t) f.b[t] = *reinterpret_cast<const bf16x8*>(b + 16 * t * kRowBytes);
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_frags(const Frags<C>& f, typename C::Acc& acc) {
 #pragma unroll
-  for (int mt = 0; mt < TM; ++mt)
+  for (int mt = 0; mt < C::TM; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < TN; ++nt)
-      acc.v[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc.v[mt][nt], 0, 0, 0);
+    for (int nt = 0; nt < C::TN; ++nt)
+      acc.v[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mt], f.b[nt], acc.v[mt][nt], 0, 0, 0);
 }
 
 // acc += A[0:BM, 32 ks0 : 32 ks1] B[0:BN, same]^T.  lds: C::kLdsBytes of shared
 // memory, the four stages in a row.  Every thread of the workgroup must call it; it
 // ends with a barrier, after which the LDS may be reused.
+//
+// Step s of the loop: wait until step s + 1 has landed (this wave's loads; the
+// barrier covers the other waves' and frees the stage of step s - 1), issue the
+// loads of step s + 3 into that stage, read step s + 1's fragments into the spare
+// register set and run step s's MFMAs from the other: the LDS reads of the next
+// step overlap the matrix work of this one.
 template <class C>
 __device__ __forceinline__ void mma(rsrc_t ra, rsrc_t rb, int64_t K, int ks0, int ks1, char* lds,
                                     typename C::Acc& acc) {
   constexpr int kStageBytes = C::kStageBytes;
+  constexpr int L = C::kLoadsPerWave;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resources and M0 stay scalar
@@ -137,23 +151,25 @@ __device__ __forceinline__ void mma(rsrc_t ra, rsrc_t rb, int64_t K, int ks0, in
   const int wm = wave >> 1, wn = wave & 1;
   const int n = ks1 - ks0;
   char* st[kStages] = {lds, lds + kStageBytes, lds + 2 * kStageBytes, lds + 3 * kStageBytes};
-  // prologue: steps 0, 1, 2 in flight (a missing step loads the last one again)
+  // prologue: steps 0, 1, 2 in flight (a missing step loads the last one again);
+  // step 0's fragments in registers
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j) load_step<C>(st[j], ra, rb, K, ks0 + (j < n ? j : n - 1), wave, lane);
-  int s = 0;
-  for (; s < n; s += kStages) {
+  Frags<C> f[2];
+  wait_vmcnt<2 * L>();
+  bar();
+  read_frags<C>(st[0], wm, wn, r, q, f[0]);
+  for (int s = 0; s < n; s += kStages) {
 #pragma unroll
     for (int j = 0; j < kStages; ++j) {
       const int cur = s + j;
       if (cur < n) {
-        // this wave's loads of step cur are done when at most the two later steps'
-        // remain; the barrier makes every wave's part visible and frees the stage
-        // read at step cur - 1 for step cur + 3
-        wait_vmcnt<(kStages - 2) * C::kLoadsPerWave>();
+        wait_vmcnt<L>();  // this wave's loads of step cur + 1 (only cur + 2's remain)
         bar();
         const int nxt = cur + kStages - 1;
         load_step<C>(st[(j + kStages - 1) % kStages], ra, rb, K, ks0 + (nxt < n ? nxt : n - 1), wave, lane);
-        compute_step<C>(st[j], wm, wn, r, q, acc);
+        if (cur + 1 < n) read_frags<C>(st[(j + 1) % kStages], wm, wn, r, q, f[(j + 1) & 1]);
+        mfma_frags<C>(f[j & 1], acc);
       }
     }
   }
