@@ -61,6 +61,8 @@ def _check(ci, y_gpu, seqs=None):
 CASES = [
     # (batch, L, D): one tile; ragged rows and a 32-column last N tile; three waves busy; full width
     (3, 5, 256), (37, 16, 1280), (5, 7, 768), (2, 16, 5120), (1, 1, 512), (9, 3, 4096),
+    # enough rows for unsplit 128 x 64 tiles, with a 32-column last tile
+    (688, 16, 1280),
 ]
 
 
