@@ -219,7 +219,7 @@ def main() -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the selector on a single GPU; --gpus must be 1 "
+        print("bench.py: the selector runs on one GPU per process; --gpus must be 1 "
               "(sequences are independent, so a multi-GPU run is batch sharding with no exchange)",
               file=sys.stderr)
         return 2

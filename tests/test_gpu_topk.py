@@ -17,7 +17,7 @@ def _need_gpu():
         pytest.skip("no GPU")
     import draft_selection_position_amd as dfs
 
-    dfs.lib()  # a GPU machine without the built library must fail, not skip
+    dfs.lib()  # a machine with a GPU but without the built library must fail, not skip
 
 
 def _run(rows_np, dtype):
