@@ -5,19 +5,21 @@
 // Selector"); the logits are the drafter's LM head applied to its hidden state.
 // Here the head's product U = h W_lm^T (h [rows, d], W_lm [V, d], bf16, fp32 sums on
 // the matrix cores) and the top-16 selection (section "The Right Tokens Are Already
-// There") run in one kernel: each workgroup walks a stripe of 128- (or 256-) column
-// tiles of U and folds every tile into running per-row top-16 lists, so U never
-// reaches HBM.  Keys and order are those of the top-16 pass (value descending, then
-// the lower token id), on the fp32 sums.  A merge pass then combines the stripes'
-// lists per row.  The same product can be written out (lmhead_logits_kernel): the
-// fused result equals the top-16 pass run on those logits, bit for bit.
+// There") run in one kernel: each workgroup walks a stripe of column tiles of U and
+// folds every tile into running per-row top-16 lists, so U never reaches HBM.  Keys
+// and order are those of the top-16 pass (value descending, then the lower token
+// id), on the fp32 sums.  A merge pass then combines the stripes' lists per row.
+// The same product can be written out (lmhead_logits*_kernel): the fused result
+// equals the top-16 pass run on those logits, bit for bit.
 //
-// Tiles: 128 x 128 (four waves of 64 x 64) for many rows; for at most 32 rows the
-// product (16 x 256 tiles: the pass streams W_lm once and the matrix cores idle) is
-// written to the workspace and the top-16 pass runs over it, which is faster there.  Workgroups are numbered so that each XCD runs 8 row tiles x 8 stripes at
-// a time (64 workgroups, two per CU): the 8 stripes' W_lm tiles and the 8 row
-// tiles' h are then shared through the XCD's L2 while their k loops advance
-// together.
+// Tiles (LDS-DMA mainloop of mfma_big.h): 128 x 128 (four waves of 64 x 64, two
+// workgroups per CU) below 2048 rows, 256 x 256 (four waves of 128 x 128, one per
+// CU) from there.  For at most 32 rows the product (16 x 256 register-staged tiles,
+// mfma_tile.h: the pass streams W_lm once and the matrix cores idle) is written to
+// the workspace and the top-16 pass runs over it, which is faster there.
+// Workgroups are numbered so that each XCD runs a group of row tiles x stripes at a
+// time: the group's W_lm tiles and h rows are shared through the XCD's L2.
+
 #include <type_traits>
 
 #include "dfs_device.h"
@@ -30,10 +32,10 @@ namespace {
 
 constexpr int kThreads = tile::kThreads;
 #ifndef DFS_LM_BIG_ROWS
-#define DFS_LM_BIG_ROWS 256
+#define DFS_LM_BIG_ROWS 2048
 #endif
 #ifndef DFS_LM_BIG_TILE
-#define DFS_LM_BIG_TILE 0
+#define DFS_LM_BIG_TILE 1
 #endif
 #ifndef DFS_LM_ROUNDS
 #define DFS_LM_ROUNDS 1
@@ -53,6 +55,7 @@ struct Grid {
   int group;           // workgroups an XCD runs at a time
   int gm, gs;          // row tiles x stripes per group (gm * gs = group)
   int mgroups, groups; // groups along the rows, all groups
+  int cand_cap;        // pending candidates a row can hold: one tile's columns + kMergeAt - 1
 };
 
 // Workgroup -> (row tile, stripe); false for the padding of the last round.
@@ -66,104 +69,97 @@ __device__ __forceinline__ bool place(const Grid& g, int& mt, int& stripe) {
   return mt < g.mtiles && stripe < g.nstripes;
 }
 
-// Fold one product tile into the running row lists.  The wave holding rows
-// 16 TM wm + ... and columns 16 TN wn + ... of the tile offers every value whose key
-// beats its row's current 16th (s_thr); the offers of a phase (CAP columns of one
-// wave column) are appended to the row's candidates in LDS, then each row with
-// offers is merged into its list (kept in `partial`) by a 64-lane sort, always on
-// wave row % 4 and lanes 0-15 so that each list slot is read back by the lane that
-// wrote it.  cand_row(lr) gives row lr's candidate array (CAP keys).
+// Candidates pending per row before its list is merged (one 64-lane sort takes the
+// list and 48 candidates).
+constexpr int kMergeAt = 32;
+
+// Fold one product tile into the running row lists, in two passes.
+// Offers: the wave holding rows 16 TM wm + ... and columns 16 TN wn + ... of the
+// tile offers every value whose key beats its row's 16th at the last merge (s_thr):
+// the key is appended to the row's pending candidates in the workspace (`cand_row`,
+// an LDS counter per row).  Every accumulator is read once, in one pass.
+// Merges: a row with kMergeAt or more pending candidates (any, at the stripe's last
+// tile) merges them into its list (kept in `partial`) by 64-lane sorts, always on
+// wave row % 4 and lanes 0-15, so that each list slot is read back by the lane that
+// wrote it.  A stale threshold only lets more candidates through; every value that
+// can be in the top-16 is offered.
 template <int TM, int TN, int WNW, class CandRow>
 __device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int tile_rows, int64_t n0,
-                                          int64_t ncols, uint64_t* s_thr, int* s_cnt, int* s_has,
-                                          CandRow cand_row, uint64_t* plist, int64_t m0,
+                                          int64_t ncols, bool last, uint64_t* s_thr, int* s_cnt,
+                                          int* s_has, CandRow cand_row, uint64_t* plist, int64_t m0,
                                           int64_t row_stride) {
-  constexpr int BPH = TN < 4 ? TN : 4;  // column tiles of a wave folded per phase
-  constexpr int NPH = WNW * (TN / BPH);
-  static_assert(TN / BPH <= 2 && TN % BPH == 0, "one or two phases per wave column");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int wm = wave / WNW, wn = wave % WNW;
-  // The offers of column tiles b0 .. b0 + BPH - 1 (b0 a compile-time constant, so the
-  // accumulators are indexed statically).
-  auto offer = [&](auto b0c) {
-    constexpr int b0 = decltype(b0c)::value;
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+  for (int a = 0; a < TM; ++a) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
-        if (lr >= tile_rows) continue;
-        const uint64_t thr = s_thr[lr];
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
+      if (lr >= tile_rows) continue;
+      const uint64_t thr = s_thr[lr];
 #pragma unroll
-        for (int bb = 0; bb < BPH; ++bb) {
-          const int lc = 16 * TN * wn + 16 * (b0 + bb) + r;
-          if (lc >= ncols) continue;
-          const uint64_t key = make_key(v[a][b0 + bb][i], (uint32_t)(n0 + lc));
-          if (key > thr) cand_row(lr)[atomicAdd(&s_cnt[lr], 1)] = key;
-        }
-        // one row's offers at a time: keeps the scheduler from hoisting every key
-        // of the tile into registers at once
-        __builtin_amdgcn_sched_barrier(0);
-      }
-  };
-  for (int ph = 0; ph < NPH; ++ph) {
-    if (wn == ph / (TN / BPH)) {
-      if (TN / BPH == 1 || ph % (TN / BPH) == 0)
-        offer(std::integral_constant<int, 0>{});
-      else
-        offer(std::integral_constant<int, (TN / BPH > 1 ? BPH : 0)>{});
-    }
-    __syncthreads();
-    for (int lr = wave; lr < tile_rows; lr += 4) {
-      const int cnt = s_cnt[lr];
-      if (cnt == 0) continue;
-      uint64_t* gl = plist + (m0 + lr) * row_stride;
-      const uint64_t* cr = cand_row(lr);
-      uint64_t cur = 0;
-      int c0 = 0;
-      if (s_has[lr]) {
-        if (lane < kK) cur = gl[lane];
-      } else {  // the row's first offers: sort them alone (no list to merge yet)
-        uint64_t x = lane < cnt ? cr[lane] : 0;
-        x = wave_sort_desc(x, lane);
-        cur = lane < kK ? x : 0;
-        c0 = kWave;
-      }
-      for (; c0 < cnt; c0 += kWave - kK) {
-        const int ci = c0 + lane - kK;
-        uint64_t x = lane < kK ? cur : (ci < cnt ? cr[ci] : 0);
-        x = wave_sort_desc(x, lane);
-        cur = lane < kK ? x : 0;
-      }
-      if (lane < kK) gl[lane] = cur;
-      const uint64_t thr = lane_u64(cur, kK - 1);
-      if (lane == 0) {
-        s_thr[lr] = thr;
-        s_cnt[lr] = 0;
-        s_has[lr] = 1;
+      for (int b = 0; b < TN; ++b) {
+        const int lc = 16 * TN * wn + 16 * b + r;
+        if (lc >= ncols) continue;
+        const uint64_t key = make_key(v[a][b][i], (uint32_t)(n0 + lc));
+        if (key > thr) cand_row(lr)[atomicAdd(&s_cnt[lr], 1)] = key;
       }
     }
-    __syncthreads();
+    // a row block at a time: keeps the scheduler from hoisting every key of the
+    // tile into registers at once
+    __builtin_amdgcn_sched_barrier(0);
   }
+  __syncthreads();
+  for (int lr = wave; lr < tile_rows; lr += 4) {
+    const int cnt = s_cnt[lr];
+    if (cnt == 0 || (cnt < kMergeAt && !last)) continue;
+    uint64_t* gl = plist + (m0 + lr) * row_stride;
+    const uint64_t* cr = cand_row(lr);
+    uint64_t cur = 0;
+    int c0 = 0;
+    if (s_has[lr]) {
+      if (lane < kK) cur = gl[lane];
+    } else {  // the row's first merge: its first 64 candidates alone (no list yet)
+      uint64_t x = lane < cnt ? cr[lane] : 0;
+      x = wave_sort_desc(x, lane);
+      cur = lane < kK ? x : 0;
+      c0 = kWave;
+    }
+    for (; c0 < cnt; c0 += kWave - kK) {
+      const int ci = c0 + lane - kK;
+      uint64_t x = lane < kK ? cur : (ci < cnt ? cr[ci] : 0);
+      x = wave_sort_desc(x, lane);
+      cur = lane < kK ? x : 0;
+    }
+    if (lane < kK) gl[lane] = cur;
+    const uint64_t thr = lane_u64(cur, kK - 1);
+    if (lane == 0) {
+      s_thr[lr] = thr;
+      s_cnt[lr] = 0;
+      s_has[lr] = 1;
+    }
+  }
+  __syncthreads();
 }
 
 // Workgroup (row tile, stripe): the product tile by tile on the LDS-DMA mainloop of
 // mfma_big.h (TM = TN = 4: 128 x 128, two workgroups per CU; 8: 256 x 256, one),
-// each tile folded into the stripe's row lists.
+// each tile folded into the stripe's row lists.  cand: the pending candidates,
+// [rows, nstripes, g.cand_cap] keys.
 template <int TM, int TN, int kMinWG>
 __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const uint16_t* __restrict__ h,
                                                                            const uint16_t* __restrict__ W,
                                                                            Grid g,
-                                                                           uint64_t* __restrict__ partial) {
+                                                                           uint64_t* __restrict__ partial,
+                                                                           uint64_t* __restrict__ cand) {
   using C = big::Cfg<TM, TN>;
-  constexpr int BM = C::BM, BN = C::BN, CAP = 16 * (TN < 4 ? TN : 4);
+  constexpr int BM = C::BM, BN = C::BN;
   __shared__ __attribute__((aligned(1024))) char lds[C::kLdsBytes];
   __shared__ uint64_t s_thr[BM];
   __shared__ int s_cnt[BM];
   __shared__ int s_has[BM];
-  static_assert(BM * CAP * 8 <= C::kLdsBytes, "candidates reuse the operand stages");
   int mt, stripe;
   if (!place(g, mt, stripe)) return;
   const int tid = threadIdx.x;
@@ -180,16 +176,15 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const
   const int KS = (int)(g.d / big::kK);
   const int64_t t0 = (int64_t)stripe * g.tps;
   const int64_t t1 = t0 + g.tps < g.ntiles ? t0 + g.tps : g.ntiles;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(lds);  // [BM][CAP], after each product
-  auto cand_row = [&](int lr) { return cand + lr * CAP; };
+  auto cand_row = [&](int lr) { return cand + ((m0 + lr) * g.nstripes + stripe) * g.cand_cap; };
   for (int64_t nt_ = t0; nt_ < t1; ++nt_) {
     const int64_t n0 = nt_ * BN;
     const int64_t ncols = g.V - n0 < BN ? g.V - n0 : BN;
     typename C::Acc acc;
     C::zero(acc);
     big::mma<C>(ra, big::rows_rsrc(W + n0 * g.d, ncols, g.d), g.d, 0, KS, lds, acc);
-    fold_tile<TM, TN, 2>(acc.v, tile_rows, n0, ncols, s_thr, s_cnt, s_has, cand_row, plist, m0,
-                         row_stride);
+    fold_tile<TM, TN, 2>(acc.v, tile_rows, n0, ncols, nt_ + 1 == t1, s_thr, s_cnt, s_has, cand_row, plist,
+                         m0, row_stride);
   }
 }
 
@@ -264,8 +259,9 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_logits_dma_kernel(con
     }
 }
 
-// Tile shapes: few rows -> 16 x 256 (W_lm streamed once); up to DFS_LM_BIG_ROWS ->
-// 128 x 128; more -> 256 x 256 (one workgroup per CU).
+// Tile shapes: few rows -> 16 x 256 (W_lm streamed once); below DFS_LM_BIG_ROWS ->
+// 128 x 128; from there 256 x 256 (one workgroup per CU; measured faster from 4096
+// rows, slower at 1024).
 constexpr int64_t kSmallRows = 32;
 enum TileKind { kSmallTile = 0, kMidTile = 1, kBigTile = 2 };
 TileKind tile_kind(int64_t rows) {
@@ -299,6 +295,7 @@ Grid make_grid(int64_t rows, int64_t V, int64_t d) {
   g.gs = g.group / g.gm;
   g.mgroups = (int)cdiv(g.mtiles, g.gm);
   g.groups = g.mgroups * (int)cdiv(g.nstripes, g.gs);
+  g.cand_cap = (int)align_up((size_t)(BN + kMergeAt - 1), 32);
   return g;
 }
 
@@ -309,6 +306,10 @@ Grid make_grid(int64_t rows, int64_t V, int64_t d) {
 // kernels stream W_lm at the same rate); the logits then live in the workspace.
 static bool lmhead_two_pass(int64_t rows) { return rows <= kSmallRows; }
 
+static size_t lmhead_lists_bytes(const Grid& g) {
+  return align_up((size_t)g.rows * g.nstripes * kK * sizeof(uint64_t), 256);
+}
+
 static size_t lmhead_logits_bytes(int64_t rows, int64_t V) {
   return align_up((size_t)rows * (size_t)V * sizeof(float), 256);
 }
@@ -316,7 +317,7 @@ static size_t lmhead_logits_bytes(int64_t rows, int64_t V) {
 size_t lmhead_workspace_bytes(int64_t rows, int64_t V, int64_t d) {
   if (lmhead_two_pass(rows)) return lmhead_logits_bytes(rows, V) + plan_topk(rows, V, 4).ws_bytes;
   const Grid g = make_grid(rows, V, d);
-  return align_up((size_t)rows * g.nstripes * kK * sizeof(uint64_t), 256);
+  return lmhead_lists_bytes(g) + align_up((size_t)rows * g.nstripes * g.cand_cap * sizeof(uint64_t), 256);
 }
 
 hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows, int64_t V, int64_t d,
@@ -331,18 +332,19 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows
   }
   const Grid g = make_grid(rows, V, d);
   uint64_t* partial = static_cast<uint64_t*>(ws);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + lmhead_lists_bytes(g));
   const dim3 grid((unsigned)(8 * g.group * cdiv(g.groups, 8)));
   const uint16_t* hp = static_cast<const uint16_t*>(hidden);
   const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
   switch (tile_kind(rows)) {  // (few rows took the two-pass way above)
     case kMidTile:
-      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
       break;
     default:
 #if DFS_LM_BIG_TILE
-      lmhead_topk_dma_kernel<8, 8, 1><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+      lmhead_topk_dma_kernel<8, 8, 1><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
 #else
-      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial);
+      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
 #endif
   }
   hipError_t e = hipGetLastError();

@@ -151,25 +151,44 @@ __device__ __forceinline__ void mma(rsrc_t ra, rsrc_t rb, int64_t K, int ks0, in
   const int wm = wave >> 1, wn = wave & 1;
   const int n = ks1 - ks0;
   char* st[kStages] = {lds, lds + kStageBytes, lds + 2 * kStageBytes, lds + 3 * kStageBytes};
-  // prologue: steps 0, 1, 2 in flight (a missing step loads the last one again);
-  // step 0's fragments in registers
+  // prologue: steps 0, 1, 2 in flight (a missing step loads the last one again)
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j) load_step<C>(st[j], ra, rb, K, ks0 + (j < n ? j : n - 1), wave, lane);
-  Frags<C> f[2];
-  wait_vmcnt<2 * L>();
-  bar();
-  read_frags<C>(st[0], wm, wn, r, q, f[0]);
-  for (int s = 0; s < n; s += kStages) {
+  if constexpr (C::TM * C::TN > 16) {
+    // 128 x 128 per wave: the accumulators fill the AGPRs, so there is no room for a
+    // second fragment set; step s waits for its own stage and reads it
+    for (int s = 0; s < n; s += kStages) {
 #pragma unroll
-    for (int j = 0; j < kStages; ++j) {
-      const int cur = s + j;
-      if (cur < n) {
-        wait_vmcnt<L>();  // this wave's loads of step cur + 1 (only cur + 2's remain)
-        bar();
-        const int nxt = cur + kStages - 1;
-        load_step<C>(st[(j + kStages - 1) % kStages], ra, rb, K, ks0 + (nxt < n ? nxt : n - 1), wave, lane);
-        if (cur + 1 < n) read_frags<C>(st[(j + 1) % kStages], wm, wn, r, q, f[(j + 1) & 1]);
-        mfma_frags<C>(f[j & 1], acc);
+      for (int j = 0; j < kStages; ++j) {
+        const int cur = s + j;
+        if (cur < n) {
+          wait_vmcnt<2 * L>();  // this wave's loads of step cur (cur + 1's and cur + 2's remain)
+          bar();
+          const int nxt = cur + kStages - 1;
+          load_step<C>(st[(j + kStages - 1) % kStages], ra, rb, K, ks0 + (nxt < n ? nxt : n - 1), wave, lane);
+          Frags<C> f;
+          read_frags<C>(st[j], wm, wn, r, q, f);
+          mfma_frags<C>(f, acc);
+        }
+      }
+    }
+  } else {
+    Frags<C> f[2];
+    wait_vmcnt<2 * L>();
+    bar();
+    read_frags<C>(st[0], wm, wn, r, q, f[0]);
+    for (int s = 0; s < n; s += kStages) {
+#pragma unroll
+      for (int j = 0; j < kStages; ++j) {
+        const int cur = s + j;
+        if (cur < n) {
+          wait_vmcnt<L>();  // this wave's loads of step cur + 1 (only cur + 2's remain)
+          bar();
+          const int nxt = cur + kStages - 1;
+          load_step<C>(st[(j + kStages - 1) % kStages], ra, rb, K, ks0 + (nxt < n ? nxt : n - 1), wave, lane);
+          if (cur + 1 < n) read_frags<C>(st[(j + 1) % kStages], wm, wn, r, q, f[(j + 1) & 1]);
+          mfma_frags<C>(f[j & 1], acc);
+        }
       }
     }
   }

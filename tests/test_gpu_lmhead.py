@@ -78,6 +78,8 @@ SHAPES = [
     (130, 777, 1024), (1, 16, 64),
     # 256 x 256 tiles: exact tiles; ragged rows and columns; one column tile; deep K
     (256, 4096, 256), (300, 20001, 512), (513, 777, 128), (257, 70000, 64), (1024, 5000, 2048),
+    # 256 x 256 tiles (from 2048 rows): ragged rows and columns
+    (2100, 3000, 256),
 ]
 
 
