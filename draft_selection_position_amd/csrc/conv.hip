@@ -19,8 +19,9 @@
 // adds the split partial sums in split order and applies the convolution (a
 // device-wide fence per workgroup to let the last split do it in place writes
 // back the L2 of a multi-XCD part and measured three times slower).
-// fp32 path (small shapes): the correction by wave dot products into workspace,
-// then an elementwise kernel.
+// fp32 path (small shapes): one kernel, each workgroup the correction of an 8-row by
+// 8-column tile by vector dot products (K split over its four waves) and then the
+// convolution of those rows over the 64 channels the columns serve.
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "mfma_tile.h"
@@ -181,64 +182,92 @@ __global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
 }
 
 // ---------------------------------------------------------------- fp32 path
-constexpr int kF32Rows = 8;  // rows per wave
+constexpr int kF32Rows = 8;  // rows of a workgroup
+constexpr int kF32Cols = 8;  // correction columns of a workgroup: four groups, 64 channels
 
-// c[m, n] = sum_k x[m, k] W_c[n, k] for 8 rows and one column per wave: lanes
-// stride k (coalesced), then a fixed-order reduction across the wave.
-__global__ __launch_bounds__(kWave) void corr_f32_kernel(const float* __restrict__ x,
-                                                         const float* __restrict__ Wc, int64_t rows,
-                                                         int64_t D, float* __restrict__ c) {
-  const int lane = threadIdx.x;
-  const int64_t N = D / 8;
-  const int64_t n = (int64_t)blockIdx.x % N;
-  const int64_t m0 = (int64_t)blockIdx.x / N * kF32Rows;
-  float acc[kF32Rows];
+// Sum over the wave of v[lane] for each of 64 per-lane values, ending in lane j with
+// the sum of everyone's v[j]: six exchange steps, each halving the values a lane
+// keeps (63 exchanges in all, against 384 for 64 separate butterflies).  Fixed
+// pairing, so the result does not depend on timing.
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[64], int lane) {
 #pragma unroll
-  for (int i = 0; i < kF32Rows; ++i) acc[i] = 0.0f;
-  for (int64_t k = lane; k < D; k += kWave) {
-    const float w = Wc[n * D + k];
+  for (int st = 0; st < 6; ++st) {
+    const int s = 32 >> st;  // partner distance, also the values kept after this step
+    const bool up = (lane & s) != 0;
 #pragma unroll
-    for (int i = 0; i < kF32Rows; ++i)
-      if (m0 + i < rows) acc[i] = fmaf(x[(m0 + i) * D + k], w, acc[i]);
+    for (int i = 0; i < s; ++i) {
+      const float keep = up ? v[i + s] : v[i];
+      const float give = up ? v[i] : v[i + s];
+      v[i] = keep + __uint_as_float(xor_lanes(__float_as_uint(give), s, lane));
+    }
   }
-#pragma unroll
-  for (int i = 0; i < kF32Rows; ++i) {
-    float v = acc[i];
-#pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) v += __uint_as_float(xor_lanes(__float_as_uint(v), s, lane));
-    if (lane == 0 && m0 + i < rows) c[(m0 + i) * N + n] = v;
-  }
+  return v[0];
 }
 
-__global__ __launch_bounds__(kThreads) void conv2_apply_f32_kernel(
+// One workgroup: the correction c[m0 .. m0+7, 8 cg .. 8 cg + 7] and the convolution
+// of those 8 rows over the 64 channels those columns serve.  The four waves split K
+// (wave w takes the 256-wide k slices w, w + 4, ...; a lane one float4 of each), sum
+// their slice partials within the wave, then in a fixed order across waves in LDS.
+// Rows past the end load the last row and are not written.
+__global__ __launch_bounds__(kThreads) void conv2_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ xprev, const float* __restrict__ base,
-    const float* __restrict__ c, int64_t rows, int L, int64_t D, float* __restrict__ y) {
-  const int64_t nvec = D / 4;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= rows * nvec) return;
-  const int64_t m = i / nvec;
-  const int64_t ch = 4 * (i - m * nvec);
-  const int64_t b = m / L;
-  const int t = (int)(m - b * L);
-  const int64_t g = ch / 16;
-  const float c0 = c[m * (D / 8) + 2 * g];
-  const float c1 = c[m * (D / 8) + 2 * g + 1];
-  const float4 xv = *reinterpret_cast<const float4*>(x + m * D + ch);
-  const float4 pv = t > 0 ? *reinterpret_cast<const float4*>(x + (m - 1) * D + ch)
-                          : *reinterpret_cast<const float4*>(xprev + b * D + ch);
-  const float4 b0 = *reinterpret_cast<const float4*>(base + ch);
-  const float4 b1 = *reinterpret_cast<const float4*>(base + D + ch);
-  float4 o;
-  o.x = fmaf(b0.x + c0, xv.x, (b1.x + c1) * pv.x);
-  o.y = fmaf(b0.y + c0, xv.y, (b1.y + c1) * pv.y);
-  o.z = fmaf(b0.z + c0, xv.z, (b1.z + c1) * pv.z);
-  o.w = fmaf(b0.w + c0, xv.w, (b1.w + c1) * pv.w);
-  *reinterpret_cast<float4*>(y + m * D + ch) = o;
+    const float* __restrict__ Wc, int64_t rows, int L, int64_t D, float* __restrict__ y) {
+  __shared__ float part[4][64];
+  __shared__ float cs[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t ncg = D / 8 / kF32Cols;
+  const int64_t cg = (int64_t)blockIdx.x % ncg;
+  const int64_t m0 = (int64_t)blockIdx.x / ncg * kF32Rows;
+  const float* xr[kF32Rows];
+#pragma unroll
+  for (int r = 0; r < kF32Rows; ++r) xr[r] = x + (m0 + r < rows ? m0 + r : rows - 1) * D;
+  const float* wr = Wc + kF32Cols * cg * D;
+  float v[64];  // v[8 r + j]: partial of c[m0 + r, 8 cg + j]
+#pragma unroll
+  for (int i = 0; i < 64; ++i) v[i] = 0.0f;
+  for (int64_t k = 4 * lane + 256 * wave; k < D; k += 1024) {
+    float4 w[kF32Cols], xv[kF32Rows];
+#pragma unroll
+    for (int j = 0; j < kF32Cols; ++j) w[j] = *reinterpret_cast<const float4*>(wr + j * D + k);
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r) xv[r] = *reinterpret_cast<const float4*>(xr[r] + k);
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+      for (int j = 0; j < kF32Cols; ++j) {
+        float a = v[8 * r + j];
+        a = fmaf(xv[r].x, w[j].x, a);
+        a = fmaf(xv[r].y, w[j].y, a);
+        a = fmaf(xv[r].z, w[j].z, a);
+        v[8 * r + j] = fmaf(xv[r].w, w[j].w, a);
+      }
+  }
+  part[wave][lane] = wave_transpose_sum(v, lane);
+  __syncthreads();
+  if (wave == 0) cs[lane] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  __syncthreads();
+  // the convolution: 8 rows x 64 channels, two per thread; cs[8 r + 2 g + tap]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = tid + kThreads * h;
+    const int r = e >> 6, cl = e & 63;
+    const int64_t m = m0 + r;
+    if (m >= rows) continue;
+    const int64_t ch = 64 * cg + cl;
+    const int64_t b = m / L;
+    const int t = (int)(m - b * L);
+    const float c0 = cs[8 * r + 2 * (cl >> 4)];
+    const float c1 = cs[8 * r + 2 * (cl >> 4) + 1];
+    const float xv = x[m * D + ch];
+    const float pv = t > 0 ? x[(m - 1) * D + ch] : xprev[b * D + ch];
+    y[m * D + ch] = fmaf(base[ch] + c0, xv, (base[D + ch] + c1) * pv);
+  }
 }
 
 }  // namespace
 
-int64_t conv2_max_f32_elems() { return (int64_t)1 << 34; }
+// fp32 grid: batch * L * D / 512 workgroups of 256 threads, within 2^32 work-items.
+int64_t conv2_max_f32_elems() { return (int64_t)1 << 32; }
 
 #ifndef DFS_CONV_TARGET_WG
 #define DFS_CONV_TARGET_WG 512
@@ -265,7 +294,7 @@ ConvSplit conv2_splits(int64_t rows, int64_t D) {
 
 size_t conv2_workspace_bytes(int64_t rows, int64_t D, bool bf16) {
   const int64_t splits = bf16 ? conv2_splits(rows, D).splits : 1;
-  if (bf16 && splits == 1) return 0;
+  if (splits == 1) return 0;
   return align_up((size_t)splits * (size_t)rows * (size_t)(D / 8) * sizeof(float), 256);
 }
 
@@ -290,13 +319,10 @@ hipError_t launch_conv2(const void* x, const void* x_prev, const void* base, con
           static_cast<uint16_t*>(y));
     }
   } else {
-    float* c = static_cast<float*>(ws);
-    corr_f32_kernel<<<dim3((unsigned)(D / 8 * cdiv(rows, kF32Rows))), kWave, 0, stream>>>(
-        static_cast<const float*>(x), static_cast<const float*>(W_c), rows, D, c);
-    const int64_t jobs = rows * (D / 4);
-    conv2_apply_f32_kernel<<<dim3((unsigned)cdiv(jobs, kThreads)), kThreads, 0, stream>>>(
+    conv2_f32_kernel<<<dim3((unsigned)(D / 8 / kF32Cols * cdiv(rows, kF32Rows))), kThreads, 0, stream>>>(
         static_cast<const float*>(x), static_cast<const float*>(x_prev),
-        static_cast<const float*>(base), c, rows, (int)L, D, static_cast<float*>(y));
+        static_cast<const float*>(base), static_cast<const float*>(W_c), rows, (int)L, D,
+        static_cast<float*>(y));
   }
   return hipGetLastError();
 }

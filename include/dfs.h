@@ -215,9 +215,10 @@ int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t
  *   y [batch, L, D]   output, same dtype as the inputs; must not overlap x or x_prev
  * All of dtype dt (bf16: correction on the matrix cores with fp32 sums, y rounded to
  * nearest-even bf16; fp32: fp32 throughout).  D a multiple of 256 in [256, DFS_MAX_D],
- * 1 <= L <= DFS_CONV_MAX_L, batch * L < 2^31 (fp32: batch * L * D <= 2^34).  Every
+ * 1 <= L <= DFS_CONV_MAX_L, batch * L < 2^31 (fp32: batch * L * D <= 2^32).  Every
  * pointer 16-byte aligned, ws 256-byte aligned.
- * ws: dfs_conv2_workspace_bytes(batch, L, D, dt) bytes (0 for bf16: ws may be NULL). */
+ * ws: dfs_conv2_workspace_bytes(batch, L, D, dt) bytes: split partial sums of the bf16
+ * correction when the shape is too small to fill the chip, else 0 (ws may then be NULL). */
 size_t dfs_conv2_workspace_bytes(int64_t batch, int64_t L, int64_t D, dfs_dtype_t dt);
 int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W_c, dfs_dtype_t dt,
               int64_t batch, int64_t L, int64_t D, void* y, void* ws, size_t ws_bytes,

@@ -192,13 +192,18 @@ def test_conv2_validation(L):
     assert _conv(L, x=P + 8) == E_ALIGN
     assert _conv(L, y=P + 64) == E_ARG  # overlaps x
     assert _conv(L, y=P + 0x100000) == E_ARG  # overlaps x_prev
-    # fp32 needs a workspace for the correction; bf16 needs none
+    # fp32 needs no workspace; bf16 needs one only when K is split (512 rows of 5120:
+    # 20 tiles, too few for the chip), for the split partial sums of the correction
+    assert L.dfs_conv2_workspace_bytes(2, 4, 512, 0) == 0
     assert L.dfs_conv2_workspace_bytes(2, 4, 512, 1) == 0
-    nb = L.dfs_conv2_workspace_bytes(2, 4, 512, 0)
-    assert nb >= 2 * 4 * 64 * 4
-    assert _conv(L, dt=0, ws=None, wsb=0) == E_WS
-    assert _conv(L, dt=0, ws=P + 0x3000000 + 1, wsb=nb) == E_ALIGN
+    nb = L.dfs_conv2_workspace_bytes(32, 16, 5120, 1)
+    assert nb >= 2 * 512 * 640 * 4
+    assert _conv(L, batch=32, Lp=16, D=5120, ws=None, wsb=0) == E_WS
+    assert _conv(L, batch=32, Lp=16, D=5120, ws=P + 0x3000000, wsb=nb - 1) == E_WS
+    assert _conv(L, dt=0, ws=P + 0x3000000 + 1, wsb=64) == E_ALIGN
     assert L.dfs_conv2_workspace_bytes(2, 4, 500, 0) == 0
+    # fp32: at most 2^32 elements of x (the grid's work-item count)
+    assert _conv(L, dt=0, batch=1 << 13, Lp=64, D=8192 + 256) == E_SHAPE
 
 
 def test_lmhead_validation(L):

@@ -74,7 +74,11 @@ def test_conv2_bf16_matches_oracle(batch, L, D, corr):
     print(f"conv2 bf16 {batch}x{L}x{D} corr {corr}: worst relative error {worst:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("batch,L,D", [(1, 8, 1024), (3, 5, 512), (2, 16, 256)], ids=lambda v: str(v))
+@pytest.mark.parametrize("batch,L,D", [
+    # one 8-row tile; ragged rows; only the first of four waves has a K slice; five K slices
+    # over four waves and a ragged last row tile; the widest workload
+    (1, 8, 1024), (3, 5, 512), (2, 16, 256), (37, 16, 256), (5, 7, 1280), (4, 16, 5120),
+], ids=lambda v: str(v))
 def test_conv2_f32_matches_oracle(batch, L, D):
     ci = make_conv(variant("tiny", batch=batch, L=L, d=D), corr_std=0.02)
     _check(ci, _run(ci))
