@@ -45,7 +45,8 @@ struct GatePlan {
   bool bf16;
   int splits;          // K-splits (partial sums reduced by the finish kernel)
   int64_t kchunk;      // hidden elements per split
-  int row_tiles;       // 16-row MFMA tiles per wave (bf16 path)
+  int row_tiles;       // 16-row MFMA tiles per wave (bf16 path, 64-row tiles)
+  bool dma;            // bf16 on 128 x 128 LDS-DMA tiles (many rows, d a multiple of 32)
   size_t packed_off, packed_bytes;    // W_h packed for the matrix cores (bf16 path)
   size_t partial_off, partial_bytes;  // [splits, rows, 256] fp32
   size_t ws_bytes;

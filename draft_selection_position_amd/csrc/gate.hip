@@ -18,6 +18,7 @@
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "gate_pack.h"
+#include "mfma_big.h"
 
 namespace dfs {
 namespace {
@@ -165,6 +166,78 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
   }
 }
 
+// ---------------------------------------------------------------- many rows
+// 128 x 128 tiles of Z on the LDS-DMA mainloop (mfma_big.h: four waves of 64 x 64,
+// operands straight from memory into an S-stage LDS ring), for row counts that give
+// enough tiles: W_h is read 128 rows at a time instead of 64, and no wave fetches
+// operands another wave also fetches.  The packed W_h is an operand whose row n of
+// k step ks sits at ks * 256 * 64 + n * 64 bytes.  Work items (K split, row tile,
+// column half) are numbered column half fastest and cut into eight contiguous runs,
+// one per XCD: an XCD holds one K slice of W_h in its L2, and the two column halves
+// of a row tile read its H rows back to back (the second from L2).
+#ifndef DFS_GATE_STAGES
+#define DFS_GATE_STAGES 4
+#endif
+#ifndef DFS_GATE_DMA_ROWS
+#define DFS_GATE_DMA_ROWS 2048
+#endif
+using GC = big::Cfg<4, 4, DFS_GATE_STAGES>;
+constexpr int kDmaBM = GC::BM;                 // 128 rows
+constexpr int kDmaBN = GC::BN;                 // 128 columns: two halves of the 256
+constexpr int kDmaPitch = kDmaBN + 4;          // fp32 per LDS row of the output tile
+constexpr int kDmaLds = GC::kLdsBytes > kDmaBM * kDmaPitch * 4 ? GC::kLdsBytes : kDmaBM * kDmaPitch * 4;
+
+__global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* __restrict__ H,
+                                                               const uint16_t* __restrict__ Wp,
+                                                               int64_t rows, int64_t d, int mtiles,
+                                                               int splits, int kps, int per_xcd,
+                                                               float* __restrict__ partial,
+                                                               float* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds[kDmaLds];
+  const int64_t t = (int64_t)(blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
+  if (t >= (int64_t)splits * mtiles * 2) return;
+  const int nh = (int)(t & 1);
+  const int mt = (int)((t >> 1) % mtiles);
+  const int s = (int)((t >> 1) / mtiles);
+  const int64_t m0 = (int64_t)mt * kDmaBM;
+  const int tile_rows = (int)(rows - m0 < kDmaBM ? rows - m0 : kDmaBM);
+  const int KB = (int)(d / kKB);
+  const int ks0 = s * kps;
+  const int ks1 = ks0 + kps < KB ? ks0 + kps : KB;
+  const big::Operand a = big::rows_operand(H + m0 * d, tile_rows, d);
+  const big::Operand b{big::span_rsrc(Wp + nh * kDmaBN * kKB, (int64_t)KB * kE * kKB * 2 - nh * kDmaBN * kKB * 2),
+                       (uint32_t)(kKB * 2), (uint32_t)(kE * kKB * 2)};
+  GC::Acc acc;
+  GC::zero(acc);
+  big::mma<GC>(a, b, ks0, ks1, lds, acc);
+  // the tile through LDS (rows of 128 fp32), then row-contiguous 16-byte stores
+  float* sOut = reinterpret_cast<float*>(lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int mt_ = 0; mt_ < GC::TM; ++mt_)
+#pragma unroll
+    for (int nt = 0; nt < GC::TN; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sOut[(16 * GC::TM * wm + 16 * mt_ + 4 * q + i) * kDmaPitch + 16 * GC::TN * wn + 16 * nt + r] =
+            acc.v[mt_][nt][i];
+  __syncthreads();
+  const int c4 = tid & 31;  // 32 float4 per row
+  for (int rr = tid >> 5; rr < tile_rows; rr += kThreads / 32) {
+    float4 v = *reinterpret_cast<const float4*>(&sOut[rr * kDmaPitch + 4 * c4]);
+    const int64_t col = (int64_t)(m0 + rr) * kE + nh * kDmaBN + 4 * c4;
+    if (splits == 1) {
+      v = make_float4(sigmoidf(v.x), sigmoidf(v.y), sigmoidf(v.z), sigmoidf(v.w));
+      *reinterpret_cast<float4*>(out + col) = v;
+    } else {
+      *reinterpret_cast<float4*>(partial + (int64_t)s * rows * kE + col) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
 constexpr int kF32Rows = 8;     // rows per workgroup
 constexpr int kF32KBlock = 256; // k staged in LDS at a time
 constexpr int kF32Unroll = 16;  // W_h loads in flight per thread
@@ -257,11 +330,14 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   p.bf16 = bf16;
   size_t off = 0;
   if (bf16) {
-    p.row_tiles = kTileM / 16;
-    const int64_t mtiles = cdiv(rows, kTileM);
     const int64_t KB = cdiv(d, kKB);
-    int64_t splits = cdiv(kTargetWG, mtiles);
-    const int64_t max_splits = KB / 2 > 1 ? KB / 2 : 1;  // at least two k steps per split
+    p.dma = rows >= DFS_GATE_DMA_ROWS && d % kKB == 0;
+    // one workgroup per CU; at least two k steps per split (eight on the DMA ring)
+    const int64_t items = p.dma ? cdiv(rows, kDmaBM) * 2 : cdiv(rows, kTileM);
+    p.row_tiles = p.dma ? 0 : kTileM / 16;
+    int64_t splits = cdiv(kTargetWG, items);
+    const int64_t min_steps = p.dma ? 8 : 2;
+    const int64_t max_splits = KB / min_steps > 1 ? KB / min_steps : 1;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     const int64_t kb_per = cdiv(KB, splits);
@@ -307,9 +383,16 @@ hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W
   if (p.bf16) {
     const uint16_t* Wp = reinterpret_cast<const uint16_t*>(wsb + p.packed_off);
     const uint16_t* H = static_cast<const uint16_t*>(hidden);
-    const dim3 grid((unsigned)(cdiv(p.rows, kTileM) * p.splits));
-    gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
-                                                         partial, out_gate);
+    if (p.dma) {
+      const int mtiles = (int)cdiv(p.rows, kDmaBM);
+      const int per_xcd = (int)cdiv((int64_t)p.splits * mtiles * 2, 8);
+      gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd)), kThreads, 0, stream>>>(
+          H, Wp, p.rows, p.d, mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate);
+    } else {
+      const dim3 grid((unsigned)(cdiv(p.rows, kTileM) * p.splits));
+      gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
+                                                           partial, out_gate);
+    }
   } else {
     const dim3 grid((unsigned)cdiv(p.rows, kF32Rows), (unsigned)p.splits);
     gate_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(hidden),

@@ -13,8 +13,9 @@
 // equals the top-16 pass run on those logits, bit for bit.
 //
 // Tiles (LDS-DMA mainloop of mfma_big.h): 128 x 128 (four waves of 64 x 64, two
-// workgroups per CU) below 2048 rows, 256 x 256 (four waves of 128 x 128, one per
-// CU) from there.  For at most 32 rows the product (16 x 256 register-staged tiles,
+// workgroups per CU, a double buffer of 64 k per step: whole 128-byte lines) below
+// 2048 rows, 256 x 256 (four waves of 128 x 128, one per CU, a four-stage ring of
+// 32 k per step: a double buffer of 64 k leaves too little in flight) from there.  For at most 32 rows the product (16 x 256 register-staged tiles,
 // mfma_tile.h: the pass streams W_lm once and the matrix cores idle) is written to
 // the workspace and the top-16 pass runs over it, which is faster there.
 // Workgroups are numbered so that each XCD runs a group of row tiles x stripes at a
@@ -46,6 +47,22 @@ constexpr int kThreads = tile::kThreads;
 #ifndef DFS_LM_DEPTH
 #define DFS_LM_DEPTH 2
 #endif
+// ring stages and k per step of the 256 x 256 and 128 x 128 tiles
+#ifndef DFS_LM_BIG_STAGES
+#define DFS_LM_BIG_STAGES 4
+#endif
+#ifndef DFS_LM_BIG_KK
+#define DFS_LM_BIG_KK 32
+#endif
+#ifndef DFS_LM_MID_STAGES
+#define DFS_LM_MID_STAGES 2
+#endif
+#ifndef DFS_LM_MID_KK
+#define DFS_LM_MID_KK 64
+#endif
+using BigCfg = big::Cfg<8, 8, DFS_LM_BIG_STAGES, DFS_LM_BIG_KK>;
+using MidCfg = big::Cfg<4, 4, DFS_LM_MID_STAGES, DFS_LM_MID_KK>;
+constexpr int kMidWG = MidCfg::kLdsBytes <= 72 * 1024 ? 2 : 1;  // workgroups per CU the LDS allows
 
 struct Grid {
   int64_t rows, V, d;
@@ -148,13 +165,13 @@ __device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int ti
 // mfma_big.h (TM = TN = 4: 128 x 128, two workgroups per CU; 8: 256 x 256, one),
 // each tile folded into the stripe's row lists.  cand: the pending candidates,
 // [rows, nstripes, g.cand_cap] keys.
-template <int TM, int TN, int kMinWG>
+template <class C, int kMinWG>
 __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const uint16_t* __restrict__ h,
                                                                            const uint16_t* __restrict__ W,
                                                                            Grid g,
                                                                            uint64_t* __restrict__ partial,
                                                                            uint64_t* __restrict__ cand) {
-  using C = big::Cfg<TM, TN>;
+  constexpr int TM = C::TM, TN = C::TN;
   constexpr int BM = C::BM, BN = C::BN;
   __shared__ __attribute__((aligned(1024))) char lds[C::kLdsBytes];
   __shared__ uint64_t s_thr[BM];
@@ -172,8 +189,8 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const
   }
   const int64_t row_stride = (int64_t)g.nstripes * kK;
   uint64_t* plist = partial + (int64_t)stripe * kK;
-  const big::rsrc_t ra = big::rows_rsrc(h + m0 * g.d, tile_rows, g.d);
-  const int KS = (int)(g.d / big::kK);
+  const big::Operand ra = big::rows_operand(h + m0 * g.d, tile_rows, g.d, C::KK);
+  const int KS = (int)(g.d / C::KK);
   const int64_t t0 = (int64_t)stripe * g.tps;
   const int64_t t1 = t0 + g.tps < g.ntiles ? t0 + g.tps : g.ntiles;
   auto cand_row = [&](int lr) { return cand + ((m0 + lr) * g.nstripes + stripe) * g.cand_cap; };
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const
     const int64_t ncols = g.V - n0 < BN ? g.V - n0 : BN;
     typename C::Acc acc;
     C::zero(acc);
-    big::mma<C>(ra, big::rows_rsrc(W + n0 * g.d, ncols, g.d), g.d, 0, KS, lds, acc);
+    big::mma<C>(ra, big::rows_operand(W + n0 * g.d, ncols, g.d, C::KK), 0, KS, lds, acc);
     fold_tile<TM, TN, 2>(acc.v, tile_rows, n0, ncols, nt_ + 1 == t1, s_thr, s_cnt, s_has, cand_row, plist,
                          m0, row_stride);
   }
@@ -225,12 +242,12 @@ __global__ __launch_bounds__(kThreads, (TM * TN > 16 ? 1 : 2)) void lmhead_logit
     }
 }
 
-template <int TM, int TN, int kMinWG>
+template <class C, int kMinWG>
 __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_logits_dma_kernel(const uint16_t* __restrict__ h,
                                                                              const uint16_t* __restrict__ W,
                                                                              int64_t rows, int64_t V, int64_t d,
                                                                              int64_t ntiles, float* __restrict__ U) {
-  using C = big::Cfg<TM, TN>;
+  constexpr int TM = C::TM, TN = C::TN;
   __shared__ __attribute__((aligned(1024))) char lds[C::kLdsBytes];
   const int64_t nt_ = (int64_t)blockIdx.x % ntiles;
   const int64_t m0 = (int64_t)blockIdx.x / ntiles * C::BM;
@@ -243,8 +260,8 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_logits_dma_kernel(con
   const int64_t ncols = V - n0 < C::BN ? V - n0 : C::BN;
   typename C::Acc acc;
   C::zero(acc);
-  big::mma<C>(big::rows_rsrc(h + m0 * d, tile_rows, d), big::rows_rsrc(W + n0 * d, ncols, d), d, 0,
-              (int)(d / big::kK), lds, acc);
+  big::mma<C>(big::rows_operand(h + m0 * d, tile_rows, d, C::KK), big::rows_operand(W + n0 * d, ncols, d, C::KK),
+              0, (int)(d / C::KK), lds, acc);
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -338,13 +355,13 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows
   const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
   switch (tile_kind(rows)) {  // (few rows took the two-pass way above)
     case kMidTile:
-      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
+      lmhead_topk_dma_kernel<MidCfg, kMidWG><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
       break;
     default:
 #if DFS_LM_BIG_TILE
-      lmhead_topk_dma_kernel<8, 8, 1><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
+      lmhead_topk_dma_kernel<BigCfg, 1><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
 #else
-      lmhead_topk_dma_kernel<4, 4, 2><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
+      lmhead_topk_dma_kernel<MidCfg, kMidWG><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
 #endif
   }
   hipError_t e = hipGetLastError();
@@ -365,18 +382,18 @@ hipError_t launch_lmhead_logits(const void* hidden, const void* W_lm, int64_t ro
     }
     case kMidTile: {
       const int64_t nt = cdiv(V, 128);
-      lmhead_logits_dma_kernel<4, 4, 2><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
+      lmhead_logits_dma_kernel<MidCfg, kMidWG><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
           hp, wp, rows, V, d, nt, out);
       break;
     }
     default: {
 #if DFS_LM_BIG_TILE
       const int64_t nt = cdiv(V, 256);
-      lmhead_logits_dma_kernel<8, 8, 1><<<dim3((unsigned)(cdiv(rows, 256) * nt)), kThreads, 0, stream>>>(
+      lmhead_logits_dma_kernel<BigCfg, 1><<<dim3((unsigned)(cdiv(rows, 256) * nt)), kThreads, 0, stream>>>(
           hp, wp, rows, V, d, nt, out);
 #else
       const int64_t nt = cdiv(V, 128);
-      lmhead_logits_dma_kernel<4, 4, 2><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
+      lmhead_logits_dma_kernel<MidCfg, kMidWG><<<dim3((unsigned)(cdiv(rows, 128) * nt)), kThreads, 0, stream>>>(
           hp, wp, rows, V, d, nt, out);
 #endif
     }
