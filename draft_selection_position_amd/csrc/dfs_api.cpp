@@ -144,14 +144,16 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   float* cand_val = reinterpret_cast<float*>(w + l.cand_val_off);
   float* gate = reinterpret_cast<float*>(w + l.gate_off);
   // One stream, in order: the top-16 pass (the W_h packing slabs ride in its
-  // tail), the gate GEMM, the gate finish when the K split is wider than the pair
-  // kernel adds up itself, then pair scores and the walk in one kernel.
+  // tail), the gate GEMM (with the merge of split rows' top-16 lists riding along),
+  // the gate finish when the K split is wider than the pair kernel adds up itself,
+  // then pair scores and the walk in one kernel.
   char* gws = w + l.gate_ws_off;
   const PackJob job = gate_pack_job(l.gate, W_h, gws);
   hipError_t e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
-                             w + l.topk_ws_off, stream, &job);
+                             w + l.topk_ws_off, stream, &job, false);
   if (e != hipSuccess) return DFS_E_HIP;
-  if ((e = launch_gate_gemm(l.gate, hidden, W_h, gate, gws, stream)) != hipSuccess) return DFS_E_HIP;
+  const MergeJob mj = topk_merge_job(l.topk, w + l.topk_ws_off, cand_idx, cand_val);
+  if ((e = launch_gate_gemm(l.gate, hidden, W_h, gate, gws, stream, &mj)) != hipSuccess) return DFS_E_HIP;
   GateSrc gs{gate, 1, 0};
   if (l.gate.splits > 1) {
     if (l.gate.splits <= pair_max_gate_splits()) {

@@ -31,9 +31,24 @@ struct TopkPlan {
 };
 TopkPlan plan_topk(int64_t rows, int64_t V, int esize);
 // `pack` (may be null): W_h packing slabs run as extra workgroups of the same launch.
+// merge false (rows split, parts > 1): the partial lists are left in ws for a merge job
+// placed elsewhere (topk_merge_job), and out_idx / out_val are not written.
 hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
                        float* out_val, void* ws, hipStream_t stream,
-                       const PackJob* pack = nullptr);
+                       const PackJob* pack = nullptr, bool merge = true);
+
+// Merge of split rows' partial lists as extra workgroups of a later launch.
+struct MergeJob {
+  const uint64_t* partial;  // [rows, parts, 16]
+  int parts;                // 0: nothing to merge
+  int64_t rows;
+  int32_t* out_idx;
+  float* out_val;
+};
+inline MergeJob topk_merge_job(const TopkPlan& p, const void* ws, int32_t* out_idx, float* out_val) {
+  if (p.parts <= 1) return MergeJob{nullptr, 0, 0, nullptr, nullptr};
+  return MergeJob{static_cast<const uint64_t*>(ws), p.parts, p.rows, out_idx, out_val};
+}
 
 // Merge of per-row partial top-16 lists [rows, parts, 16] (64-bit keys, 0 = empty).
 hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, int32_t* out_idx,
@@ -60,8 +75,11 @@ hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, f
 // leaves partial sums [splits, rows, 256] at gate_partials() and out_gate is only
 // written by the finish.
 PackJob gate_pack_job(const GatePlan& p, const void* W_h, void* ws);
+// `merge` (may be null or empty): the split rows' top-16 merge runs as extra
+// workgroups of the GEMM launch.
 hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W_h,
-                            float* out_gate, void* ws, hipStream_t stream);
+                            float* out_gate, void* ws, hipStream_t stream,
+                            const MergeJob* merge = nullptr);
 hipError_t launch_gate_finish(const GatePlan& p, float* out_gate, void* ws, hipStream_t stream);
 const float* gate_partials(const GatePlan& p, const void* ws);
 

@@ -19,6 +19,7 @@
 #include "dfs_internal.h"
 #include "gate_pack.h"
 #include "mfma_big.h"
+#include "topk_merge.h"
 
 namespace dfs {
 namespace {
@@ -69,11 +70,22 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
                                                                  int64_t rows, int64_t d,
                                                                  int64_t kchunk, int splits,
                                                                  float* __restrict__ partial,
-                                                                 float* __restrict__ out) {
+                                                                 float* __restrict__ out,
+                                                                 int gemm_blocks, MergeJob mj) {
   constexpr int kPitch = kKB + 16;  // bf16 per LDS row of the H tile (+32 bytes: fewest bank conflicts)
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kPitch];
   __shared__ __attribute__((aligned(16))) float sOut[kTileM][kOutPitch];
   const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= gemm_blocks) {  // a merge job: two rows, four waves each
+    __shared__ uint64_t s_merge[2][kMergeWaves * kK];
+    const int g = tid >> 8;
+    const int64_t row = 2 * (int64_t)(blockIdx.x - gemm_blocks) + g;
+    const bool live = row < mj.rows;
+    const int64_t rr = live ? row : 0;
+    merge_row_lists(mj.partial + rr * mj.parts * kK, mj.parts, live, (tid >> 6) & 3, tid & (kWave - 1),
+                    s_merge[g], mj.out_idx + rr * kK, mj.out_val + rr * kK);
+    return;
+  }
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int r = lane & 15;
@@ -250,11 +262,21 @@ __global__ __launch_bounds__(kThreads) void gate_f32_kernel(const float* __restr
                                                             int64_t rows, int64_t d,
                                                             int64_t kchunk, int splits,
                                                             float* __restrict__ partial,
-                                                            float* __restrict__ out) {
+                                                            float* __restrict__ out, int mtiles,
+                                                            MergeJob mj) {
   __shared__ float sH[kF32Rows][kF32KBlock];
   const int n = threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.x * kF32Rows;
-  const int s = blockIdx.y;
+  const int gemm_blocks = mtiles * splits;
+  if ((int)blockIdx.x >= gemm_blocks) {  // a merge job: one row
+    static_assert(kThreads == kMergeWaves * kWave, "one row per workgroup");
+    __shared__ uint64_t s_merge[kMergeWaves * kK];
+    const int64_t row = blockIdx.x - gemm_blocks;
+    merge_row_lists(mj.partial + row * mj.parts * kK, mj.parts, true, n >> 6, n & (kWave - 1), s_merge,
+                    mj.out_idx + row * kK, mj.out_val + row * kK);
+    return;
+  }
+  const int64_t m0 = (int64_t)(blockIdx.x % mtiles) * kF32Rows;
+  const int s = (int)(blockIdx.x / mtiles);
   const int64_t k0 = (int64_t)s * kchunk;
   const int64_t k1 = k0 + kchunk < d ? k0 + kchunk : d;
   float acc[kF32Rows];
@@ -377,7 +399,8 @@ const float* gate_partials(const GatePlan& p, const void* ws) {
 }
 
 hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W_h,
-                            float* out_gate, void* ws, hipStream_t stream) {
+                            float* out_gate, void* ws, hipStream_t stream, const MergeJob* merge) {
+  const MergeJob mj = merge && merge->parts > 1 ? *merge : MergeJob{nullptr, 0, 0, nullptr, nullptr};
   char* wsb = static_cast<char*>(ws);
   float* partial = p.splits > 1 ? reinterpret_cast<float*>(wsb + p.partial_off) : nullptr;
   if (p.bf16) {
@@ -388,16 +411,23 @@ hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W
       const int per_xcd = (int)cdiv((int64_t)p.splits * mtiles * 2, 8);
       gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd)), kThreads, 0, stream>>>(
           H, Wp, p.rows, p.d, mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate);
+      if (mj.parts > 1) {  // (many rows: the top-16 pass does not split them, kept for completeness)
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_topk_merge(mj.partial, mj.rows, mj.parts, mj.out_idx, mj.out_val, stream);
+      }
     } else {
-      const dim3 grid((unsigned)(cdiv(p.rows, kTileM) * p.splits));
+      const int gemm_blocks = (int)(cdiv(p.rows, kTileM) * p.splits);
+      const dim3 grid((unsigned)(gemm_blocks + cdiv(mj.rows, 2)));
       gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
-                                                           partial, out_gate);
+                                                           partial, out_gate, gemm_blocks, mj);
     }
   } else {
-    const dim3 grid((unsigned)cdiv(p.rows, kF32Rows), (unsigned)p.splits);
+    const int mtiles = (int)cdiv(p.rows, kF32Rows);
+    const dim3 grid((unsigned)((int64_t)mtiles * p.splits + mj.rows));
     gate_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(hidden),
                                                    static_cast<const float*>(W_h), p.rows, p.d,
-                                                   p.kchunk, p.splits, partial, out_gate);
+                                                   p.kchunk, p.splits, partial, out_gate, mtiles, mj);
   }
   return hipGetLastError();
 }

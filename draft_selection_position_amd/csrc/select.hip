@@ -204,7 +204,10 @@ __device__ __forceinline__ void draft_q(const float (*sS)[kK][kK], const WalkTab
 
 // Gate splits the pair kernel adds up itself (more are finished by a kernel of
 // their own first).
-constexpr int kMaxGateSplits = 4;
+#ifndef DFS_PAIR_GATE_SPLITS
+#define DFS_PAIR_GATE_SPLITS 4
+#endif
+constexpr int kMaxGateSplits = DFS_PAIR_GATE_SPLITS;
 
 // This lane's 16-byte piece [4 lane, + 4) of the gate row `row`: the finished gate
 // (splits == 1), or the K-split partial sums [splits, rows, 256] (row stride

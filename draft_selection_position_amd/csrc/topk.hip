@@ -19,6 +19,7 @@
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "gate_pack.h"
+#include "topk_merge.h"
 
 namespace dfs {
 namespace {
@@ -301,34 +302,11 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
                                                               int parts,
                                                               int32_t* __restrict__ out_idx,
                                                               float* __restrict__ out_val) {
+  static_assert(kWaves == kMergeWaves, "one row per workgroup");
   __shared__ uint64_t s_list[kWaves * kK];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int64_t row = blockIdx.x;
-  const uint64_t* src = partial + row * parts * kK;
-  uint64_t list = 0;
-  // Each sort takes the wave's list plus up to three more lists (48 keys).
-  for (int p0 = wave * 3; p0 < parts; p0 += kWaves * 3) {
-    uint64_t x = 0;
-    if (lane < kK) {
-      x = list;
-    } else {
-      const int p = p0 + (lane - kK) / kK;
-      if (p < parts) x = src[(int64_t)p * kK + (lane & (kK - 1))];
-    }
-    x = wave_sort_desc(x, lane);
-    list = lane < kK ? x : 0;
-  }
-  if (lane < kK) s_list[wave * kK + lane] = list;
-  __syncthreads();
-  if (wave == 0) {
-    uint64_t x = wave_sort_desc(s_list[lane], lane);
-    if (lane < kK) {
-      out_idx[row * kK + lane] = (int32_t)key_index(x);
-      out_val[row * kK + lane] = key_value(x);
-    }
-  }
+  merge_row_lists(partial + row * parts * kK, parts, true, threadIdx.x / kWave, threadIdx.x & (kWave - 1),
+                  s_list, out_idx + row * kK, out_val + row * kK);
 }
 
 }  // namespace
@@ -358,7 +336,7 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int esize) {
 }
 
 hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
-                       float* out_val, void* ws, hipStream_t stream, const PackJob* pack) {
+                       float* out_val, void* ws, hipStream_t stream, const PackJob* pack, bool merge) {
   static_assert(kThreads == kPackThreads, "packing jobs run on top-16 workgroups");
   uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
   const int64_t ntopk = p.rows * p.parts;
@@ -371,7 +349,7 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
     topk_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk,
                                                             partial, out_idx, out_val, ntopk, job);
   }
-  if (p.parts > 1) {
+  if (p.parts > 1 && merge) {
     topk_merge_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.parts, out_idx,
                                                                         out_val);
   }
