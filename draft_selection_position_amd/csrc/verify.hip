@@ -30,7 +30,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 2;           // 16-byte vectors per lane per step (two steps in flight)
+#ifndef DFS_LSE_UNROLL
+#define DFS_LSE_UNROLL 2
+#endif
+#ifndef DFS_LSE_SEGS_PER_WAVE
+#define DFS_LSE_SEGS_PER_WAVE 8  // segments a wave streams back to back (1, 2, 4, 16, 32 measured slower)
+#endif
+constexpr int kUnroll = DFS_LSE_UNROLL;  // 16-byte vectors per lane per step (two steps in flight)
 constexpr int kSeg = 4096;           // tokens per segment of a target row
 constexpr int kMaxSeg = 1024;        // segments per row the draw holds in LDS (V <= 2^22)
 constexpr int kMaxL = 16;            // longest block
@@ -86,25 +92,30 @@ template <bool kBf16, int N>
 __device__ __forceinline__ void ms_add_vecs(MS& a, const uint4* d, float scale) {
   constexpr int PV = kBf16 ? 8 : 4;
   float x[N][PV];
+#pragma unroll
+  for (int u = 0; u < N; ++u) unpack_vec<kBf16>(d[u], x[u]);
   float zm = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
-    unpack_vec<kBf16>(d[u], x[u]);
+  for (int u = 0; u < N; ++u)
 #pragma unroll
     for (int e = 0; e < PV; ++e) zm = fmaxf(zm, x[u][e]);
-  }
   const float vm = zm * scale;
-  if (vm > a.m) {  // a new maximum (rare once a row is under way): rescale the sum
+  // A new maximum is rare once a row is under way: the rescale (an exponential and
+  // an fp64 product) sits behind a branch that a wave skips when none of its lanes
+  // needs it, instead of running, masked, on every step (the empty volatile asm keeps
+  // the compiler from turning the branch into selects).
+  if (vm > a.m) {
+    __asm__ volatile("");
     a.s = a.m == -INFINITY ? 0.0 : a.s * (double)fast_exp2(a.m - vm);
     a.m = vm;
   }
   if (a.m == -INFINITY) return;
   const float nm = -a.m;
-  float vs = 0.0f;
+  float vs = fast_exp2(fmaf(x[0][0], scale, nm));  // (the sum starts at its first term: no 0 + x)
 #pragma unroll
   for (int u = 0; u < N; ++u)
 #pragma unroll
-    for (int e = 0; e < PV; ++e) vs += fast_exp2(fmaf(x[u][e], scale, nm));
+    for (int e = (u == 0 ? 1 : 0); e < PV; ++e) vs += fast_exp2(fmaf(x[u][e], scale, nm));
   a.s += (double)vs;
 }
 
@@ -515,9 +526,9 @@ VerifyPlan plan_verify(int64_t batch, int64_t L, int64_t V, int esize) {
   const int64_t rows = batch * (L + 1);
   // segments per row (at most one more than the aligned middle needs)
   p.nseg = cdiv(V, kSeg) + 1;
-  // workgroups per row: about two segments per wave, so that the launch is many
-  // short workgroups (a ragged last round of the chip's slots costs little)
-  const int64_t parts = cdiv(p.nseg, 2 * kWaves);
+  // workgroups per row: about eight segments per wave (32 KB of bf16 streamed back to
+  // back); two per wave, many short workgroups, was 5% slower at 256 x 17 x 151936
+  const int64_t parts = cdiv(p.nseg, DFS_LSE_SEGS_PER_WAVE * kWaves);
   p.parts = (int)parts;
   p.ws_bytes = align_up((size_t)rows * p.nseg * sizeof(double2), 256);
   return p;
