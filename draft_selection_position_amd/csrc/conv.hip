@@ -24,6 +24,7 @@
 // convolution of those rows over the 64 channels the columns serve.
 #include "dfs_device.h"
 #include "dfs_internal.h"
+#include "mfma_big.h"
 #include "mfma_tile.h"
 
 namespace dfs {
@@ -41,7 +42,16 @@ constexpr int kPitchC = kTileN + 4;           // fp32 per LDS row of the correct
 #ifndef DFS_CONV_XCD
 #define DFS_CONV_XCD 1
 #endif
-static_assert(kTileM * kPitchC * 4 <= CT::kLdsBytes, "the correction tile reuses the operand stages");
+// The product's mainloop: the LDS-DMA double buffer of 64 k per step (mfma_big.h),
+// or (DFS_CONV_BIG 0) the register-staged tile of mfma_tile.h.  Both add the k
+// chunks in the same order.
+#ifndef DFS_CONV_BIG
+#define DFS_CONV_BIG 1
+#endif
+using ConvCfg = big::Cfg<4, 4, 2, 64>;
+static_assert(ConvCfg::BM == kTileM && ConvCfg::BN == kTileN && ConvCfg::KK == kKStep, "same tile");
+constexpr int kMainLds = DFS_CONV_BIG ? ConvCfg::kLdsBytes : CT::kLdsBytes;
+constexpr int kConvLds = kMainLds > kTileM * kPitchC * 4 ? kMainLds : kTileM * kPitchC * 4;
 
 // fp32 -> bf16 bits, round to nearest, ties to even (finite and infinite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -76,7 +86,7 @@ __global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_ke
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ Wc, int64_t rows, int L,
     int64_t D, int ntiles_n, int64_t mtiles, int splits, int ks_per_split,
     float* __restrict__ partial, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[CT::kLdsBytes / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kConvLds / 2];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -105,10 +115,17 @@ __global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_ke
   const int ks0 = split * ks_per_split;
   const int ks1 = ks0 + ks_per_split < KS ? ks0 + ks_per_split : KS;
 
+#if DFS_CONV_BIG
+  ConvCfg::Acc acc;
+  ConvCfg::zero(acc);
+  big::mma<ConvCfg>(big::rows_operand(x + m0 * D, tile_rows, D, kKStep),
+                    big::rows_operand(Wc + n0 * D, ncols, D, kKStep), ks0, ks1, reinterpret_cast<char*>(lds), acc);
+#else
   CT::Acc acc;
   tile::zero<2, 2, 4, 4>(acc);
   tile::mma<2, 2, 4, 4, DFS_CONV_DEPTH>(tile::rows_rsrc(x + m0 * D, tile_rows, D),
                                         tile::rows_rsrc(Wc + n0 * D, ncols, D), D, ks0, ks1, lds, acc);
+#endif
 
   float* sC = reinterpret_cast<float*>(lds);  // [kTileM][kPitchC], after the loop's last barrier
   const int wm = wave >> 1, wn = wave & 1;
