@@ -172,31 +172,62 @@ __global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_ke
 }
 
 // The convolution after a K-split correction: partial sums added in split order.
-__global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xprev,
-    const uint16_t* __restrict__ base, const float* __restrict__ partial, int splits, int64_t rows,
-    int L, int64_t D, uint16_t* __restrict__ y) {
-  const int64_t nvec = D / 8;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= rows * nvec) return;
-  const int64_t m = i / nvec;
-  const int64_t ch = 8 * (i - m * nvec);
-  const int64_t b = m / L;
-  const int t = (int)(m - b * L);
-  const int64_t col = m * nvec + 2 * (ch / 16);
-  float c0 = 0.0f, c1 = 0.0f;
+// One thread per 16-byte piece (8 channels) of kR consecutive positions of one
+// sequence: each position's x piece is read once and serves as the next position's
+// predecessor from registers (with kR = 1 the predecessor is read again), and the
+// base kernel's two pieces are read once.  Per position, the group's two correction
+// columns are read for every split and added in split order.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_sum(const float* pc, int64_t sstride, int splits, float& c0, float& c1) {
+  c0 = 0.0f;
+  c1 = 0.0f;
   for (int s = 0; s < splits; ++s) {
-    const float2 v = *reinterpret_cast<const float2*>(partial + s * rows * nvec + col);
+    const f32x2 v = *reinterpret_cast<const f32x2*>(pc + s * sstride);
     c0 += v.x;
     c1 += v.y;
   }
-  const uint4 xv = *reinterpret_cast<const uint4*>(x + m * D + ch);
-  const uint4 pv = t > 0 ? *reinterpret_cast<const uint4*>(x + (m - 1) * D + ch)
-                         : *reinterpret_cast<const uint4*>(xprev + b * D + ch);
+}
+
+template <typename Idx, int kR>
+__global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xprev,
+    const uint16_t* __restrict__ base, const float* __restrict__ partial, int splits, int64_t batch,
+    int L, int64_t D, uint16_t* __restrict__ y) {
+  const Idx P = (Idx)(D / 8);                 // pieces per row
+  const Idx runs = (Idx)((L + kR - 1) / kR);  // runs of kR positions per sequence
+  const Idx j = (Idx)blockIdx.x * kThreads + threadIdx.x;
+  if ((int64_t)j >= batch * (int64_t)runs * (int64_t)P) return;
+  const Idx run = j / P;                      // (sequence, run), pieces fastest
+  const int64_t ch = 8 * (int64_t)(j - run * P);
+  const Idx b = run / runs;
+  const int t0 = (int)(run - b * runs) * kR;
+  const int t1 = t0 + kR < L ? t0 + kR : L;
+  const int64_t rows = batch * (int64_t)L;
+  const int64_t nvec = D / 8;
+  const int64_t sstride = rows * nvec;
   const uint4 b0 = *reinterpret_cast<const uint4*>(base + ch);
   const uint4 b1 = *reinterpret_cast<const uint4*>(base + D + ch);
-  *reinterpret_cast<uint4*>(y + m * D + ch) = conv8(xv, pv, b0, b1, c0, c1);
+  const int64_t m0 = (int64_t)b * L + t0;
+  uint4 pv = t0 > 0 ? *reinterpret_cast<const uint4*>(x + (m0 - 1) * D + ch)
+                    : *reinterpret_cast<const uint4*>(xprev + (int64_t)b * D + ch);
+  for (int t = t0; t < t1; ++t) {
+    const int64_t m = (int64_t)b * L + t;
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + m * D + ch);
+    float c0, c1;
+    split_sum(partial + m * nvec + 2 * (ch / 16), sstride, splits, c0, c1);
+    *reinterpret_cast<uint4*>(y + m * D + ch) = conv8(xv, pv, b0, b1, c0, c1);
+    pv = xv;
+  }
 }
+
+// Positions per thread of the split epilogue: runs of 4 while that leaves enough
+// threads to fill the chip, else one position per thread.
+#ifndef DFS_CONV_EPI_RUN
+#define DFS_CONV_EPI_RUN 4
+#endif
+#ifndef DFS_CONV_EPI_MIN_THREADS
+#define DFS_CONV_EPI_MIN_THREADS (256 * 1024)
+#endif
 
 // ---------------------------------------------------------------- fp32 path
 constexpr int kF32Rows = 8;  // rows of a workgroup
@@ -330,10 +361,26 @@ hipError_t launch_conv2(const void* x, const void* x_prev, const void* base, con
         static_cast<const uint16_t*>(base), static_cast<const uint16_t*>(W_c), rows, (int)L, D, ntn,
         mtiles, splits, kps, static_cast<float*>(ws), static_cast<uint16_t*>(y));
     if (splits > 1) {
-      conv2_split_epilogue_kernel<<<dim3((unsigned)cdiv(rows * (D / 8), kThreads)), kThreads, 0, stream>>>(
-          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x_prev),
-          static_cast<const uint16_t*>(base), static_cast<const float*>(ws), splits, rows, (int)L, D,
-          static_cast<uint16_t*>(y));
+      const int64_t runs4 = cdiv(L, DFS_CONV_EPI_RUN);
+      const bool long_runs = DFS_CONV_EPI_RUN > 1 && batch * runs4 * (D / 8) >= DFS_CONV_EPI_MIN_THREADS;
+      const int64_t jobs = batch * (long_runs ? runs4 : L) * (D / 8);
+      const dim3 eg((unsigned)cdiv(jobs, kThreads));
+      const uint16_t* xp = static_cast<const uint16_t*>(x);
+      const uint16_t* pp = static_cast<const uint16_t*>(x_prev);
+      const uint16_t* bp = static_cast<const uint16_t*>(base);
+      const float* sp = static_cast<const float*>(ws);
+      uint16_t* yp = static_cast<uint16_t*>(y);
+      if (jobs < ((int64_t)1 << 31)) {
+        if (long_runs)
+          conv2_split_epilogue_kernel<uint32_t, DFS_CONV_EPI_RUN><<<eg, kThreads, 0, stream>>>(xp, pp, bp, sp, splits, batch, (int)L, D, yp);
+        else
+          conv2_split_epilogue_kernel<uint32_t, 1><<<eg, kThreads, 0, stream>>>(xp, pp, bp, sp, splits, batch, (int)L, D, yp);
+      } else {
+        if (long_runs)
+          conv2_split_epilogue_kernel<uint64_t, DFS_CONV_EPI_RUN><<<eg, kThreads, 0, stream>>>(xp, pp, bp, sp, splits, batch, (int)L, D, yp);
+        else
+          conv2_split_epilogue_kernel<uint64_t, 1><<<eg, kThreads, 0, stream>>>(xp, pp, bp, sp, splits, batch, (int)L, D, yp);
+      }
     }
   } else {
     conv2_f32_kernel<<<dim3((unsigned)(D / 8 / kF32Cols * cdiv(rows, kF32Rows))), kThreads, 0, stream>>>(

@@ -63,6 +63,8 @@ CASES = [
     (3, 5, 256), (37, 16, 1280), (5, 7, 768), (2, 16, 5120), (1, 1, 512), (9, 3, 4096),
     # enough rows for unsplit 128 x 64 tiles, with a 32-column last tile
     (688, 16, 1280),
+    # a K split whose epilogue walks runs of four positions per thread, L not a multiple of 4
+    (4096, 7, 1024),
 ]
 
 
