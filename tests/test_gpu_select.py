@@ -157,3 +157,25 @@ def test_best_path_full_size(name, full_workload):
         path, scores, slots, margins = oracle.viterbi(res.pair, res.cand_idx)
         res.path, res.scores, res.slots, res.margins = path, scores, slots, margins
         check_path(vp[i], vs[i], res, "viterbi", b=int(inp.seq_ids[i]))
+
+
+def test_select_many_rows_unsplit_gate():
+    # 16384 rows: the top-16 pass keeps every row whole, and the gate GEMM's 128 x 128 tiles
+    # fill the chip without a K split (the sigmoid in its own epilogue); the fused call must
+    # equal the step chain bit for bit and the oracle on sampled sequences
+    import draft_selection_position_amd as dfs
+
+    cfg = variant("throughput", emb_std=0.3, batch=1024, V=4096, d=256)
+    inp = make(cfg)
+    dev = upload(inp)
+    print(f"select many rows: batch {cfg.batch} L {cfg.L} V {cfg.V} d {cfg.d}", flush=True)
+    path, scores = _select(dev, cfg)
+    idx, val = dfs.topk(dev["logits"])
+    g = dfs.gate(dev["hidden"], dev["W_h"])
+    pair = dfs.pair_scores(idx, val, dev["prev_token"], g, dev["A"], dev["B"])
+    p2, s2 = dfs.walk(pair, idx, cfg.walk, cfg.temperature, cfg.walk_seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(path, p2.cpu().numpy())
+    assert np.array_equal(scores, s2.cpu().numpy())
+    seqs = np.unique(np.r_[0, cfg.batch - 1, np.random.default_rng(4).choice(cfg.batch, 22, replace=False)])
+    _check(inp, path, scores, seqs)
