@@ -12,9 +12,9 @@
 //     k_{t,tap}[ch] = base[tap, ch] + c_t[2 (ch / 16) + tap].
 //
 // bf16 path: the correction is a [rows, D] x [D, D/8] product on the matrix cores
-// (mfma_tile.h: 128 x 128 tiles staged through LDS); a workgroup's epilogue applies
-// the convolution to exactly its 128 rows and 1024 channels, so the correction
-// never leaves the chip.  W_c is K-contiguous, the operand order the tile wants: no
+// (mfma_big.h: 128 x 128 tiles, operands loaded straight into LDS); a workgroup's
+// epilogue applies the convolution to exactly its 128 rows and 1024 channels, so the
+// correction never leaves the chip.  W_c is K-contiguous, the operand order the tile wants: no
 // repacking.  Shapes too small to fill the chip split K; an elementwise kernel then
 // adds the split partial sums in split order and applies the convolution (a
 // device-wide fence per workgroup to let the last split do it in place writes

@@ -217,8 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* _
   const int ks0 = s * kps;
   const int ks1 = ks0 + kps < KB ? ks0 + kps : KB;
   const big::Operand a = big::rows_operand(H + m0 * d, tile_rows, d);
-  const big::Operand b{big::span_rsrc(Wp + nh * kDmaBN * kKB, (int64_t)KB * kE * kKB * 2 - nh * kDmaBN * kKB * 2),
-                       (uint32_t)(kKB * 2), (uint32_t)(kE * kKB * 2)};
+  const big::Operand b = big::make_operand(Wp + nh * kDmaBN * kKB, (int64_t)KB * kE * kKB * 2 - nh * kDmaBN * kKB * 2,
+                                           (uint32_t)(kKB * 2), (uint32_t)(kE * kKB * 2));
   GC::Acc acc;
   GC::zero(acc);
   big::mma<GC>(a, b, ks0, ks1, lds, acc);

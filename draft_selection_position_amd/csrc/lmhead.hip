@@ -15,9 +15,10 @@
 // Tiles (LDS-DMA mainloop of mfma_big.h): 128 x 128 (four waves of 64 x 64, two
 // workgroups per CU, a double buffer of 64 k per step: whole 128-byte lines) below
 // 2048 rows, 256 x 256 (four waves of 128 x 128, one per CU, a four-stage ring of
-// 32 k per step: a double buffer of 64 k leaves too little in flight) from there.  For at most 32 rows the product (16 x 256 register-staged tiles,
-// mfma_tile.h: the pass streams W_lm once and the matrix cores idle) is written to
-// the workspace and the top-16 pass runs over it, which is faster there.
+// 32 k per step: a double buffer of 64 k leaves too little in flight) from there.
+// For at most 32 rows the product (16 x 256 register-staged tiles, mfma_tile.h: the
+// pass streams W_lm once and the matrix cores idle) is written to the workspace and
+// the top-16 pass runs over it, which is faster there.
 // Workgroups are numbered so that each XCD runs a group of row tiles x stripes at a
 // time: the group's W_lm tiles and h rows are shared through the XCD's L2.
 

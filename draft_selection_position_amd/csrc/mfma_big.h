@@ -85,9 +85,13 @@ struct Operand {
   rsrc_t rsrc;
   uint32_t row_bytes, step_bytes;
 };
+__device__ __forceinline__ Operand make_operand(const void* p, int64_t bytes, uint32_t row_bytes,
+                                                uint32_t step_bytes) {
+  return Operand{span_rsrc(p, bytes), row_bytes, step_bytes};
+}
 // Row-major [nrows, K] bf16 starting at p, steps of kk.
 __device__ __forceinline__ Operand rows_operand(const uint16_t* p, int64_t nrows, int64_t K, int kk = kK) {
-  return Operand{span_rsrc(p, nrows * K * 2), (uint32_t)(K * 2), (uint32_t)(2 * kk)};
+  return make_operand(p, nrows * K * 2, (uint32_t)(K * 2), (uint32_t)(2 * kk));
 }
 
 // LDS slot of 16-byte chunk c of stage row `row`: XOR-swizzled so that the 16 rows a
@@ -272,6 +276,8 @@ __device__ __forceinline__ void mma(const Operand& a, const Operand& b, int ks0,
   wait_vmcnt<0>();
   __syncthreads();
 }
+
+
 
 }  // namespace big
 }  // namespace dfs
