@@ -9,11 +9,13 @@
 // V_MFMA_F32_16X16X32_BF16.  The MFMA wants every lane's operand to be 8
 // consecutive k values, but W_h is n-contiguous, so W_h is first repacked once per
 // call into [d/32][256][32] (gate_pack.h; 2.6 MB at d = 5120, stays in L2) and both
-// operands are then read straight from memory with 16-byte loads.  A workgroup
-// computes a 64-row x 256-column tile over one K split, each of its 8 waves 32
-// columns; row counts too small to fill the chip split K, and the partial sums
-// are added in split order (by the finish kernel here, or by the pair kernel
-// that reads the gate) before the sigmoid.
+// operands are then read straight from memory with 16-byte loads.  From 512 rows
+// (d a multiple of 32) the product runs on 128 x 128 LDS-DMA tiles (gate_dma_kernel,
+// below); for fewer rows a workgroup computes a 64-row x 256-column tile over one K
+// split, each of its 8 waves 32 columns.  Row counts too small to fill the chip split
+// K, and the partial sums are added in split order (by the finish kernel here, or by
+// the pair kernel that reads the gate) before the sigmoid.  Either GEMM launch can
+// carry the merge of split top-16 rows as extra workgroups (dfs_select).
 // fp32 path: plain FMA over a [8 rows x 256 columns] tile per workgroup.
 #include "dfs_device.h"
 #include "dfs_internal.h"
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
 #define DFS_GATE_STAGES 4
 #endif
 #ifndef DFS_GATE_DMA_ROWS
-#define DFS_GATE_DMA_ROWS 2048
+#define DFS_GATE_DMA_ROWS 512
 #endif
 using GC = big::Cfg<4, 4, DFS_GATE_STAGES>;
 constexpr int kDmaBM = GC::BM;                 // 128 rows
@@ -204,8 +206,16 @@ __global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* _
                                                                int64_t rows, int64_t d, int mtiles,
                                                                int splits, int kps, int per_xcd,
                                                                float* __restrict__ partial,
-                                                               float* __restrict__ out) {
+                                                               float* __restrict__ out, MergeJob mj) {
   __shared__ __attribute__((aligned(1024))) char lds[kDmaLds];
+  if (blockIdx.x >= 8u * (unsigned)per_xcd) {  // a merge job (split top-16 rows): one row
+    static_assert(kThreads == kMergeWaves * kWave, "one row per workgroup");
+    __shared__ uint64_t s_merge[kMergeWaves * kK];
+    const int64_t row = blockIdx.x - 8u * (unsigned)per_xcd;
+    merge_row_lists(mj.partial + row * mj.parts * kK, mj.parts, true, threadIdx.x >> 6,
+                    threadIdx.x & (kWave - 1), s_merge, mj.out_idx + row * kK, mj.out_val + row * kK);
+    return;
+  }
   const int64_t t = (int64_t)(blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
   if (t >= (int64_t)splits * mtiles * 2) return;
   const int nh = (int)(t & 1);
@@ -409,13 +419,8 @@ hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W
     if (p.dma) {
       const int mtiles = (int)cdiv(p.rows, kDmaBM);
       const int per_xcd = (int)cdiv((int64_t)p.splits * mtiles * 2, 8);
-      gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd)), kThreads, 0, stream>>>(
-          H, Wp, p.rows, p.d, mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate);
-      if (mj.parts > 1) {  // (many rows: the top-16 pass does not split them, kept for completeness)
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_topk_merge(mj.partial, mj.rows, mj.parts, mj.out_idx, mj.out_val, stream);
-      }
+      gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd + mj.rows)), kThreads, 0, stream>>>(
+          H, Wp, p.rows, p.d, mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate, mj);
     } else {
       const int gemm_blocks = (int)(cdiv(p.rows, kTileM) * p.splits);
       const dim3 grid((unsigned)(gemm_blocks + cdiv(mj.rows, 2)));

@@ -46,7 +46,7 @@ def test_gate_full_size_configs(cfg, full_workload):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-# from 2048 rows with d a multiple of 32 the bf16 gate runs on 128 x 128 LDS-DMA tiles: one K
+# from 512 rows with d a multiple of 32 the bf16 gate runs on 128 x 128 LDS-DMA tiles: one K
 # step (2049 x 256, unsplit), two (4100 x 64), ragged rows over 8 splits (2100 x 5120, finished
 # by its own kernel), 4 splits (4096 x 2048); 3000 x 1000 keeps the 64-row tiles (d % 32 != 0)
 @pytest.mark.parametrize("rows,d", [(1, 8), (37, 72), (16, 5120), (300, 1000), (2049, 256), (4100, 64),
