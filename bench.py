@@ -369,7 +369,10 @@ def main() -> int:
         del lg
         T = cfg.temperature if cfg.walk == "gumbel" else 1.0
         dargs = (dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])
-        dkw = dict(mode="gumbel", temperature=T, seed=cfg.walk_seed, draft=True)
+        sws = torch.empty(dfs.select_workspace_bytes(cfg.batch, cfg.L, cfg.V, cfg.d, dev["logits"].dtype,
+                                                     dev["hidden"].dtype, dev["A"].dtype),
+                          dtype=torch.uint8, device=logits2d.device)
+        dkw = dict(mode="gumbel", temperature=T, seed=cfg.walk_seed, draft=True, workspace=sws)
         vws = torch.empty(dfs.verify_workspace_bytes(cfg.batch, cfg.L, cfg.V, tgt.dtype), dtype=torch.uint8,
                           device=tgt.device)
         path_d, _, q_d, cand_d = dfs.select(*dargs, **dkw)
