@@ -64,6 +64,7 @@ VARIANTS = [
     dict(V=50000, batch=2, neg_inf_frac=0.9997, peak_kind="none"),  # rows with < 16 finite values
     dict(V=151936, batch=2, zipf_ids=True),  # peaks clustered at low ids
     dict(V=262144, batch=1, L=3),
+    dict(V=4190208, batch=1, L=2),  # rows of 8 MB (bf16), split into the most chunks
 ]
 
 

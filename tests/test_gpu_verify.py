@@ -90,26 +90,34 @@ def _verify_case(cfg, noise, T_target, seed):
              temperature=0.7), 1.0, 0.8),
     (variant("tiny", emb_std=0.3, batch=16, walk="gumbel", walk_seed=9), 0.5, 1.0),
     (variant("sampled", emb_std=0.3, batch=8, V=50000, d=256, L=5, walk_seed=10), 0.2, 1.3),
+    # the largest vocabulary the draw handles: 1023 segments of 4096 tokens per row
+    (variant("single_stream", emb_std=0.3, batch=3, V=4190208, d=64, L=4, walk="gumbel", walk_seed=11), 0.3, 1.0),
 ], ids=lambda x: getattr(x, "name", str(x)))
 def test_verify_matches_oracle(cfg, noise, T):
     acc, tok, path, cand, q, tgt = _verify_case(cfg, noise, T, seed=12345)
-    near = 0
+    near_acc = near_draw = 0
     for b in range(cfg.batch):
         v = oracle.verify.verify_block(tgt[b], path[b], cand[b], q[b].astype(np.float64), T, 12345, b)
         if v.accept_margin < NEAR_ACCEPT:
-            near += 1
+            near_acc += 1
             assert 0 <= acc[b] <= cfg.L and 0 <= tok[b] < cfg.V
             continue
         assert int(acc[b]) == v.accepted, (b, acc[b], v)
         if v.draw_margin < NEAR_DRAW:
             # near an interval edge: the GPU's token must still be one whose interval
             # lies within NEAR_DRAW of the draw (on the oracle's own sums)
-            near += 1
+            near_draw += 1
             assert _draw_within(tgt[b], cand[b], q[b], v.accepted, int(tok[b]), T, 12345, b, NEAR_DRAW)
             continue
         assert (int(acc[b]), int(tok[b])) == (v.accepted, v.token), (b, acc[b], tok[b], v)
-    print(f"verify {cfg.name}: accepted mean {acc.mean():.2f}, {near} near ties", flush=True)
-    assert near <= cfg.batch // 4
+    print(f"verify {cfg.name}: accepted mean {acc.mean():.2f}, {near_acc} accept and {near_draw} draw near ties",
+          flush=True)
+    if cfg.V < 1_000_000:
+        assert near_acc + near_draw <= cfg.batch // 4
+    else:
+        # with millions of tokens a token's interval is narrower than NEAR_DRAW of the mass,
+        # so nearly every draw is near an edge; each was checked to land within it above
+        assert near_acc <= cfg.batch // 4
 
 
 def test_verify_emitted_tokens_follow_the_target():
