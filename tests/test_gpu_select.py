@@ -179,3 +179,32 @@ def test_select_many_rows_unsplit_gate():
     assert np.array_equal(scores, s2.cpu().numpy())
     seqs = np.unique(np.r_[0, cfg.batch - 1, np.random.default_rng(4).choice(cfg.batch, 22, replace=False)])
     _check(inp, path, scores, seqs)
+
+
+@pytest.mark.parametrize("batch,d,splits", [(263, 1024, 4), (375, 768, 3), (512, 512, 2), (131, 256, 1)],
+                         ids=lambda v: str(v))
+def test_select_ragged_rows_each_gate_split(batch, d, splits):
+    # unsplit top-16 rows, row counts that are not a multiple of the gate's 128-row tiles,
+    # and each K split the pair kernel adds up itself (1 to 4): the fused call must equal
+    # the step chain bit for bit, and the oracle on sampled sequences
+    import draft_selection_position_amd as dfs
+
+    cfg = variant("throughput", emb_std=0.3, batch=batch, V=4096, d=d)
+    rows = cfg.batch * cfg.L
+    kb = d // 32
+    items = -(-rows // 128) * 2
+    s = min(max(-(-256 // items), 1), max(kb // 8, 1))
+    assert -(-kb // -(-kb // s)) == splits  # the gate plan's split count for this shape
+    inp = make(cfg)
+    dev = upload(inp)
+    print(f"select ragged rows: rows {rows} d {d} gate splits {splits}", flush=True)
+    path, scores = _select(dev, cfg)
+    idx, val = dfs.topk(dev["logits"])
+    g = dfs.gate(dev["hidden"], dev["W_h"])
+    pair = dfs.pair_scores(idx, val, dev["prev_token"], g, dev["A"], dev["B"])
+    p2, s2 = dfs.walk(pair, idx, cfg.walk, cfg.temperature, cfg.walk_seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(path, p2.cpu().numpy())
+    assert np.array_equal(scores, s2.cpu().numpy())
+    seqs = np.unique(np.r_[0, cfg.batch - 1, np.random.default_rng(6).choice(cfg.batch, 8, replace=False)])
+    _check(inp, path, scores, seqs)
