@@ -16,6 +16,8 @@
 // are merged at the end; rows split over several workgroups are merged by a
 // second kernel.  Every comparison is on exact integer keys, so the result does
 // not depend on the order in which elements are seen.
+#include <type_traits>
+
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "gate_pack.h"
@@ -256,7 +258,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
         dst[u] = load_vec(rsrc, vid * 16u);  // past the end: zeros, flagged invalid below
       }
     };
-    auto scan_iter = [&](const uint4* src, int64_t it) {
+    // kCheck false: every vector of the iteration lies inside the chunk (no range test)
+    auto scan_iter = [&](const uint4* src, int64_t it, auto kCheck) {
       {  // other waves may have raised the chunk's threshold
         const uint32_t m = uniform(
             (int)__hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
@@ -268,19 +271,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t vid = it * step + (int64_t)u * kThreads + tid;
-        scan_vec<kBf16>(src[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, &s_thr, lane,
-                        it == 0 && u == 0);
+        scan_vec<kBf16>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
+                        &s_thr, lane, it == 0 && u == 0);
       }
     };
+    constexpr std::false_type kInside{};
+    constexpr std::true_type kEdge{};
+    const int64_t nfull = nvec / step;  // iterations with every vector inside the chunk
     load_iter(bufA, 0);
     int64_t it = 0;
-    for (; it + 2 <= niter; it += 2) {  // no exit in the middle: exact load waits
+    // bufA holds iteration `it` at the top of each loop; no exit in the middle of an
+    // iteration pair, so the compiler's load waits stay exact
+    for (; it + 2 <= nfull; it += 2) {
       load_iter(bufB, it + 1);
-      scan_iter(bufA, it);
+      scan_iter(bufA, it, kInside);
       load_iter(bufA, it + 2);
-      scan_iter(bufB, it + 1);
+      scan_iter(bufB, it + 1, kInside);
     }
-    if (it < niter) scan_iter(bufA, it);  // odd count: bufA holds the last iteration
+    for (; it + 2 <= niter; it += 2) {  // at most once: the last iteration may be ragged
+      load_iter(bufB, it + 1);
+      scan_iter(bufA, it, kEdge);
+      load_iter(bufA, it + 2);
+      scan_iter(bufB, it + 1, kEdge);
+    }
+    if (it < niter) scan_iter(bufA, it, kEdge);  // odd count: bufA holds the last iteration
   }
 
   if (w.cnt > 0) wave_merge(w, buf, &s_thr, lane);
