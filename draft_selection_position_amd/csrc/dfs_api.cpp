@@ -15,6 +15,14 @@ namespace {
 
 constexpr int64_t kMaxV = 2147483647;  // token ids are int32
 constexpr int64_t kMaxD = DFS_MAX_D;    // the gate's 32-bit buffer offsets
+// bf16 convolution: row tiles x column tiles stay within 2^22 workgroups
+constexpr int64_t kMaxConvElems = (int64_t)1 << 36;
+// LM head: rows and vocabulary within range, and its 128 x 128 tiles within 2^23
+// workgroups (the launch grids stay within 2^31 work-items)
+inline bool lmhead_shape_ok(int64_t rows, int64_t V, int64_t d) {
+  if (rows < 1 || rows > DFS_MAX_ROWS || V < DFS_K || V > kMaxV || d < 64 || d > kMaxD) return false;
+  return ((rows + 127) / 128) * ((V + 127) / 128) <= ((int64_t)1 << 23);
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int esize(dfs_dtype_t t) { return t == DFS_BF16 ? 2 : 4; }
@@ -51,7 +59,7 @@ int check_topk_args(const void* logits, int dt, int64_t rows, int64_t V, int k,
   if (!logits || !out_idx || !out_val) return DFS_E_NULL;
   if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
   if (k != DFS_K) return DFS_E_UNSUPPORTED;
-  if (rows < 1 || V < DFS_K || V > kMaxV) return DFS_E_SHAPE;
+  if (rows < 1 || rows > DFS_MAX_ROWS || V < DFS_K || V > kMaxV) return DFS_E_SHAPE;
   if (!aligned(logits, esize((dfs_dtype_t)dt)) || !aligned(out_idx, 4) || !aligned(out_val, 4))
     return DFS_E_ALIGN;
   return DFS_OK;
@@ -62,7 +70,7 @@ int check_gate_args(const void* hidden, const void* W_h, int dt, int64_t rows, i
   if (!hidden || !W_h || !out) return DFS_E_NULL;
   if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
   if (E != DFS_E) return DFS_E_UNSUPPORTED;
-  if (rows < 1 || d < 1 || d > kMaxD) return DFS_E_SHAPE;
+  if (rows < 1 || rows > DFS_MAX_ROWS || d < 1 || d > kMaxD) return DFS_E_SHAPE;
   if (d % 8 != 0) return DFS_E_UNSUPPORTED;
   if (!aligned(hidden, 16) || !aligned(W_h, 16) || !aligned(out, 4)) return DFS_E_ALIGN;
   return DFS_OK;
@@ -111,7 +119,7 @@ int check_shape(const dfs_shape_t* s) {
       s->d > kMaxD)
     return DFS_E_SHAPE;
   if (s->d % 8 != 0) return DFS_E_UNSUPPORTED;
-  if (s->batch > (int64_t)1 << 30) return DFS_E_SHAPE;
+  if (s->batch > DFS_MAX_ROWS / s->L) return DFS_E_SHAPE;
   return DFS_OK;
 }
 
@@ -191,7 +199,7 @@ const char* dfs_status_str(int status) {
 }
 
 size_t dfs_topk_workspace_bytes(int64_t rows, int64_t V, dfs_dtype_t dt) {
-  if (rows < 1 || V < DFS_K || V > kMaxV || !valid_dtype(dt)) return 0;
+  if (rows < 1 || rows > DFS_MAX_ROWS || V < DFS_K || V > kMaxV || !valid_dtype(dt)) return 0;
   return plan_topk(rows, V, esize(dt)).ws_bytes;
 }
 
@@ -208,7 +216,7 @@ int dfs_topk(const void* logits, dfs_dtype_t dt, int64_t rows, int64_t V, int k,
 }
 
 size_t dfs_gate_workspace_bytes(int64_t rows, int64_t d, dfs_dtype_t dt) {
-  if (rows < 1 || d < 1 || d > kMaxD || d % 8 != 0 || !valid_dtype(dt)) return 0;
+  if (rows < 1 || rows > DFS_MAX_ROWS || d < 1 || d > kMaxD || d % 8 != 0 || !valid_dtype(dt)) return 0;
   return plan_gate(rows, d, dt == DFS_BF16).ws_bytes;
 }
 
@@ -230,7 +238,7 @@ int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_
                     hipStream_t stream) {
   if (!cand_idx || !cand_val || !prev_token || !gate || !A || !B || !out_pair) return DFS_E_NULL;
   if (!valid_dtype(table_dt) || k != DFS_K || E != DFS_E) return DFS_E_UNSUPPORTED;
-  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K || V > kMaxV)
+  if (batch < 1 || L < 1 || L > DFS_MAX_L || batch > DFS_MAX_ROWS / L || V < DFS_K || V > kMaxV)
     return DFS_E_SHAPE;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(gate, 16) || !aligned(cand_idx, 4) ||
       !aligned(cand_val, 4) || !aligned(prev_token, 4) || !aligned(out_pair, 4))
@@ -250,7 +258,7 @@ int dfs_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t 
   if (k != DFS_K) return DFS_E_UNSUPPORTED;
   int st = check_walk_mode(mode, temperature);
   if (st != DFS_OK) return st;
-  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L) return DFS_E_SHAPE;
+  if (batch < 1 || L < 1 || L > DFS_MAX_L || batch > DFS_MAX_ROWS / L) return DFS_E_SHAPE;
   if (!aligned(pair, 4) || !aligned(cand_idx, 4) || !aligned(out_path, 4) ||
       !aligned(out_scores, 4))
     return DFS_E_ALIGN;
@@ -286,7 +294,7 @@ int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev
 }
 
 size_t dfs_verify_workspace_bytes(int64_t batch, int64_t L, int64_t V, dfs_dtype_t dt) {
-  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K ||
+  if (batch < 1 || L < 1 || L > DFS_MAX_L || batch > DFS_MAX_ROWS / (L + 1) || V < DFS_K ||
       V > verify_max_vocab() || !valid_dtype(dt))
     return 0;
   return plan_verify(batch, L, V, esize(dt)).ws_bytes;
@@ -299,7 +307,7 @@ int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t
   if (!target_logits || !path || !cand || !q || !out_accepted || !out_token || !ws)
     return DFS_E_NULL;
   if (!valid_dtype(dt) || k != DFS_K) return DFS_E_UNSUPPORTED;
-  if (batch < 1 || batch > (int64_t)1 << 30 || L < 1 || L > DFS_MAX_L || V < DFS_K ||
+  if (batch < 1 || L < 1 || L > DFS_MAX_L || batch > DFS_MAX_ROWS / (L + 1) || V < DFS_K ||
       V > verify_max_vocab())
     return DFS_E_SHAPE;
   if (!(std::isfinite(temperature) && temperature > 0.0)) return DFS_E_ARG;
@@ -320,7 +328,8 @@ static int check_conv2_shape(int64_t batch, int64_t L, int64_t D, int dt) {
   if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
   if (batch < 1 || L < 1 || L > DFS_CONV_MAX_L || D < 256 || D > kMaxD) return DFS_E_SHAPE;
   if (D % 256 != 0) return DFS_E_UNSUPPORTED;
-  if (batch > ((int64_t)1 << 31) / L) return DFS_E_SHAPE;
+  if (batch > DFS_MAX_ROWS / L) return DFS_E_SHAPE;
+  if (batch * L * D > kMaxConvElems) return DFS_E_SHAPE;
   if (dt == DFS_F32 && batch * L * D > conv2_max_f32_elems()) return DFS_E_SHAPE;
   return DFS_OK;
 }
@@ -360,16 +369,14 @@ static int check_lmhead(const void* hidden, const void* W_lm, dfs_dtype_t dt, in
                         int64_t d) {
   if (!hidden || !W_lm) return DFS_E_NULL;
   if (dt != DFS_BF16) return DFS_E_UNSUPPORTED;
-  if (rows < 1 || rows > ((int64_t)1 << 30) || V < DFS_K || V > kMaxV || d < 64 || d > kMaxD)
-    return DFS_E_SHAPE;
+  if (!lmhead_shape_ok(rows, V, d)) return DFS_E_SHAPE;
   if (d % 64 != 0) return DFS_E_UNSUPPORTED;
   if (!aligned(hidden, 16) || !aligned(W_lm, 16)) return DFS_E_ALIGN;
   return DFS_OK;
 }
 
 size_t dfs_lmhead_topk_workspace_bytes(int64_t rows, int64_t V, int64_t d) {
-  if (rows < 1 || rows > ((int64_t)1 << 30) || V < DFS_K || V > kMaxV || d < 64 || d > kMaxD || d % 64)
-    return 0;
+  if (!lmhead_shape_ok(rows, V, d) || d % 64) return 0;
   return lmhead_workspace_bytes(rows, V, d);
 }
 

@@ -51,6 +51,10 @@ extern "C" {
 #define DFS_E 256     /* embedding and gate width */
 #define DFS_MAX_L 16  /* longest block handled; the post's blocks span 4 to 16 tokens */
 #define DFS_MAX_D (1 << 20) /* widest hidden state handled */
+/* Most rows per call: logit or hidden-state rows (B*L; B*(L+1) target rows for verification).
+   Larger calls return DFS_E_SHAPE before anything is launched, so that no launch grid
+   exceeds 2^31 work-items. */
+#define DFS_MAX_ROWS (1 << 22)
 #define DFS_CONV_MAX_L 65536 /* longest run of positions dfs_conv2 takes per sequence */
 
 typedef enum {
@@ -215,7 +219,7 @@ int dfs_verify(const void* target_logits, dfs_dtype_t dt, int64_t batch, int64_t
  *   y [batch, L, D]   output, same dtype as the inputs; must not overlap x or x_prev
  * All of dtype dt (bf16: correction on the matrix cores with fp32 sums, y rounded to
  * nearest-even bf16; fp32: fp32 throughout).  D a multiple of 256 in [256, DFS_MAX_D],
- * 1 <= L <= DFS_CONV_MAX_L, batch * L < 2^31 (fp32: batch * L * D <= 2^32).  Every
+ * 1 <= L <= DFS_CONV_MAX_L, batch * L <= DFS_MAX_ROWS, batch * L * D <= 2^36 (fp32: <= 2^32).  Every
  * pointer 16-byte aligned, ws 256-byte aligned.
  * ws: dfs_conv2_workspace_bytes(batch, L, D, dt) bytes: split partial sums of the bf16
  * correction when the shape is too small to fill the chip, else 0 (ws may then be NULL). */
@@ -237,7 +241,8 @@ int dfs_conv2(const void* x, const void* x_prev, const void* base, const void* W
  *   out_idx [rows, 16] int32, out_val [rows, 16] fp32: value descending, then the
  *     lower id, on the fp32 sums -- exactly dfs_topk run on dfs_lmhead_logits' U.
  * dt must be DFS_BF16; d a multiple of 64 in [64, DFS_MAX_D]; 16 <= V < 2^31;
- * 1 <= rows <= 2^30.  hidden and W_lm 16-byte aligned, outputs 4, ws 256.
+ * 1 <= rows <= DFS_MAX_ROWS and ceil(rows / 128) * ceil(V / 128) <= 2^23.  hidden and W_lm
+ * 16-byte aligned, outputs 4, ws 256.
  * ws: dfs_lmhead_topk_workspace_bytes(rows, V, d) bytes (never 0): per-row lists of
  * the column stripes, merged at the end (for <= 32 rows: U and the top-16 pass's
  * lists).  Finite inputs whose sums stay finite. */

@@ -225,3 +225,28 @@ def test_lmhead_validation(L):
     assert 0 < nb < 1 << 24
     assert L.dfs_lmhead_topk_workspace_bytes(16, 151936, 5100) == 0
     assert L.dfs_lmhead_logits(P, P, 0, 16, 1000, 512, P, None) == E_UNSUP
+
+
+def test_row_limit(L):
+    # DFS_MAX_ROWS rows per call: one more is a shape error before any launch, so that no
+    # launch grid passes 2^31 work-items; at the limit validation goes on to the next check
+    M = 1 << 22
+    assert _topk(L, rows=M + 1, V=16) == E_SHAPE
+    assert L.dfs_topk_workspace_bytes(M + 1, 16, 1) == 0
+    assert _topk(L, rows=M, V=16, ws=None, wsb=0) != E_SHAPE
+    assert L.dfs_gate(P, P, 1, M + 1, 64, 256, P, P, 1 << 20, None) == E_SHAPE
+    assert L.dfs_gate_workspace_bytes(M + 1, 64, 1) == 0
+    assert L.dfs_pair_scores(P, P, P, P, P, P, 1, M // 16 + 1, 16, 100, 256, 16, P, None) == E_SHAPE
+    assert L.dfs_walk(P, P, M // 4 + 1, 4, 16, 0, 1.0, 0, P, P, None) == E_SHAPE
+    assert L.dfs_walk(P, P, M + 1, 1, 16, 0, 1.0, 0, P, P, None) == E_SHAPE
+    sh = dfs._Shape(M // 16 + 1, 16, 1000, 64, 1, 1, 1)
+    assert L.dfs_select_workspace_bytes(ctypes.byref(sh)) == 0
+    assert L.dfs_select(P, P, P, P, P, P, 16, ctypes.byref(sh), 0, 1.0, 0, P, 1 << 26, P, P, None) == E_SHAPE
+    assert L.dfs_verify_workspace_bytes(M // 17 + 1, 16, 1000, 1) == 0
+    assert L.dfs_verify_workspace_bytes(M // 17, 16, 1000, 1) > 0
+    assert L.dfs_conv2_workspace_bytes(M // 16 + 1, 16, 256, 1) == 0
+    assert L.dfs_conv2_workspace_bytes(M // 16, 16, 256, 1) >= 0
+    assert _conv(L, batch=1 << 16, Lp=64, D=1 << 20) == E_SHAPE  # 2^22 rows x 2^20 channels
+    assert L.dfs_lmhead_topk_workspace_bytes(M + 1, 1000, 512) == 0
+    assert L.dfs_lmhead_topk_workspace_bytes(1 << 16, 1 << 24, 512) == 0  # 2^9 x 2^17 tiles
+    assert L.dfs_lmhead_topk_workspace_bytes(4096, 151936, 5120) > 0
