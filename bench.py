@@ -138,6 +138,17 @@ def _affinity() -> int:
         return os.cpu_count() or 1
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _oracle_worker(args):
     # One process of the CPU baseline: the oracle on some sequences, single-threaded.
     from threadpoolctl import threadpool_limits
@@ -176,6 +187,8 @@ def cpu_baseline(name: str, walk: str, batch: int, target_cpu_s: float, workers:
         "value": nseq / wall,
         "unit": "blocks/s",
         "cores": len(chunks),
+        "host_cores": _affinity(),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"{nseq} of {batch} sequences of workload {name} (full V, L, d), "
                   f"{len(chunks)} worker processes x 1 thread, {cpu_s:.1f} CPU-s of oracle work "
@@ -194,7 +207,9 @@ def main() -> int:
     ap.add_argument("--walk", choices=["greedy", "gumbel", "viterbi"],
                     help="walk mode instead of the workload's own (its temperature and seed are kept)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU work of the baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=32.0,
+                    help="oracle CPU work of the baseline sample (32 s covers all 256 sequences of the "
+                         "throughput workload)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run device-to-device copies of this size (counter calibration)")
     ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
@@ -240,12 +255,14 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (before the GPU is touched)", file=sys.stderr, flush=True)
+        # One worker process per core the process may run on, at most 16: a one-GPU machine's
+        # share of its host is 16 cores, whatever the affinity mask shows there.
         cpu = cpu_baseline(cfg.name, cfg.walk, cfg.batch, args.cpu_seconds, max(1, min(16, _affinity())))
 
     import torch
 
     import draft_selection_position_amd as dfs
-    from tests.parity import upload
+    from workloads.device import upload
 
     dev = upload(inp)
     # Copies of the whole input set at other addresses, rotated call by call, so that
@@ -260,7 +277,12 @@ def main() -> int:
                        seed=cfg.walk_seed,
                        logits_dtype=dev["logits"].dtype, act_dtype=dev["hidden"].dtype,
                        table_dtype=dev["A"].dtype)
-    args_of = [tuple(st[k] for k in names) for st in sets]
+    # W_h is a constant of the drafter: each input set's copy is packed once, before any
+    # timing (dfs_gate_pack), and the timed calls take it packed (dfs_select_packed, the
+    # same bits as dfs_select on the row-major weight).
+    packed = [dfs.gate_pack(st["W_h"]) for st in sets]
+    args_of = [tuple(st[k] for k in names[:5]) + (pk,) for st, pk in zip(sets, packed)]
+    args_rowmajor = [tuple(st[k] for k in names) for st in sets]
 
     def call(i=0):
         return sel(*args_of[i % nsets])
@@ -270,7 +292,20 @@ def main() -> int:
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
+    # Per-call spread first (each call between its own pair of events): it also keeps
+    # the timed figure below from depending on how short the warm-up is.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(args.steps, 50))]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in evs])
+    pct = {f"p{q}": float(np.percentile(per_call, q)) for q in (10, 50, 90)}
+
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
@@ -281,17 +316,20 @@ def main() -> int:
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     blocks_per_s = cfg.batch / (ms_per_step * 1e-3)
     path = sel.path.cpu().numpy()  # the last call's (every set holds the same values)
+    scores_gpu = sel.scores.cpu().numpy()
 
-    # Per-call spread: the same calls again, each between its own pair of events.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        call(i)
-        b.record()
+    # The same calls with the row-major weight (dfs_select packs it on every call).
+    for i in range(5):
+        sel(*args_rowmajor[i % nsets])
     torch.cuda.synchronize()
-    per_call = np.array([a.elapsed_time(b) for a, b in evs])
-    pct = {f"p{q}": float(np.percentile(per_call, q)) for q in (10, 50, 90)}
+    ev0.record()
+    for i in range(args.steps):
+        sel(*args_rowmajor[i % nsets])
+    ev1.record()
+    torch.cuda.synchronize()
+    rowmajor_ms = ev0.elapsed_time(ev1) / args.steps
+    if not np.array_equal(sel.path.cpu().numpy(), path):
+        raise RuntimeError("dfs_select and dfs_select_packed gave different paths")
 
     # The dominant kernel alone: the top-16 pass over [batch*L, V], same stream,
     # rotating over the input sets' logits like the calls above.
@@ -324,7 +362,7 @@ def main() -> int:
         return ev0.elapsed_time(ev1) / n
 
     hidden2d = dev["hidden"].view(-1, cfg.d)
-    gate_ms = timed(lambda: dfs.gate(hidden2d, dev["W_h"]))
+    gate_ms = timed(lambda: dfs.gate(hidden2d, packed[0]))
     idx, val = dfs.topk(logits2d, workspace=ws)
     g = dfs.gate(hidden2d, dev["W_h"])
     idx3, val3 = idx.view(cfg.batch, cfg.L, 16), val.view(cfg.batch, cfg.L, 16)
@@ -391,7 +429,7 @@ def main() -> int:
     if args.conv:
         # One convolution site of the drafter at this workload's shape: x [batch, L, d].
         from workloads.conv import make_conv
-        from tests.parity import to_dev
+        from workloads.device import to_dev
 
         ci = make_conv(cfg)
         cx = [to_dev(ci.x)]
@@ -420,7 +458,7 @@ def main() -> int:
         # The drafter's LM head on the workload's own hidden states: W_lm [V, d] ~ N(0, 0.02).
         from workloads.lmhead import make_lm_head
 
-        from tests.parity import to_dev as _to_dev
+        from workloads.device import to_dev as _to_dev
 
         W_lm = _to_dev(make_lm_head(cfg))
         rows = cfg.batch * cfg.L
@@ -474,7 +512,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": topk_gbs / HBM_PEAK_GBS, "traffic": None if traffic is None else traffic[0],
                      "kernel": "topk_chunk_kernel", "bytes_per_launch": topk_bytes, "avg_ms": topk_ms},
-        "step_ms": {"topk": topk_ms, "gate": gate_ms, "pair_scores": pair_ms, "select": ms_per_step},
+        "entry_point": "dfs_select_packed (W_h packed once per weight by dfs_gate_pack)",
+        "step_ms": {"topk": topk_ms, "gate": gate_ms, "pair_scores": pair_ms, "select": ms_per_step,
+                    "select_rowmajor_W_h": rowmajor_ms},
         "select_ms_per_call": pct,
         "input_sets": nsets,
         "host_wall_s": wall,
@@ -491,6 +531,7 @@ def main() -> int:
     if cpu is not None:
         paths = cpu.pop("_paths")
         mism = near = 0
+        near_positions = sum(int(sum(1 for x in m if x < 1e-4)) for _, m in paths.values())
         for s, (p, m) in paths.items():
             for t in range(cfg.L):
                 if int(path[s, t]) != p[t]:
@@ -499,7 +540,8 @@ def main() -> int:
                     else:
                         mism += 1
                     break
-        cpu["parity_sample"] = {"sequences": len(paths), "mismatched": mism, "near_tie_divergence": near}
+        cpu["parity_sample"] = {"sequences": len(paths), "of": cfg.batch, "mismatched": mism,
+                                "near_tie_divergence": near, "oracle_near_tie_positions": near_positions}
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0

@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "DfsError", "K", "E", "MAX_L", "lib", "lib_path", "topk", "gate", "pair_scores", "walk",
-    "select", "Selector", "select_workspace_bytes", "topk_workspace_bytes",
+    "select", "Selector", "select_workspace_bytes", "topk_workspace_bytes", "PackedWeight", "gate_pack",
     "gate_workspace_bytes", "status_str", "conv2", "conv2_workspace_bytes", "Conv2", "lmhead_topk", "lmhead_logits",
     "lmhead_topk_workspace_bytes",
 ]
@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.dfs_gate_workspace_bytes.argtypes, L.dfs_gate_workspace_bytes.restype = [i64, i64, c_int], sz
         L.dfs_gate.argtypes = [vp, vp, c_int, i64, i64, i64, f32p, vp, sz, vp]
         L.dfs_gate.restype = c_int
+        L.dfs_gate_packed.argtypes = [vp, vp, c_int, i64, i64, i64, f32p, vp, sz, vp]
+        L.dfs_gate_packed.restype = c_int
+        L.dfs_gate_pack_bytes.argtypes, L.dfs_gate_pack_bytes.restype = [i64, c_int], sz
+        L.dfs_gate_pack.argtypes = [vp, c_int, i64, vp, sz, vp]
+        L.dfs_gate_pack.restype = c_int
         L.dfs_pair_scores.argtypes = [i32p, f32p, i32p, f32p, vp, vp, c_int, i64, i64, i64, i64, c_int,
                                       f32p, vp]
         L.dfs_pair_scores.restype = c_int
@@ -82,9 +87,13 @@ def lib() -> ctypes.CDLL:
         L.dfs_select.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int, c_double,
                                  u64, vp, sz, i32p, f32p, vp]
         L.dfs_select.restype = c_int
+        L.dfs_select_packed.argtypes = L.dfs_select.argtypes
+        L.dfs_select_packed.restype = c_int
         L.dfs_select_draft.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int,
                                        c_double, u64, vp, sz, i32p, f32p, f32p, i32p, vp]
         L.dfs_select_draft.restype = c_int
+        L.dfs_select_draft_packed.argtypes = L.dfs_select_draft.argtypes
+        L.dfs_select_draft_packed.restype = c_int
         L.dfs_verify_workspace_bytes.argtypes, L.dfs_verify_workspace_bytes.restype = [i64, i64, i64, c_int], sz
         L.dfs_verify.argtypes = [vp, c_int, i64, i64, i64, i32p, i32p, f32p, c_int, c_double, u64, vp, sz,
                                  i32p, i32p, vp]
@@ -146,18 +155,31 @@ def _ptr(t) -> int | None:
 
 
 class _Workspace:
-    """A per-device cached byte buffer (grown on demand, never shrunk)."""
+    """Cached scratch buffers, one per (device, stream), grown on demand, never shrunk.
+
+    A call without an explicit workspace uses the buffer of the stream it is enqueued
+    on, so calls on different streams never share scratch memory.  Each buffer is
+    allocated while its own stream is current, so when a grown buffer replaces it, the
+    caching allocator hands the old block out again only to later work on that same
+    stream (after everything already enqueued there).
+    """
 
     def __init__(self):
-        self._bufs: dict[torch.device, torch.Tensor] = {}
+        self._bufs: dict[tuple, torch.Tensor] = {}
+
+    @staticmethod
+    def key(device: torch.device) -> tuple:
+        return (device, torch.cuda.current_stream(device).cuda_stream)
 
     def get(self, device: torch.device, nbytes: int) -> torch.Tensor | None:
         if nbytes == 0:
             return None
-        buf = self._bufs.get(device)
+        key = self.key(device)
+        buf = self._bufs.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-            self._bufs[device] = buf
+            with torch.cuda.device(device):
+                buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
         return buf
 
 
@@ -202,20 +224,66 @@ def gate_workspace_bytes(rows: int, d: int, dtype: torch.dtype) -> int:
     return int(lib().dfs_gate_workspace_bytes(rows, d, BF16 if dtype == torch.bfloat16 else F32))
 
 
-def gate(hidden: torch.Tensor, W_h: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """sigmoid(hidden @ W_h) in fp32: hidden [..., d], W_h [d, 256] (same dtype) -> [..., 256]."""
+class PackedWeight:
+    """W_h [d, 256] packed once for the gate's matrix cores (dfs_gate_pack).
+
+    Pass it wherever W_h is taken (``gate``, ``select``, ``Selector``): the results are
+    bitwise those of the unpacked weight, without repacking it on every call.  It holds
+    its own device bytes; ``d`` and ``dtype`` are those of the weight it came from.
+    """
+
+    def __init__(self, data: torch.Tensor, d: int, dtype: torch.dtype):
+        self.data, self.d, self.dtype = data, int(d), dtype
+        self.device = data.device
+        self.shape = (int(d), E)
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def gate_pack(W_h: torch.Tensor) -> PackedWeight:
+    """Pack the gate weight W_h [d, 256] (bf16 or fp32) for the matrix cores, once."""
+    _dev(W_h, "W_h")
+    dt = _dtype_code(W_h, "W_h")
+    if W_h.dim() != 2 or W_h.shape[1] != E:
+        raise ValueError(f"W_h must be [d, 256], got {tuple(W_h.shape)}")
+    d = W_h.shape[0]
+    nb = int(lib().dfs_gate_pack_bytes(d, dt))
+    if nb == 0:
+        raise ValueError(f"unsupported gate width d = {d}")
+    out = torch.empty(nb, dtype=torch.uint8, device=W_h.device)
+    _check(lib().dfs_gate_pack(W_h.data_ptr(), dt, d, out.data_ptr(), nb, _stream(W_h.device)), "dfs_gate_pack")
+    return PackedWeight(out, d, W_h.dtype)
+
+
+def _weight(W_h, d: int, dtype: torch.dtype, what: str = "W_h"):
+    """(pointer, packed?) of a W_h argument: a [d, 256] tensor of `dtype` or a PackedWeight."""
+    if isinstance(W_h, PackedWeight):
+        if W_h.d != d or W_h.dtype != dtype:
+            raise ValueError(f"{what} was packed for d = {W_h.d}, {W_h.dtype}; need d = {d}, {dtype}")
+        if W_h.device.type != "cuda":
+            raise ValueError(f"{what} must be on a HIP device")
+        return W_h.data_ptr(), True
+    _dev(W_h, what, dtype)
+    if W_h.dim() != 2 or tuple(W_h.shape) != (d, E):
+        raise ValueError(f"{what} must be [{d}, 256], got {tuple(W_h.shape)}")
+    return W_h.data_ptr(), False
+
+
+def gate(hidden: torch.Tensor, W_h, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """sigmoid(hidden @ W_h) in fp32: hidden [..., d], W_h [d, 256] (same dtype, or a
+    PackedWeight) -> [..., 256]."""
     _dev(hidden, "hidden")
-    _dev(W_h, "W_h", hidden.dtype)
     dt = _dtype_code(hidden, "hidden")
     d = hidden.shape[-1]
-    if W_h.dim() != 2 or W_h.shape[0] != d:
-        raise ValueError(f"W_h must be [{d}, 256], got {tuple(W_h.shape)}")
+    wptr, packed = _weight(W_h, d, hidden.dtype)
     rows = hidden.numel() // d if d else 0
     out = torch.empty(tuple(hidden.shape[:-1]) + (E,), dtype=torch.float32, device=hidden.device)
     nb = int(lib().dfs_gate_workspace_bytes(rows, d, dt))
     ws = _ws_arg(workspace, hidden.device, nb)
-    _check(lib().dfs_gate(hidden.data_ptr(), W_h.data_ptr(), dt, rows, d, W_h.shape[1], out.data_ptr(),
-                          _ptr(ws), nb, _stream(hidden.device)), "dfs_gate")
+    fn = lib().dfs_gate_packed if packed else lib().dfs_gate
+    _check(fn(hidden.data_ptr(), wptr, dt, rows, d, E, out.data_ptr(), _ptr(ws), nb, _stream(hidden.device)),
+           "dfs_gate_packed" if packed else "dfs_gate")
     return out
 
 
@@ -274,28 +342,28 @@ def select_workspace_bytes(batch: int, L: int, V: int, d: int, logits_dtype=torc
 
 
 def select(logits: torch.Tensor, hidden: torch.Tensor, prev_token: torch.Tensor, A: torch.Tensor,
-           B: torch.Tensor, W_h: torch.Tensor, k: int = K, mode: str = "greedy", temperature: float = 1.0,
+           B: torch.Tensor, W_h, k: int = K, mode: str = "greedy", temperature: float = 1.0,
            seed: int = 0, workspace: torch.Tensor | None = None, out=None, draft: bool = False):
     """The whole selector on one draft block per sequence.
 
     logits [batch, L, V]; hidden [batch, L, d]; prev_token [batch] int32 (last
-    verified token); A, B [V, 256]; W_h [d, 256].  Returns (path int32 [batch, L],
-    scores fp32 [batch, L]).  ``out`` may pass preallocated (path, scores).  With
-    ``draft=True`` also the draft distributions q fp32 [batch, L, 16] and the
-    candidate ids int32 [batch, L, 16] (dfs_select_draft).
+    verified token); A, B [V, 256]; W_h [d, 256] or a PackedWeight (gate_pack).
+    Returns (path int32 [batch, L], scores fp32 [batch, L]).  ``out`` may pass
+    preallocated (path, scores).  With ``draft=True`` also the draft distributions q
+    fp32 [batch, L, 16] and the candidate ids int32 [batch, L, 16] (dfs_select_draft).
     """
     _dev(logits, "logits")
     _dev(hidden, "hidden")
     _dev(prev_token, "prev_token", torch.int32)
     _dev(A, "A")
     _dev(B, "B", A.dtype)
-    _dev(W_h, "W_h", hidden.dtype)
     if logits.dim() != 3 or hidden.dim() != 3 or hidden.shape[:2] != logits.shape[:2]:
         raise ValueError("logits must be [batch, L, V] and hidden [batch, L, d]")
     batch, L, V = logits.shape
     d = hidden.shape[2]
-    if A.shape != (V, E) or B.shape != (V, E) or W_h.shape != (d, E) or prev_token.shape != (batch,):
-        raise ValueError("A, B must be [V, 256], W_h [d, 256] and prev_token [batch]")
+    wptr, packed = _weight(W_h, d, hidden.dtype)
+    if A.shape != (V, E) or B.shape != (V, E) or prev_token.shape != (batch,):
+        raise ValueError("A, B must be [V, 256] and prev_token [batch]")
     s = _shape(batch, L, V, d, _dtype_code(logits, "logits"), _dtype_code(hidden, "hidden"),
                _dtype_code(A, "A"))
     nb = int(lib().dfs_select_workspace_bytes(ctypes.byref(s)))
@@ -306,18 +374,19 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, prev_token: torch.Tensor,
     else:
         path, scores = out
     if not draft:
-        _check(lib().dfs_select(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(),
-                                B.data_ptr(), W_h.data_ptr(), k, ctypes.byref(s), _MODES[mode],
-                                float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb, path.data_ptr(),
-                                scores.data_ptr(), _stream(logits.device)), "dfs_select")
+        fn = lib().dfs_select_packed if packed else lib().dfs_select
+        _check(fn(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(), B.data_ptr(), wptr,
+                  k, ctypes.byref(s), _MODES[mode], float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb,
+                  path.data_ptr(), scores.data_ptr(), _stream(logits.device)),
+               "dfs_select_packed" if packed else "dfs_select")
         return path, scores
     q = torch.empty((batch, L, K), dtype=torch.float32, device=logits.device)
     cand = torch.empty((batch, L, K), dtype=torch.int32, device=logits.device)
-    _check(lib().dfs_select_draft(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(),
-                                  B.data_ptr(), W_h.data_ptr(), k, ctypes.byref(s), _MODES[mode],
-                                  float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb, path.data_ptr(),
-                                  scores.data_ptr(), q.data_ptr(), cand.data_ptr(), _stream(logits.device)),
-           "dfs_select_draft")
+    fn = lib().dfs_select_draft_packed if packed else lib().dfs_select_draft
+    _check(fn(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(), B.data_ptr(), wptr, k,
+              ctypes.byref(s), _MODES[mode], float(temperature), int(seed) & (2**64 - 1), _ptr(ws), nb,
+              path.data_ptr(), scores.data_ptr(), q.data_ptr(), cand.data_ptr(), _stream(logits.device)),
+           "dfs_select_draft_packed" if packed else "dfs_select_draft")
     return path, scores, q, cand
 
 
@@ -457,18 +526,24 @@ class Selector:
             ((V, E), table_dtype), ((V, E), table_dtype), ((d, E), act_dtype),
         )
         self._fn = lib().dfs_select
+        self._fn_packed = lib().dfs_select_packed
 
     def __call__(self, logits, hidden, prev_token, A, B, W_h):
-        args = (logits, hidden, prev_token, A, B, W_h)
+        """W_h: the [d, 256] weight, or a PackedWeight of it (then dfs_select_packed)."""
+        packed = isinstance(W_h, PackedWeight)
+        args = (logits, hidden, prev_token, A, B) if packed else (logits, hidden, prev_token, A, B, W_h)
         for t, (shape, dtype) in zip(args, self._expect):
             if t.shape != shape or t.dtype != dtype or t.device != self.device or not t.is_contiguous():
                 raise ValueError(f"selector input must be a contiguous {dtype} tensor of shape {shape} "
                                  f"on {self.device}")
-        rc = self._fn(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(), B.data_ptr(),
-                      W_h.data_ptr(), K, ctypes.byref(self._shape), self.mode, self.temperature, self.seed,
-                      self.workspace.data_ptr(), self._ws_bytes, self.path.data_ptr(), self.scores.data_ptr(),
-                      torch.cuda.current_stream(self.device).cuda_stream)
-        _check(rc, "dfs_select")
+        if packed and (W_h.d, W_h.dtype, W_h.device) != (self._expect[5][0][0], self._expect[5][1], self.device):
+            raise ValueError("packed W_h does not match the selector's d, dtype or device")
+        fn = self._fn_packed if packed else self._fn
+        rc = fn(logits.data_ptr(), hidden.data_ptr(), prev_token.data_ptr(), A.data_ptr(), B.data_ptr(),
+                W_h.data_ptr(), K, ctypes.byref(self._shape), self.mode, self.temperature, self.seed,
+                self.workspace.data_ptr(), self._ws_bytes, self.path.data_ptr(), self.scores.data_ptr(),
+                torch.cuda.current_stream(self.device).cuda_stream)
+        _check(rc, "dfs_select_packed" if packed else "dfs_select")
         return self.path, self.scores
 
 

@@ -25,6 +25,10 @@ inline bool lmhead_shape_ok(int64_t rows, int64_t V, int64_t d) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
 int esize(dfs_dtype_t t) { return t == DFS_BF16 ? 2 : 4; }
 bool valid_dtype(int t) { return t == DFS_F32 || t == DFS_BF16; }
 
@@ -126,7 +130,7 @@ int check_shape(const dfs_shape_t* s) {
 }  // namespace
 
 static int select_impl(const void* logits, const void* hidden, const int32_t* prev_token,
-                       const void* A, const void* B, const void* W_h, int k,
+                       const void* A, const void* B, const void* W_h, bool wh_packed, int k,
                        const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
                        uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                        float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream) {
@@ -151,31 +155,50 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   int32_t* cand_idx = reinterpret_cast<int32_t*>(w + l.cand_idx_off);
   float* cand_val = reinterpret_cast<float*>(w + l.cand_val_off);
   float* gate = reinterpret_cast<float*>(w + l.gate_off);
-  // One stream, in order: the top-16 pass (the W_h packing slabs ride in its
-  // tail), the gate GEMM (with the merge of split rows' top-16 lists riding along),
-  // the gate finish when the K split is wider than the pair kernel adds up itself,
-  // then pair scores and the walk in one kernel.
   char* gws = w + l.gate_ws_off;
-  const PackJob job = gate_pack_job(l.gate, W_h, gws);
-  hipError_t e = launch_topk(l.topk, logits, s.logits_dtype == DFS_BF16, cand_idx, cand_val,
-                             w + l.topk_ws_off, stream, &job, false);
-  if (e != hipSuccess) return DFS_E_HIP;
-  const MergeJob mj = topk_merge_job(l.topk, w + l.topk_ws_off, cand_idx, cand_val);
-  if ((e = launch_gate_gemm(l.gate, hidden, W_h, gate, gws, stream, &mj)) != hipSuccess) return DFS_E_HIP;
-  GateSrc gs{gate, 1, 0};
-  if (l.gate.splits > 1) {
-    if (l.gate.splits <= pair_max_gate_splits()) {
-      gs = GateSrc{gate_partials(l.gate, gws), l.gate.splits, s.batch * s.L * DFS_E};
-    } else if ((e = launch_gate_finish(l.gate, gate, gws, stream)) != hipSuccess) {
-      return DFS_E_HIP;
-    }
+  char* tws = w + l.topk_ws_off;
+  const bool bf16_logits = s.logits_dtype == DFS_BF16;
+  const bool bf16_act = s.act_dtype == DFS_BF16;
+  // Two or three launches on one stream.  (1) The top-16 pass; rows split into parts
+  // leave their partial lists for the pair kernel to merge.  With few rows and a gate
+  // that needs no repacking (fp32, or W_h packed by the caller) the gate's tiles ride
+  // in the same launch; otherwise the W_h packing slabs (when needed) ride in its tail
+  // and (2) the gate GEMM follows.  (3) Pair scores and the walk in one kernel, which
+  // also merges the split rows' lists and adds up the gate's K-split partial sums.
+  hipError_t e;
+  if (l.gate.kind == GatePlan::kJobs && (wh_packed || !bf16_act)) {
+    const GateJobs gj = gate_jobs(l.gate, hidden, W_h, gate, gws);
+    e = launch_topk_gate(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, gj, bf16_act, stream);
+    if (e != hipSuccess) return DFS_E_HIP;
+  } else {
+    const PackJob job = bf16_act && !wh_packed ? gate_pack_job(l.gate, W_h, gws) : PackJob{nullptr, 0, nullptr, 0};
+    e = launch_topk(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, stream, &job, false);
+    if (e != hipSuccess) return DFS_E_HIP;
+    const void* Wg = bf16_act && !wh_packed ? gate_packed_in_ws(l.gate, gws) : W_h;
+    if ((e = launch_gate_gemm(l.gate, hidden, Wg, gate, gws, stream)) != hipSuccess) return DFS_E_HIP;
   }
+  const CandSrc cs = l.topk.parts > 1 ? CandSrc{nullptr, nullptr, reinterpret_cast<const uint64_t*>(tws), l.topk.parts}
+                                      : cand_lists(cand_idx, cand_val);
+  const GateSrc gs = l.gate.splits > 1 ? GateSrc{gate_partials(l.gate, gws), l.gate.splits, s.batch * s.L * DFS_E}
+                                       : GateSrc{gate, 1, 0};
   const WalkArgs wa{(int)mode, temperature, seed, out_q, out_cand};
-  e = launch_pair_walk(cand_idx, cand_val, prev_token, gs, A, B, s.table_dtype == DFS_BF16,
-                       s.batch, s.L, s.V, nullptr, &wa, out_path, out_scores, stream);
+  e = launch_pair_walk(cs, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V, nullptr, &wa,
+                       out_path, out_scores, stream);
   return hip_status(e);
 }
 
+static int select_entry(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                        const void* B, const void* W_h, bool wh_packed, int k, const dfs_shape_t* shape,
+                        dfs_walk_t mode, double temperature, uint64_t seed, void* ws, size_t ws_bytes,
+                        int32_t* out_path, float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream) {
+  if (out_q || out_cand) {
+    if (!out_q || !out_cand) return DFS_E_NULL;
+    if (!aligned(out_q, 4) || !aligned(out_cand, 4)) return DFS_E_ALIGN;
+    if (!(std::isfinite(temperature) && temperature > 0.0)) return DFS_E_ARG;
+  }
+  return select_impl(logits, hidden, prev_token, A, B, W_h, wh_packed, k, shape, mode, temperature, seed, ws,
+                     ws_bytes, out_path, out_scores, out_q, out_cand, stream);
+}
 
 extern "C" {
 
@@ -220,8 +243,8 @@ size_t dfs_gate_workspace_bytes(int64_t rows, int64_t d, dfs_dtype_t dt) {
   return plan_gate(rows, d, dt == DFS_BF16).ws_bytes;
 }
 
-int dfs_gate(const void* hidden, const void* W_h, dfs_dtype_t dt, int64_t rows, int64_t d,
-             int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int gate_entry(const void* hidden, const void* W_h, bool prepacked, dfs_dtype_t dt, int64_t rows,
+                      int64_t d, int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_gate_args(hidden, W_h, dt, rows, d, E, out_gate);
   if (st != DFS_OK) return st;
   const GatePlan p = plan_gate(rows, d, dt == DFS_BF16);
@@ -229,7 +252,40 @@ int dfs_gate(const void* hidden, const void* W_h, dfs_dtype_t dt, int64_t rows, 
   if (ws && !aligned(ws, 256)) return DFS_E_ALIGN;
   if ((st = check_device()) != DFS_OK) return st;
   (void)hipGetLastError();
-  return hip_status(launch_gate(p, hidden, W_h, out_gate, ws, stream));
+  return hip_status(launch_gate(p, hidden, W_h, prepacked, out_gate, ws, stream));
+}
+
+int dfs_gate(const void* hidden, const void* W_h, dfs_dtype_t dt, int64_t rows, int64_t d,
+             int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return gate_entry(hidden, W_h, false, dt, rows, d, E, out_gate, ws, ws_bytes, stream);
+}
+
+int dfs_gate_packed(const void* hidden, const void* W_packed, dfs_dtype_t dt, int64_t rows, int64_t d,
+                    int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return gate_entry(hidden, W_packed, true, dt, rows, d, E, out_gate, ws, ws_bytes, stream);
+}
+
+size_t dfs_gate_pack_bytes(int64_t d, dfs_dtype_t dt) {
+  if (d < 1 || d > kMaxD || d % 8 != 0 || !valid_dtype(dt)) return 0;
+  return dt == DFS_BF16 ? gate_packed_bytes(d) : (size_t)d * DFS_E * sizeof(float);
+}
+
+int dfs_gate_pack(const void* W_h, dfs_dtype_t dt, int64_t d, void* out_packed, size_t out_bytes,
+                  hipStream_t stream) {
+  if (!W_h || !out_packed) return DFS_E_NULL;
+  if (!valid_dtype(dt)) return DFS_E_UNSUPPORTED;
+  if (d < 1 || d > kMaxD) return DFS_E_SHAPE;
+  if (d % 8 != 0) return DFS_E_UNSUPPORTED;
+  if (!aligned(W_h, 16) || !aligned(out_packed, 16)) return DFS_E_ALIGN;
+  const size_t need = dfs_gate_pack_bytes(d, dt);
+  if (out_bytes < need) return DFS_E_WORKSPACE;
+  const size_t in_bytes = (size_t)d * DFS_E * (size_t)esize(dt);
+  if (overlaps(W_h, in_bytes, out_packed, need)) return DFS_E_ARG;
+  int st = check_device();
+  if (st != DFS_OK) return st;
+  (void)hipGetLastError();
+  if (dt == DFS_F32) return hip_status(hipMemcpyAsync(out_packed, W_h, need, hipMemcpyDeviceToDevice, stream));
+  return hip_status(launch_gate_pack(W_h, d, out_packed, stream));
 }
 
 int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* prev_token,
@@ -246,7 +302,7 @@ int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_
   int st = check_device();
   if (st != DFS_OK) return st;
   (void)hipGetLastError();
-  return hip_status(launch_pair_walk(cand_idx, cand_val, prev_token, GateSrc{gate, 1, 0}, A, B,
+  return hip_status(launch_pair_walk(cand_lists(cand_idx, cand_val), prev_token, GateSrc{gate, 1, 0}, A, B,
                                      table_dt == DFS_BF16, batch, L, V, out_pair, nullptr, nullptr,
                                      nullptr, stream));
 }
@@ -277,8 +333,16 @@ int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token
                const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
                double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                float* out_scores, hipStream_t stream) {
-  return select_impl(logits, hidden, prev_token, A, B, W_h, k, shape, mode, temperature, seed, ws,
-                     ws_bytes, out_path, out_scores, nullptr, nullptr, stream);
+  return select_entry(logits, hidden, prev_token, A, B, W_h, false, k, shape, mode, temperature, seed, ws,
+                      ws_bytes, out_path, out_scores, nullptr, nullptr, stream);
+}
+
+int dfs_select_packed(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                      const void* B, const void* W_packed, int k, const dfs_shape_t* shape, dfs_walk_t mode,
+                      double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+                      float* out_scores, hipStream_t stream) {
+  return select_entry(logits, hidden, prev_token, A, B, W_packed, true, k, shape, mode, temperature, seed, ws,
+                      ws_bytes, out_path, out_scores, nullptr, nullptr, stream);
 }
 
 int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev_token,
@@ -287,10 +351,18 @@ int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev
                      void* ws, size_t ws_bytes, int32_t* out_path, float* out_scores,
                      float* out_q, int32_t* out_cand, hipStream_t stream) {
   if (!out_q || !out_cand) return DFS_E_NULL;
-  if (!aligned(out_q, 4) || !aligned(out_cand, 4)) return DFS_E_ALIGN;
-  if (!(std::isfinite(temperature) && temperature > 0.0)) return DFS_E_ARG;
-  return select_impl(logits, hidden, prev_token, A, B, W_h, k, shape, mode, temperature, seed, ws,
-                     ws_bytes, out_path, out_scores, out_q, out_cand, stream);
+  return select_entry(logits, hidden, prev_token, A, B, W_h, false, k, shape, mode, temperature, seed, ws,
+                      ws_bytes, out_path, out_scores, out_q, out_cand, stream);
+}
+
+int dfs_select_draft_packed(const void* logits, const void* hidden, const int32_t* prev_token,
+                            const void* A, const void* B, const void* W_packed, int k,
+                            const dfs_shape_t* shape, dfs_walk_t mode, double temperature, uint64_t seed,
+                            void* ws, size_t ws_bytes, int32_t* out_path, float* out_scores,
+                            float* out_q, int32_t* out_cand, hipStream_t stream) {
+  if (!out_q || !out_cand) return DFS_E_NULL;
+  return select_entry(logits, hidden, prev_token, A, B, W_packed, true, k, shape, mode, temperature, seed, ws,
+                      ws_bytes, out_path, out_scores, out_q, out_cand, stream);
 }
 
 size_t dfs_verify_workspace_bytes(int64_t batch, int64_t L, int64_t V, dfs_dtype_t dt) {
@@ -332,11 +404,6 @@ static int check_conv2_shape(int64_t batch, int64_t L, int64_t D, int dt) {
   if (batch * L * D > kMaxConvElems) return DFS_E_SHAPE;
   if (dt == DFS_F32 && batch * L * D > conv2_max_f32_elems()) return DFS_E_SHAPE;
   return DFS_OK;
-}
-
-static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
-  return pa < pb + nb && pb < pa + na;
 }
 
 size_t dfs_conv2_workspace_bytes(int64_t batch, int64_t L, int64_t D, dfs_dtype_t dt) {

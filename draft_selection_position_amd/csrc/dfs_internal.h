@@ -21,6 +21,17 @@ struct PackJob {
   int nslabs;
 };
 
+// A gate GEMM for few rows, as a list of independent 256-thread jobs (gate_tile.h):
+// bf16 (pre-packed W_h) 16-row tiles or fp32 8-row tiles; job j = row tile j % mtiles of
+// K split j / mtiles.  kchunk: k per split (a multiple of 32 for bf16).
+struct GateJobs {
+  const void* H = nullptr;
+  const void* W = nullptr;  // packed (bf16) or as stored (fp32)
+  int64_t rows = 0, d = 0, kchunk = 0;
+  int mtiles = 0, splits = 0;  // mtiles * splits jobs (0: none)
+  float* partial = nullptr;    // [splits, rows, 256] when splits > 1
+  float* out = nullptr;        // [rows, 256] when splits == 1
+};
 // ---------------------------------------------------------------- top-16
 struct TopkPlan {
   int64_t rows, V;
@@ -37,18 +48,10 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
                        float* out_val, void* ws, hipStream_t stream,
                        const PackJob* pack = nullptr, bool merge = true);
 
-// Merge of split rows' partial lists as extra workgroups of a later launch.
-struct MergeJob {
-  const uint64_t* partial;  // [rows, parts, 16]
-  int parts;                // 0: nothing to merge
-  int64_t rows;
-  int32_t* out_idx;
-  float* out_val;
-};
-inline MergeJob topk_merge_job(const TopkPlan& p, const void* ws, int32_t* out_idx, float* out_val) {
-  if (p.parts <= 1) return MergeJob{nullptr, 0, 0, nullptr, nullptr};
-  return MergeJob{static_cast<const uint64_t*>(ws), p.parts, p.rows, out_idx, out_val};
-}
+// The top-16 pass (merge false) with the gate's jobs as extra workgroups of the same
+// launch (ahead of the rows), for few rows; gate_bf16 selects the gate tile kind.
+hipError_t launch_topk_gate(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx, float* out_val,
+                            void* ws, const GateJobs& g, bool gate_bf16, hipStream_t stream);
 
 // Merge of per-row partial top-16 lists [rows, parts, 16] (64-bit keys, 0 = empty).
 hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, int32_t* out_idx,
@@ -56,32 +59,38 @@ hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, i
 
 // ---------------------------------------------------------------- gate
 struct GatePlan {
+  enum Kind { kJobs = 0, kTile64 = 1, kDma = 2 };
   int64_t rows, d;
   bool bf16;
-  int splits;          // K-splits (partial sums reduced by the finish kernel)
+  int kind;            // kJobs: independent 256-thread tiles (bf16 16 rows, fp32 8 rows);
+                       // kTile64: 64-row tiles of eight waves; kDma: 128 x 128 LDS-DMA tiles
+  int mtiles;          // row tiles
+  int splits;          // K splits (partial sums added in split order before the sigmoid)
   int64_t kchunk;      // hidden elements per split
-  int row_tiles;       // 16-row MFMA tiles per wave (bf16 path, 64-row tiles)
-  bool dma;            // bf16 on 128 x 128 LDS-DMA tiles (many rows, d a multiple of 32)
   size_t packed_off, packed_bytes;    // W_h packed for the matrix cores (bf16 path)
   size_t partial_off, partial_bytes;  // [splits, rows, 256] fp32
   size_t ws_bytes;
 };
 GatePlan plan_gate(int64_t rows, int64_t d, bool bf16);
-// The whole gate: pack W_h (bf16), GEMM, finish (when split).
-hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, float* out_gate,
+// Bytes of W_h [d, 256] bf16 packed for the matrix cores: [ceil(d/32)][256][32], zero past d.
+size_t gate_packed_bytes(int64_t d);
+hipError_t launch_gate_pack(const void* W_h, int64_t d, void* Wp, hipStream_t stream);
+// The whole gate: pack W_h into the workspace (bf16, unless `prepacked`: W_h is then
+// the packed weight), GEMM, finish (when split).
+hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, bool prepacked, float* out_gate,
                        void* ws, hipStream_t stream);
 // Its parts, for callers that place them themselves.  The packing job (bf16 only;
 // nslabs == 0 otherwise) must complete before the GEMM; with splits > 1 the GEMM
 // leaves partial sums [splits, rows, 256] at gate_partials() and out_gate is only
-// written by the finish.
+// written by the finish.  W: the packed weight (bf16) or W_h as stored (fp32).
 PackJob gate_pack_job(const GatePlan& p, const void* W_h, void* ws);
-// `merge` (may be null or empty): the split rows' top-16 merge runs as extra
-// workgroups of the GEMM launch.
-hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W_h,
-                            float* out_gate, void* ws, hipStream_t stream,
-                            const MergeJob* merge = nullptr);
+const void* gate_packed_in_ws(const GatePlan& p, const void* ws);
+hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W, float* out_gate, void* ws,
+                            hipStream_t stream);
 hipError_t launch_gate_finish(const GatePlan& p, float* out_gate, void* ws, hipStream_t stream);
 const float* gate_partials(const GatePlan& p, const void* ws);
+// kind == kJobs: the GEMM as independent workgroup jobs another launch can carry.
+GateJobs gate_jobs(const GatePlan& p, const void* hidden, const void* W, float* out_gate, void* ws);
 
 // ---------------------------------------------------------------- pair scores and walk
 struct WalkArgs {
@@ -91,20 +100,28 @@ struct WalkArgs {
   float* out_q = nullptr;       // optional [B, L, 16] draft distributions (fused walk only)
   int32_t* out_cand = nullptr;  // with out_q: [B, L, 16] candidate ids
 };
-// Where the pair kernel finds the gate: the finished gate [rows, 256] (splits 1),
-// or up to pair_max_gate_splits() K-split partial sums [splits, rows, 256], `stride`
-// floats apart, which it adds up in split order and passes through the sigmoid.
+// Where the pair kernel finds the gate: the finished gate [rows, 256] (splits 1), or
+// K-split partial sums [splits, rows, 256], `stride` floats apart, which it adds up in
+// split order and passes through the sigmoid (the gate's finish kernel does the same).
 struct GateSrc {
   const float* gate;
   int splits;
   int64_t stride;
 };
-int pair_max_gate_splits();
+// Where it finds the candidates: final lists idx / val [rows, 16] (parts <= 1), or the
+// top-16 pass's `parts` (2..64) sorted partial lists per row [rows, parts, 16] of 64-bit
+// keys, which it merges itself.
+struct CandSrc {
+  const int32_t* idx;
+  const float* val;
+  const uint64_t* partial;
+  int parts;
+};
+inline CandSrc cand_lists(const int32_t* idx, const float* val) { return CandSrc{idx, val, nullptr, 1}; }
 // Pair scores for every (sequence, position); optionally written to out_pair and
 // optionally followed by the walk in the same kernel (out_path/out_scores non-null).
-hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
-                            const int32_t* prev_token, const GateSrc& gate, const void* A,
-                            const void* B, bool bf16_tables, int64_t batch, int64_t L,
+hipError_t launch_pair_walk(const CandSrc& cand, const int32_t* prev_token, const GateSrc& gate,
+                            const void* A, const void* B, bool bf16_tables, int64_t batch, int64_t L,
                             int64_t V, float* out_pair, const WalkArgs* walk, int32_t* out_path,
                             float* out_scores, hipStream_t stream);
 hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L,

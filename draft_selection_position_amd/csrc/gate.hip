@@ -7,21 +7,25 @@
 //
 // bf16 path (gfx950 matrix cores): Z[rows, 256] = H[rows, d] x W_h[d, 256] with
 // V_MFMA_F32_16X16X32_BF16.  The MFMA wants every lane's operand to be 8
-// consecutive k values, but W_h is n-contiguous, so W_h is first repacked once per
-// call into [d/32][256][32] (gate_pack.h; 2.6 MB at d = 5120, stays in L2) and both
-// operands are then read straight from memory with 16-byte loads.  From 512 rows
-// (d a multiple of 32) the product runs on 128 x 128 LDS-DMA tiles (gate_dma_kernel,
-// below); for fewer rows a workgroup computes a 64-row x 256-column tile over one K
-// split, each of its 8 waves 32 columns.  Row counts too small to fill the chip split
-// K, and the partial sums are added in split order (by the finish kernel here, or by
-// the pair kernel that reads the gate) before the sigmoid.  Either GEMM launch can
-// carry the merge of split top-16 rows as extra workgroups (dfs_select).
-// fp32 path: plain FMA over a [8 rows x 256 columns] tile per workgroup.
+// consecutive k values, but W_h is n-contiguous, so W_h is repacked into
+// [ceil(d/32)][256][32] (gate_pack.h; 2.6 MB at d = 5120): by the caller once
+// (dfs_gate_pack), or per call into the workspace.  Both operands are then read
+// straight from memory with 16-byte loads.  Three tilings, one operand layout (so
+// a K split adds the same products in the same order in each):
+//   - up to 64 rows: 16-row x 256-column tiles of four waves (gate_tile.h), K split
+//     across workgroups; the same tiles ride in the top-16 launch of the fused
+//     selector when W_h comes pre-packed;
+//   - from 512 rows (d a multiple of 32): 128 x 128 LDS-DMA tiles (gate_dma_kernel);
+//   - in between: 64-row x 256-column tiles of eight waves sharing the H tile in LDS.
+// Row counts too small to fill the chip split K; the partial sums are added in split
+// order (by the finish kernel here, or by the pair kernel that reads the gate) before
+// the sigmoid.
+// fp32 path: plain FMA over [8 rows x 256 columns] tiles (gate_tile.h).
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "gate_pack.h"
+#include "gate_tile.h"
 #include "mfma_big.h"
-#include "topk_merge.h"
 
 namespace dfs {
 namespace {
@@ -36,6 +40,18 @@ static_assert(kKB == kPackK, "the GEMM steps through W_h one packed slab at a ti
 #define DFS_GATE_TARGET_WG 256
 #endif
 constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims for
+// Few rows (16-row tiles): up to this many rows, about this many workgroups, at least
+// this many k steps per split.
+#ifndef DFS_GATE_SMALL_ROWS
+#define DFS_GATE_SMALL_ROWS 64
+#endif
+#ifndef DFS_GATE_SMALL_WG
+#define DFS_GATE_SMALL_WG 32
+#endif
+#ifndef DFS_GATE_SMALL_MIN_STEPS
+#define DFS_GATE_SMALL_MIN_STEPS 4
+#endif
+static_assert(kThreads == gtile::kThreads, "gate tiles are 256-thread workgroups");
 
 __global__ __launch_bounds__(kPackThreads) void pack_w_kernel(const uint16_t* __restrict__ W,
                                                               int64_t d, uint16_t* __restrict__ Wp) {
@@ -72,22 +88,11 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
                                                                  int64_t rows, int64_t d,
                                                                  int64_t kchunk, int splits,
                                                                  float* __restrict__ partial,
-                                                                 float* __restrict__ out,
-                                                                 int gemm_blocks, MergeJob mj) {
+                                                                 float* __restrict__ out) {
   constexpr int kPitch = kKB + 16;  // bf16 per LDS row of the H tile (+32 bytes: fewest bank conflicts)
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM][kPitch];
   __shared__ __attribute__((aligned(16))) float sOut[kTileM][kOutPitch];
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x >= gemm_blocks) {  // a merge job: two rows, four waves each
-    __shared__ uint64_t s_merge[2][kMergeWaves * kK];
-    const int g = tid >> 8;
-    const int64_t row = 2 * (int64_t)(blockIdx.x - gemm_blocks) + g;
-    const bool live = row < mj.rows;
-    const int64_t rr = live ? row : 0;
-    merge_row_lists(mj.partial + rr * mj.parts * kK, mj.parts, live, (tid >> 6) & 3, tid & (kWave - 1),
-                    s_merge[g], mj.out_idx + rr * kK, mj.out_val + rr * kK);
-    return;
-  }
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int r = lane & 15;
@@ -206,16 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* _
                                                                int64_t rows, int64_t d, int mtiles,
                                                                int splits, int kps, int per_xcd,
                                                                float* __restrict__ partial,
-                                                               float* __restrict__ out, MergeJob mj) {
+                                                               float* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds[kDmaLds];
-  if (blockIdx.x >= 8u * (unsigned)per_xcd) {  // a merge job (split top-16 rows): one row
-    static_assert(kThreads == kMergeWaves * kWave, "one row per workgroup");
-    __shared__ uint64_t s_merge[kMergeWaves * kK];
-    const int64_t row = blockIdx.x - 8u * (unsigned)per_xcd;
-    merge_row_lists(mj.partial + row * mj.parts * kK, mj.parts, true, threadIdx.x >> 6,
-                    threadIdx.x & (kWave - 1), s_merge, mj.out_idx + row * kK, mj.out_val + row * kK);
-    return;
-  }
   const int64_t t = (int64_t)(blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
   if (t >= (int64_t)splits * mtiles * 2) return;
   const int nh = (int)(t & 1);
@@ -259,76 +256,13 @@ __global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* _
   }
 }
 
-// ---------------------------------------------------------------- fp32 path
-constexpr int kF32Rows = 8;     // rows per workgroup
-constexpr int kF32KBlock = 256; // k staged in LDS at a time
-constexpr int kF32Unroll = 16;  // W_h loads in flight per thread
-
-// One thread per output column n, eight rows per workgroup, k range of one split.
-// The H rows of each k block are staged in LDS (read back as broadcasts); the
-// W_h column values are loaded 16 ahead of the FMAs.  Accumulation is in k order.
-__global__ __launch_bounds__(kThreads) void gate_f32_kernel(const float* __restrict__ H,
-                                                            const float* __restrict__ W,
-                                                            int64_t rows, int64_t d,
-                                                            int64_t kchunk, int splits,
-                                                            float* __restrict__ partial,
-                                                            float* __restrict__ out, int mtiles,
-                                                            MergeJob mj) {
-  __shared__ float sH[kF32Rows][kF32KBlock];
-  const int n = threadIdx.x;
-  const int gemm_blocks = mtiles * splits;
-  if ((int)blockIdx.x >= gemm_blocks) {  // a merge job: one row
-    static_assert(kThreads == kMergeWaves * kWave, "one row per workgroup");
-    __shared__ uint64_t s_merge[kMergeWaves * kK];
-    const int64_t row = blockIdx.x - gemm_blocks;
-    merge_row_lists(mj.partial + row * mj.parts * kK, mj.parts, true, n >> 6, n & (kWave - 1), s_merge,
-                    mj.out_idx + row * kK, mj.out_val + row * kK);
-    return;
-  }
-  const int64_t m0 = (int64_t)(blockIdx.x % mtiles) * kF32Rows;
-  const int s = (int)(blockIdx.x / mtiles);
-  const int64_t k0 = (int64_t)s * kchunk;
-  const int64_t k1 = k0 + kchunk < d ? k0 + kchunk : d;
-  float acc[kF32Rows];
-#pragma unroll
-  for (int i = 0; i < kF32Rows; ++i) acc[i] = 0.0f;
-  for (int64_t kb = k0; kb < k1; kb += kF32KBlock) {
-    const int kc = (int)(k1 - kb < kF32KBlock ? k1 - kb : kF32KBlock);
-    __syncthreads();  // the previous block has been consumed
-    for (int e = n; e < kF32Rows * kF32KBlock; e += kThreads) {
-      const int i = e / kF32KBlock, kk = e % kF32KBlock;
-      float v = 0.0f;
-      if (kk < kc && m0 + i < rows) v = H[(m0 + i) * d + kb + kk];
-      sH[i][kk] = v;
-    }
-    __syncthreads();
-    int k = 0;
-    for (; k + kF32Unroll <= kc; k += kF32Unroll) {
-      float w[kF32Unroll];
-#pragma unroll
-      for (int u = 0; u < kF32Unroll; ++u) w[u] = W[(kb + k + u) * kE + n];
-#pragma unroll
-      for (int u = 0; u < kF32Unroll; ++u)
-#pragma unroll
-        for (int i = 0; i < kF32Rows; ++i) acc[i] = fmaf(sH[i][k + u], w[u], acc[i]);
-    }
-    for (; k < kc; ++k) {
-      const float w = W[(kb + k) * kE + n];
-#pragma unroll
-      for (int i = 0; i < kF32Rows; ++i) acc[i] = fmaf(sH[i][k], w, acc[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kF32Rows; ++i) {
-    const int64_t m = m0 + i;
-    if (m < rows) {
-      if (splits == 1) {
-        out[m * kE + n] = sigmoidf(acc[i]);
-      } else {
-        partial[((int64_t)s * rows + m) * kE + n] = acc[i];
-      }
-    }
-  }
+// ---------------------------------------------------------------- few rows, fp32
+// Independent 256-thread tiles (gate_tile.h): bf16 16-row tiles on the packed W_h, or
+// fp32 8-row tiles; workgroup j is job j.
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void gate_jobs_kernel(GateJobs g) {
+  __shared__ float sH[gtile::kF32Rows][gtile::kF32KBlock];
+  run_gate_job(g, kBf16, blockIdx.x, threadIdx.x, sH);
 }
 
 // out[m, n] = sigmoid(sum over splits, in split order).  The loads are issued
@@ -363,12 +297,26 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   size_t off = 0;
   if (bf16) {
     const int64_t KB = cdiv(d, kKB);
-    p.dma = rows >= DFS_GATE_DMA_ROWS && d % kKB == 0;
-    // one workgroup per CU; at least two k steps per split (eight on the DMA ring)
-    const int64_t items = p.dma ? cdiv(rows, kDmaBM) * 2 : cdiv(rows, kTileM);
-    p.row_tiles = p.dma ? 0 : kTileM / 16;
-    int64_t splits = cdiv(kTargetWG, items);
-    const int64_t min_steps = p.dma ? 8 : 2;
+    int64_t splits, min_steps;
+    if (rows <= DFS_GATE_SMALL_ROWS) {
+      // few rows: 16-row tiles, K split over about kSmallWG workgroups (at least
+      // kSmallMinSteps k steps each, so that a tile's loads overlap)
+      p.kind = GatePlan::kJobs;
+      p.mtiles = (int)cdiv(rows, gtile::kRows16);
+      splits = cdiv(DFS_GATE_SMALL_WG, p.mtiles);
+      min_steps = DFS_GATE_SMALL_MIN_STEPS;
+    } else if (rows >= DFS_GATE_DMA_ROWS && d % kKB == 0) {
+      // one workgroup per CU; at least eight k steps per split on the DMA ring
+      p.kind = GatePlan::kDma;
+      p.mtiles = (int)cdiv(rows, kDmaBM);
+      splits = cdiv(kTargetWG, (int64_t)p.mtiles * 2);
+      min_steps = 8;
+    } else {
+      p.kind = GatePlan::kTile64;
+      p.mtiles = (int)cdiv(rows, kTileM);
+      splits = cdiv(kTargetWG, p.mtiles);
+      min_steps = 2;
+    }
     const int64_t max_splits = KB / min_steps > 1 ? KB / min_steps : 1;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
@@ -376,12 +324,12 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
     p.kchunk = kb_per * kKB;
     p.splits = (int)cdiv(KB, kb_per);
     p.packed_off = 0;
-    p.packed_bytes = align_up((size_t)KB * kE * kKB * sizeof(uint16_t), 256);
+    p.packed_bytes = gate_packed_bytes(d);
     off = p.packed_bytes;
   } else {
-    p.row_tiles = 0;
-    const int64_t mtiles = cdiv(rows, kF32Rows);
-    int64_t splits = cdiv(kTargetWG, mtiles);
+    p.kind = GatePlan::kJobs;
+    p.mtiles = (int)cdiv(rows, gtile::kF32Rows);
+    int64_t splits = cdiv(kTargetWG, p.mtiles);
     const int64_t max_splits = d / 64 > 1 ? d / 64 : 1;  // at least 64 k per split
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
@@ -396,6 +344,8 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   return p;
 }
 
+size_t gate_packed_bytes(int64_t d) { return align_up((size_t)cdiv(d, kKB) * kE * kKB * sizeof(uint16_t), 256); }
+
 PackJob gate_pack_job(const GatePlan& p, const void* W_h, void* ws) {
   if (!p.bf16) return PackJob{nullptr, 0, nullptr, 0};
   return PackJob{static_cast<const uint16_t*>(W_h), p.d,
@@ -403,36 +353,45 @@ PackJob gate_pack_job(const GatePlan& p, const void* W_h, void* ws) {
                  (int)cdiv(p.d, kKB)};
 }
 
+const void* gate_packed_in_ws(const GatePlan& p, const void* ws) {
+  return static_cast<const char*>(ws) + p.packed_off;
+}
+
 const float* gate_partials(const GatePlan& p, const void* ws) {
   return p.splits > 1 ? reinterpret_cast<const float*>(static_cast<const char*>(ws) + p.partial_off)
                       : nullptr;
 }
 
-hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W_h,
-                            float* out_gate, void* ws, hipStream_t stream, const MergeJob* merge) {
-  const MergeJob mj = merge && merge->parts > 1 ? *merge : MergeJob{nullptr, 0, 0, nullptr, nullptr};
+GateJobs gate_jobs(const GatePlan& p, const void* hidden, const void* W, float* out_gate, void* ws) {
+  if (p.kind != GatePlan::kJobs) return GateJobs{};
+  float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.partial_off) : nullptr;
+  return GateJobs{hidden, W, p.rows, p.d, p.kchunk, p.mtiles, p.splits, partial, out_gate};
+}
+
+hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W, float* out_gate, void* ws,
+                            hipStream_t stream) {
   char* wsb = static_cast<char*>(ws);
   float* partial = p.splits > 1 ? reinterpret_cast<float*>(wsb + p.partial_off) : nullptr;
-  if (p.bf16) {
-    const uint16_t* Wp = reinterpret_cast<const uint16_t*>(wsb + p.packed_off);
-    const uint16_t* H = static_cast<const uint16_t*>(hidden);
-    if (p.dma) {
-      const int mtiles = (int)cdiv(p.rows, kDmaBM);
-      const int per_xcd = (int)cdiv((int64_t)p.splits * mtiles * 2, 8);
-      gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd + mj.rows)), kThreads, 0, stream>>>(
-          H, Wp, p.rows, p.d, mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate, mj);
+  if (p.kind == GatePlan::kJobs) {
+    const GateJobs g = gate_jobs(p, hidden, W, out_gate, ws);
+    const dim3 grid((unsigned)((int64_t)g.mtiles * g.splits));
+    if (p.bf16) {
+      gate_jobs_kernel<true><<<grid, kThreads, 0, stream>>>(g);
     } else {
-      const int gemm_blocks = (int)(cdiv(p.rows, kTileM) * p.splits);
-      const dim3 grid((unsigned)(gemm_blocks + cdiv(mj.rows, 2)));
-      gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits,
-                                                           partial, out_gate, gemm_blocks, mj);
+      gate_jobs_kernel<false><<<grid, kThreads, 0, stream>>>(g);
     }
   } else {
-    const int mtiles = (int)cdiv(p.rows, kF32Rows);
-    const dim3 grid((unsigned)((int64_t)mtiles * p.splits + mj.rows));
-    gate_f32_kernel<<<grid, kThreads, 0, stream>>>(static_cast<const float*>(hidden),
-                                                   static_cast<const float*>(W_h), p.rows, p.d,
-                                                   p.kchunk, p.splits, partial, out_gate, mtiles, mj);
+    const uint16_t* Wp = static_cast<const uint16_t*>(W);
+    const uint16_t* H = static_cast<const uint16_t*>(hidden);
+    if (p.kind == GatePlan::kDma) {
+      const int per_xcd = (int)cdiv((int64_t)p.splits * p.mtiles * 2, 8);
+      gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd)), kThreads, 0, stream>>>(
+          H, Wp, p.rows, p.d, p.mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate);
+    } else {
+      const dim3 grid((unsigned)((int64_t)p.mtiles * p.splits));
+      gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits, partial,
+                                                           out_gate);
+    }
   }
   return hipGetLastError();
 }
@@ -445,13 +404,21 @@ hipError_t launch_gate_finish(const GatePlan& p, float* out_gate, void* ws, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, float* out_gate,
+hipError_t launch_gate_pack(const void* W_h, int64_t d, void* Wp, hipStream_t stream) {
+  pack_w_kernel<<<dim3((unsigned)cdiv(d, kKB)), kPackThreads, 0, stream>>>(static_cast<const uint16_t*>(W_h), d,
+                                                                        static_cast<uint16_t*>(Wp));
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(const GatePlan& p, const void* hidden, const void* W_h, bool prepacked, float* out_gate,
                        void* ws, hipStream_t stream) {
-  if (p.bf16) {
+  const void* W = W_h;
+  if (p.bf16 && !prepacked) {
     const PackJob job = gate_pack_job(p, W_h, ws);
     pack_w_kernel<<<dim3((unsigned)job.nslabs), kPackThreads, 0, stream>>>(job.W, job.d, job.Wp);
+    W = job.Wp;
   }
-  hipError_t e = launch_gate_gemm(p, hidden, W_h, out_gate, ws, stream);
+  hipError_t e = launch_gate_gemm(p, hidden, W, out_gate, ws, stream);
   if (e != hipSuccess) return e;
   return launch_gate_finish(p, out_gate, ws, stream);
 }

@@ -24,6 +24,7 @@
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "philox.h"
+#include "topk_merge.h"
 
 namespace dfs {
 namespace {
@@ -202,34 +203,44 @@ __device__ __forceinline__ void draft_q(const float (*sS)[kK][kK], const WalkTab
   }
 }
 
-// Gate splits the pair kernel adds up itself (more are finished by a kernel of
-// their own first).
-#ifndef DFS_PAIR_GATE_SPLITS
-#define DFS_PAIR_GATE_SPLITS 4
-#endif
-constexpr int kMaxGateSplits = DFS_PAIR_GATE_SPLITS;
+// The gate row of a position, one 16-byte piece [4 lane, + 4) per lane: the finished
+// gate (splits == 1), or the K-split partial sums [splits, rows, 256] (row stride
+// `stride` between splits) added in split order from zero, exactly as the gate's finish
+// kernel adds them, then passed through the sigmoid.  gate_issue puts the first round
+// of loads (up to 16 splits) in flight without waiting for any; gate_finish adds them
+// up, loading any further rounds.  The guards are wave-uniform branches, not predicated
+// loads.
+constexpr int kGateRound = 16;
+struct GateRegs {
+  float4 v[kGateRound];
+};
 
-// This lane's 16-byte piece [4 lane, + 4) of the gate row `row`: the finished gate
-// (splits == 1), or the K-split partial sums [splits, rows, 256] (row stride
-// `stride` between splits) added in split order from zero, exactly as the finish
-// kernel adds them, then passed through the sigmoid.  The loads are not
-// predicated (a clamped split index), so none waits for another.
-__device__ __forceinline__ float4 gate_piece(const float* __restrict__ gate, int splits,
-                                             int64_t stride, int64_t row, int lane) {
-  const float* p = gate + row * kE + 4 * lane;
-  float4 v[kMaxGateSplits];
+__device__ __forceinline__ void gate_load_round(const float* p, int s0, int splits, int64_t stride, GateRegs& g) {
 #pragma unroll
-  for (int u = 0; u < kMaxGateSplits; ++u)
-    v[u] = *reinterpret_cast<const float4*>(p + (int64_t)(u < splits ? u : splits - 1) * stride);
-  if (splits == 1) return v[0];
+  for (int u = 0; u < kGateRound; ++u)
+    if (s0 + u < splits) g.v[u] = *reinterpret_cast<const float4*>(p + (int64_t)(s0 + u) * stride);
+}
+
+__device__ __forceinline__ void gate_issue(const float* __restrict__ gate, int splits, int64_t stride,
+                                           int64_t row, int lane, GateRegs& g) {
+  gate_load_round(gate + row * kE + 4 * lane, 0, splits, stride, g);
+}
+
+__device__ __forceinline__ float4 gate_finish(const float* __restrict__ gate, int splits, int64_t stride,
+                                              int64_t row, int lane, GateRegs& g) {
+  if (splits == 1) return g.v[0];
   float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float* p = gate + row * kE + 4 * lane;
+  for (int s0 = 0; s0 < splits; s0 += kGateRound) {
+    if (s0 > 0) gate_load_round(p, s0, splits, stride, g);
 #pragma unroll
-  for (int u = 0; u < kMaxGateSplits; ++u) {
-    if (u < splits) {
-      z.x += v[u].x;
-      z.y += v[u].y;
-      z.z += v[u].z;
-      z.w += v[u].w;
+    for (int u = 0; u < kGateRound; ++u) {
+      if (s0 + u < splits) {
+        z.x += g.v[u].x;
+        z.y += g.v[u].y;
+        z.z += g.v[u].z;
+        z.w += g.v[u].w;
+      }
     }
   }
   return make_float4(sigmoidf(z.x), sigmoidf(z.y), sigmoidf(z.z), sigmoidf(z.w));
@@ -241,6 +252,7 @@ __device__ __forceinline__ float4 gate_piece(const float* __restrict__ gate, int
 template <bool kBf16Tables, bool kWritePair, bool kWalk>
 __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4, 4))) void pair_walk_kernel(
     const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_val,
+    const uint64_t* __restrict__ partial, int parts,
     const int32_t* __restrict__ prev_token, const float* __restrict__ gate, int gate_splits,
     int64_t gate_stride, const void* __restrict__ A_, const void* __restrict__ B_, int L,
     int64_t V, float* __restrict__ out_pair, int mode, double temperature, uint64_t seed,
@@ -249,6 +261,9 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   __shared__ WalkTables sW;
   __shared__ __attribute__((aligned(16))) float sG[kMaxL][kE];  // gate row of each position
   __shared__ float sS[kWalk ? kMaxL : 1][kK][kK];                // whole tiles (best-path walk)
+  __shared__ int32_t sC[kMaxL][kK];                              // merged candidates: ids
+  __shared__ float sU[kMaxL][kK];                                //   and their logits
+  __shared__ uint64_t sMerge[kMaxL][kMergeBatch];                // merge buffers, one per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;  // block position of this wave
   const int64_t b = blockIdx.x;
@@ -256,21 +271,45 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   const int q = lane >> 4;  // embedding quarter [64q, 64q + 64)
   const int64_t row = b * L + t;
 
-  // (a pointer select, not a branch: no load has to wait for another)
-  const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
-  const int32_t pred_id = *pred_p;
-  const int32_t cand_id = cand_idx[row * kK + r];
-  const float u = cand_val[row * kK + r];
+  int32_t pred_id, cand_id;
+  float u;
+  GateRegs gr;
+  if (parts <= 1) {
+    // The candidates are final lists (cand_idx / cand_val).  The gate row does not
+    // depend on them: its loads go out with the id loads (a pointer select, not a
+    // branch: no load has to wait for another).
+    const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
+    pred_id = *pred_p;
+    cand_id = cand_idx[row * kK + r];
+    u = cand_val[row * kK + r];
+    gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
+  } else {
+    // The top-16 pass left `parts` sorted partial lists per row: each wave merges its
+    // own row's, with the gate loads in flight meanwhile, and the merged lists meet in
+    // LDS (position t needs the candidates of position t - 1 as predecessors).
+    MergeRegs mr;
+    merge_load(partial + row * parts * kK, parts, lane, mr);
+    const int32_t prev = prev_token[b];
+    gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
+    const uint64_t key = merge_keys(mr, parts, lane, sMerge[t]);
+    if (lane < kK) {
+      sC[t][lane] = (int32_t)key_index(key);
+      sU[t][lane] = key_value(key);
+    }
+    __syncthreads();
+    pred_id = t == 0 ? prev : sC[t - 1][r];
+    cand_id = sC[t][r];
+    u = sU[t][r];
+  }
   // Ids outside [0, V) break the caller's contract; clamp them so that no gather
   // leaves the tables.
   const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
   const int64_t cand = cand_id < 0 ? 0 : (cand_id >= V ? V - 1 : cand_id);
 
-  // The gate row does not depend on the candidate ids: it is fetched (one 16-byte
-  // piece per lane) before the ids arrive and parked in LDS, so that the table-row
-  // fragments can all be in flight at once right after.  The scheduling barriers
-  // keep that order; the row is read back by other lanes of the same wave only.
-  const float4 gp = gate_piece(gate, gate_splits, gate_stride, row, lane);
+  // The gate row is parked in LDS before the table-row fragments are loaded, so that
+  // all of them can be in flight at once; the scheduling barriers keep that order.  The
+  // row is read back by other lanes of the same wave only.
+  const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
   __builtin_amdgcn_sched_barrier(0);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kBf16Tables) {
@@ -315,8 +354,8 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
                                                        4 * q);
     *reinterpret_cast<float4*>(&sG[t][4 * lane]) = gp;
     __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-    for (int c = 0; c < 16; ++c) {
+#pragma unroll 8
+    for (int c = 0; c < 16; ++c) {  // two rounds of 8 + 8 row loads in flight
       const float4 a = Ap[4 * c], bb = Bp[4 * c];
       const float4 g = *reinterpret_cast<const float4*>(&sG[t][16 * c + 4 * q]);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
@@ -387,32 +426,28 @@ __global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __rest
 }
 
 template <bool kBf16, bool kWritePair, bool kWalk>
-void launch_pw(int64_t batch, int64_t L, int64_t V, const int32_t* cand_idx, const float* cand_val,
-               const int32_t* prev_token, const GateSrc& g, const void* A, const void* B,
-               float* out_pair, const WalkArgs* w, int32_t* out_path, float* out_scores,
-               hipStream_t stream) {
+void launch_pw(int64_t batch, int64_t L, int64_t V, const CandSrc& c, const int32_t* prev_token,
+               const GateSrc& g, const void* A, const void* B, float* out_pair, const WalkArgs* w,
+               int32_t* out_path, float* out_scores, hipStream_t stream) {
   pair_walk_kernel<kBf16, kWritePair, kWalk><<<dim3((unsigned)batch), dim3((unsigned)(kWave * L)),
                                                 0, stream>>>(
-      cand_idx, cand_val, prev_token, g.gate, g.splits, g.stride, A, B, (int)L, V, out_pair,
+      c.idx, c.val, c.partial, c.parts, prev_token, g.gate, g.splits, g.stride, A, B, (int)L, V, out_pair,
       w ? w->mode : 0, w ? w->temperature : 1.0, w ? w->seed : 0ull, out_path, out_scores,
       w ? w->out_q : nullptr, w ? w->out_cand : nullptr);
 }
 
 }  // namespace
 
-int pair_max_gate_splits() { return kMaxGateSplits; }
-
-hipError_t launch_pair_walk(const int32_t* cand_idx, const float* cand_val,
-                            const int32_t* prev_token, const GateSrc& gate, const void* A,
-                            const void* B, bool bf16_tables, int64_t batch, int64_t L,
+hipError_t launch_pair_walk(const CandSrc& cand, const int32_t* prev_token, const GateSrc& gate,
+                            const void* A, const void* B, bool bf16_tables, int64_t batch, int64_t L,
                             int64_t V, float* out_pair, const WalkArgs* walk, int32_t* out_path,
                             float* out_scores, hipStream_t stream) {
-  if (gate.splits < 1 || gate.splits > kMaxGateSplits) return hipErrorInvalidValue;
+  if (gate.splits < 1) return hipErrorInvalidValue;
+  if (cand.parts > kMaxMergeParts || (cand.parts > 1 && cand.partial == nullptr)) return hipErrorInvalidValue;
   const bool wp = out_pair != nullptr;
   const bool wk = walk != nullptr;
-#define DFS_PW(BF, WP, WK)                                                                      \
-  launch_pw<BF, WP, WK>(batch, L, V, cand_idx, cand_val, prev_token, gate, A, B, out_pair, walk,   \
-                        out_path, out_scores, stream)
+#define DFS_PW(BF, WP, WK) \
+  launch_pw<BF, WP, WK>(batch, L, V, cand, prev_token, gate, A, B, out_pair, walk, out_path, out_scores, stream)
   if (bf16_tables) {
     if (wp && wk) DFS_PW(true, true, true);
     else if (wp) DFS_PW(true, true, false);

@@ -21,6 +21,7 @@
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "gate_pack.h"
+#include "gate_tile.h"
 #include "topk_merge.h"
 
 namespace dfs {
@@ -71,6 +72,21 @@ struct Elems<false> {
   using T = float;
 };
 
+// Out-of-line copy of the 64-lane sort for the compact build of the pass (few rows),
+// where each wave runs the code about once per launch and every inlined copy would be
+// fetched cold: one copy, called from every merge and seed.
+__device__ __attribute__((noinline)) uint64_t wave_sort_desc_call(uint64_t x, int lane) {
+  return wave_sort_desc(x, lane);
+}
+template <bool kCompact>
+__device__ __forceinline__ uint64_t sort_desc(uint64_t x, int lane) {
+  if constexpr (kCompact) {
+    return wave_sort_desc_call(x, lane);
+  } else {
+    return wave_sort_desc(x, lane);
+  }
+}
+
 struct WaveTop {
   uint64_t list;  // lanes 0..15: best keys so far, descending (0 = empty slot)
   float thr;      // admission threshold, identical in every lane
@@ -78,6 +94,7 @@ struct WaveTop {
 };
 
 // Merge the buffered keys into the wave's list and raise the threshold.
+template <bool kCompact>
 __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint32_t* s_thr,
                                            int lane) {
   __builtin_amdgcn_wave_barrier();
@@ -90,7 +107,7 @@ __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint
     } else if (lane - 16 < n) {
       x = buf[cnt - n + (lane - 16)];
     }
-    x = wave_sort_desc(x, lane);
+    x = sort_desc<kCompact>(x, lane);
     w.list = lane < 16 ? x : 0;
     cnt -= n;
   }
@@ -145,7 +162,7 @@ __device__ __forceinline__ float load_scalar(const typename Elems<kBf16>::T* p, 
 // first vector (`seed`), the threshold is first raised to the 16th largest lane
 // maximum: those 16 maxima are distinct elements, so nothing below it can make
 // the top 16.
-template <bool kBf16>
+template <bool kBf16, bool kCompact>
 __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, WaveTop& w,
                                          uint64_t* buf, uint32_t* s_thr, int lane, bool seed) {
   constexpr int PV = Elems<kBf16>::per_vec;
@@ -166,7 +183,7 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
   for (int e = 1; e < PV; ++e) m = fmaxf(m, v[e]);
   if (seed) {
     const uint64_t lk = (m == m) ? make_key(m, (uint32_t)lane) : 0ull;
-    const uint64_t k16 = lane_u64(wave_sort_desc(lk, lane), 15);
+    const uint64_t k16 = lane_u64(sort_desc<kCompact>(lk, lane), 15);
     if (k16 != 0) {
       const float t = key_value(k16);
       if (t > w.thr) w.thr = uniformf(t);
@@ -175,32 +192,28 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
   if (__ballot(m >= w.thr) == 0) return;
 #pragma unroll
   for (int e = 0; e < PV; ++e) append(w, v[e] >= w.thr, v[e], idx0 + e, buf);
-  if (w.cnt > kMergeAt) wave_merge(w, buf, s_thr, lane);
+  if (w.cnt > kMergeAt) wave_merge<kCompact>(w, buf, s_thr, lane);
 }
 
-template <bool kBf16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TOPK_WAVES_PER_EU))) void topk_chunk_kernel(const void* __restrict__ logits,
-                                                              int64_t V, int parts, int64_t chunk,
-                                                              uint64_t* __restrict__ partial,
-                                                              int32_t* __restrict__ out_idx,
-                                                              float* __restrict__ out_val,
-                                                              int64_t ntopk, PackJob pack) {
+struct TopkLds {
+  uint64_t buf[kWaves][kCap];  // per-wave key buffers
+  uint64_t list[kWaves * kK];
+  uint32_t thr;
+};
+static_assert(sizeof(TopkLds::buf) >= kPackLdsBytes, "a packing job reuses the key buffers");
+static_assert(sizeof(TopkLds::buf) >= gtile::kF32LdsBytes, "a gate job reuses the key buffers");
+
+// One (row, part) of the pass: workgroup `bid` of the rows.  kCompact: the sorts are
+// out-of-line calls (few rows: each wave runs the code about once).
+template <bool kBf16, bool kCompact>
+__device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64_t V, int parts, int64_t chunk,
+                                          uint64_t* __restrict__ partial, int32_t* __restrict__ out_idx,
+                                          float* __restrict__ out_val, int64_t bid, TopkLds& lds) {
   using T = typename Elems<kBf16>::T;
   constexpr int PV = Elems<kBf16>::per_vec;
-  __shared__ uint64_t s_buf[kWaves][kCap];
-  __shared__ uint64_t s_list[kWaves * kK];
-  __shared__ uint32_t s_thr;
-  static_assert(sizeof(s_buf) >= kPackLdsBytes, "the packing job reuses the key buffers");
-
-  // packing jobs (fused selector) ride in the same grid, after or before the rows
-  const int64_t job = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ntopk;
-  const int64_t bid = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x - pack.nslabs : (int64_t)blockIdx.x;
-  if (DFS_TOPK_PACK_FIRST ? job < pack.nslabs : job >= 0) {
-    pack_w_slab(pack.W, pack.d, pack.Wp, job, threadIdx.x,
-                reinterpret_cast<uint16_t(*)[kPackPitch]>(&s_buf[0][0]));
-    return;
-  }
-
+  auto& s_buf = lds.buf;
+  auto& s_list = lds.list;
+  auto& s_thr = lds.thr;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t vid = it * step + (int64_t)u * kThreads + tid;
-        scan_vec<kBf16>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
+        scan_vec<kBf16, kCompact>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
                         &s_thr, lane, it == 0 && u == 0);
       }
     };
@@ -297,12 +310,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
     if (it < niter) scan_iter(bufA, it, kEdge);  // odd count: bufA holds the last iteration
   }
 
-  if (w.cnt > 0) wave_merge(w, buf, &s_thr, lane);
+  if (w.cnt > 0) wave_merge<kCompact>(w, buf, &s_thr, lane);
   if (lane < kK) s_list[wave * kK + lane] = w.list;
   __syncthreads();
   if (wave == 0) {
     uint64_t x = s_list[lane];  // kWaves * kK == 64 keys
-    x = wave_sort_desc(x, lane);
+    x = sort_desc<kCompact>(x, lane);
     if (lane < kK) {
       if (parts == 1) {
         out_idx[row * kK + lane] = (int32_t)key_index(x);
@@ -312,6 +325,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
       }
     }
   }
+}
+
+// The pass over `ntopk` = rows * parts workgroups; W_h packing slabs (the fused
+// selector) ride as extra workgroups after or before the rows.
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TOPK_WAVES_PER_EU))) void topk_chunk_kernel(
+    const void* __restrict__ logits, int64_t V, int parts, int64_t chunk, uint64_t* __restrict__ partial,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_val, int64_t ntopk, PackJob pack) {
+  __shared__ TopkLds lds;
+  const int64_t job = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ntopk;
+  const int64_t bid = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x - pack.nslabs : (int64_t)blockIdx.x;
+  if (DFS_TOPK_PACK_FIRST ? job < pack.nslabs : job >= 0) {
+    pack_w_slab(pack.W, pack.d, pack.Wp, job, threadIdx.x, reinterpret_cast<uint16_t(*)[kPackPitch]>(&lds.buf[0][0]));
+    return;
+  }
+  topk_body<kBf16, false>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+}
+
+// The pass with the gate's jobs (few rows) as the first workgroups of the launch: the
+// gate tiles hold more registers than the pass's 8-waves-per-SIMD budget, which few
+// rows do not need.
+template <bool kBf16, bool kGateBf16>
+__global__ __launch_bounds__(kThreads) void topk_gate_kernel(const void* __restrict__ logits, int64_t V, int parts,
+                                                             int64_t chunk, uint64_t* __restrict__ partial,
+                                                             int32_t* __restrict__ out_idx,
+                                                             float* __restrict__ out_val, GateJobs g) {
+  __shared__ TopkLds lds;
+  const int64_t njobs = (int64_t)g.mtiles * g.splits;
+  if ((int64_t)blockIdx.x < njobs) {
+    run_gate_job(g, kGateBf16, blockIdx.x, threadIdx.x, &lds.buf[0][0]);
+    return;
+  }
+  topk_body<kBf16, true>(logits, V, parts, chunk, partial, out_idx, out_val, (int64_t)blockIdx.x - njobs, lds);
 }
 
 // Merge `parts` partial top-16 lists per row (one workgroup per row).
@@ -370,6 +416,21 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
     topk_merge_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.parts, out_idx,
                                                                         out_val);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_gate(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx, float* out_val,
+                            void* ws, const GateJobs& g, bool gate_bf16, hipStream_t stream) {
+  uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
+  const dim3 grid((unsigned)(p.rows * p.parts + (int64_t)g.mtiles * g.splits));
+#define DFS_TG(LB, GB) \
+  topk_gate_kernel<LB, GB><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial, out_idx, out_val, g)
+  if (bf16) {
+    if (gate_bf16) DFS_TG(true, true); else DFS_TG(true, false);
+  } else {
+    if (gate_bf16) DFS_TG(false, true); else DFS_TG(false, false);
+  }
+#undef DFS_TG
   return hipGetLastError();
 }
 

@@ -43,4 +43,91 @@ __device__ __forceinline__ void merge_row_lists(const uint64_t* __restrict__ src
   }
 }
 
+// ---------------------------------------------------------------- one wave, one row
+// Most lists one wave merges (the top-16 pass splits a row into at most this many).
+constexpr int kMaxMergeParts = 64;
+// Keys buffered per sort: with the running list (16 lanes) they fill the wave.
+constexpr int kMergeBatch = kWave - kK;
+
+// One wave merges one row's `parts` (1..64) sorted lists of 16 keys (src [parts, 16])
+// into their top 16: lanes 0..15 of the result hold it, descending; the other lanes 0.
+// merge_load issues every load (list p's key j goes to lane 16 (p % 4) + j of group
+// p / 4); merge_keys then needs only the registers, so a caller can put other loads in
+// flight in between.  Pruning: if some list's 16th key is T, that list alone holds 16
+// keys >= T, so no key below T can be in the result; T only rises as the running list
+// fills.  The survivors are appended to `scratch` (kMergeBatch keys of LDS for this
+// wave) and sorted with the running list whenever the buffer would overflow, and once
+// at the end.  Every lane of the wave must call both.
+constexpr int kMergeGroups = kMaxMergeParts / 4;  // 4 lists per 64 lanes
+struct MergeRegs {
+  uint64_t x[kMergeGroups];
+};
+
+__device__ __forceinline__ void merge_load(const uint64_t* __restrict__ src, int parts, int lane, MergeRegs& m) {
+  const int groups = (parts + 3) >> 2;
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) {
+    m.x[g] = 0;
+    const int p = 4 * g + (lane >> 4);
+    if (g < groups && p < parts) m.x[g] = src[(int64_t)p * kK + (lane & (kK - 1))];
+  }
+}
+
+__device__ __forceinline__ uint64_t merge_keys(MergeRegs& m, int parts, int lane, uint64_t* scratch) {
+  const int groups = (parts + 3) >> 2;
+  // T = the largest 16th key of any list (lanes 15, 31, 47, 63 of each group hold them)
+  uint64_t t = 0;
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) t = ((lane & (kK - 1)) == kK - 1 && m.x[g] > t) ? m.x[g] : t;
+#pragma unroll
+  for (int j = 1; j < kWave; j <<= 1) {
+    const uint64_t o = shfl_xor_u64(t, j, lane);
+    t = o > t ? o : t;
+  }
+  uint64_t list = 0;
+  int n = 0;  // keys in the buffer (wave-uniform)
+  // One pass per group plus a final one that only flushes.  The group in hand is always
+  // m.x[0] (the registers shift down by one per pass), and the 64-lane sort has a single
+  // call site: a wave runs this code once per call, so its size, not its loop count, is
+  // what costs (every instruction fetched cold).
+#pragma unroll 1
+  for (int g = 0; g <= groups; ++g) {
+    const bool last = g == groups;
+    uint64_t v = last ? 0 : m.x[0];
+#pragma unroll
+    for (int i = 0; i + 1 < kMergeGroups; ++i) m.x[i] = m.x[i + 1];
+#pragma unroll 1
+    for (;;) {
+      const bool keep = v != 0 && v >= t;
+      const uint64_t mask = __ballot(keep);
+      if ((n == kMergeBatch && mask != 0) || (last && n > 0)) {
+        __builtin_amdgcn_wave_barrier();
+        uint64_t y = 0;
+        if (lane < kK) {
+          y = list;
+        } else if (lane - kK < n) {
+          y = scratch[lane - kK];
+        }
+        y = wave_sort_desc(y, lane);
+        list = lane < kK ? y : 0;
+        n = 0;
+        const uint64_t k16 = lane_u64(list, kK - 1);
+        t = k16 > t ? k16 : t;
+        __builtin_amdgcn_wave_barrier();
+        continue;
+      }
+      if (mask == 0) break;
+      const int room = kMergeBatch - n;
+      const int below = lanes_below(mask);
+      if (keep && below < room) {
+        scratch[n + below] = v;
+        v = 0;  // taken
+      }
+      const int c = __popcll(mask);
+      n += c < room ? c : room;
+    }
+  }
+  return list;
+}
+
 }  // namespace dfs

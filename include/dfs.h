@@ -91,6 +91,10 @@ typedef struct {
 } dfs_shape_t;
 
 /* ---------------------------------------------------------------- top-16
+ * Step 1.  The post observes that the right token is usually among the drafter's 16
+ * best candidates even when its top pick is wrong, and keeps those 16 per block
+ * position (blog post "DFlash 2: Keep Drafting Parallel", section "The Right Tokens Are
+ * Already There", Table 1's recall@16).
  * For each of `rows` rows of `logits` [rows, V] (dtype dt), the k = 16 largest
  * entries ordered by value descending, then token id ascending (ties go to the
  * lower id); -0 and +0 count as equal and +0 is reported.
@@ -104,6 +108,10 @@ int dfs_topk(const void* logits, dfs_dtype_t dt, int64_t rows, int64_t V, int k,
              int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- context gate
+ * Step 2.  The score weights each candidate pair's embedding match by a context gate
+ * computed from the drafter's hidden state, H(h_t) (section "A Lightweight Path
+ * Selector"; the symbol survives in the twiscan.com Chinese translation's equation).
+ * The pages do not say how H is built; this library takes a sigmoid of a linear map:
  * out_gate[r, e] = sigmoid( sum_c hidden[r, c] * W_h[c, e] ),  r < rows, e < E = 256.
  *   hidden [rows, d] and W_h [d, 256] of dtype dt; products and sums in fp32;
  *   out_gate [rows, 256] fp32.
@@ -113,7 +121,26 @@ size_t dfs_gate_workspace_bytes(int64_t rows, int64_t d, dfs_dtype_t dt);
 int dfs_gate(const void* hidden, const void* W_h, dfs_dtype_t dt, int64_t rows, int64_t d,
              int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* W_h packed once for the gate's matrix cores, for callers that keep the weight across
+ * calls (it is a constant of the drafter).  bf16: the packed layout is
+ * [ceil(d/32)][256][32] (slab kb, column n, then the 32 k values 32 kb .. 32 kb + 31 of
+ * that column; zero past d); fp32: a plain copy of W_h.  out_packed must hold
+ * dfs_gate_pack_bytes(d, dt) bytes (16-byte aligned) and must not overlap W_h; it is
+ * caller-owned device memory, written on `stream`.  dfs_gate_packed,
+ * dfs_select_packed and dfs_select_draft_packed take it in place of W_h and give the
+ * same bits as their unpacked forms, without repacking W_h on every call. */
+size_t dfs_gate_pack_bytes(int64_t d, dfs_dtype_t dt);
+int dfs_gate_pack(const void* W_h, dfs_dtype_t dt, int64_t d, void* out_packed, size_t out_bytes,
+                  hipStream_t stream);
+int dfs_gate_packed(const void* hidden, const void* W_packed, dfs_dtype_t dt, int64_t rows, int64_t d,
+                    int64_t E, float* out_gate, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- pair scores
+ * Step 3.  Every adjacent (predecessor a, candidate b) pair is scored at once by
+ *   S_t(a, b) = U_t(b) + < A(a) (elementwise) H(h_t), B(b) >
+ * (section "A Lightweight Path Selector", equation as printed in the twiscan.com
+ * Chinese and decomputer.nl Dutch translations; the bud-325 wiki summary notes the
+ * 16 x 16 x K score tensor is computed once).  U_t(b) is the drafter's own logit.
  * For sequence b and position t (row r = b*L + t):
  *   t >= 1:  out_pair[b, t, i, j] = cand_val[r, j]
  *              + sum_e A[cand_idx[r-1, i], e] * gate[r, e] * B[cand_idx[r, j], e]
@@ -131,6 +158,9 @@ int dfs_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_
                     hipStream_t stream);
 
 /* ---------------------------------------------------------------- walk
+ * Step 4, the only sequential work: from the last verified token, greedy follows the
+ * best successor at each step and sampling draws from the same scores (section "A
+ * Lightweight Path Selector").
  * One walk per sequence over pair [batch, L, 16, 16] (a dfs_pair_scores result):
  * start at predecessor slot 0 of position 0 (the last verified token's row); at
  * step t choose slot j* in row i (the previous choice):
@@ -166,6 +196,12 @@ int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token
                const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
                double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                float* out_scores, hipStream_t stream);
+/* dfs_select with W_h already packed by dfs_gate_pack (the same bits).  With few rows
+ * (batch * L <= 64) the gate then runs inside the top-16 launch: two kernels per call. */
+int dfs_select_packed(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                      const void* B, const void* W_packed, int k, const dfs_shape_t* shape, dfs_walk_t mode,
+                      double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+                      float* out_scores, hipStream_t stream);
 
 /* ---------------------------------------------------------------- draft distributions
  * dfs_select plus the draft distribution the walk drew from at every position:
@@ -180,6 +216,12 @@ int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev
                      const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
                      uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                      float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream);
+/* dfs_select_draft with W_h packed by dfs_gate_pack. */
+int dfs_select_draft_packed(const void* logits, const void* hidden, const int32_t* prev_token,
+                            const void* A, const void* B, const void* W_packed, int k,
+                            const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
+                            uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+                            float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream);
 
 /* ---------------------------------------------------------------- verification
  * Speculative-sampling verification of drafted blocks (Leviathan, Kalman and Matias,
@@ -259,7 +301,7 @@ int dfs_lmhead_logits(const void* hidden, const void* W_lm, dfs_dtype_t dt, int6
 const char* dfs_status_str(int status);
 
 /* ABI version of this header and library (major * 100 + minor). */
-#define DFS_ABI_VERSION 103
+#define DFS_ABI_VERSION 104
 int dfs_abi_version(void);
 
 #ifdef __cplusplus

@@ -11,30 +11,13 @@ Bars (scores are fp32 on the GPU from bf16/fp32 inputs, fp64 in the oracle):
 from __future__ import annotations
 
 import numpy as np
-import torch
 
 import oracle
+from workloads.device import to_dev, upload  # noqa: F401  (re-exported for the tests)
 
 TOL_ABS = 1e-3
 TOL_REL = 2e-3
 NEAR_TIE = 1e-4
-
-
-def to_dev(x: np.ndarray, device="cuda") -> torch.Tensor:
-    if x.dtype == np.uint16:  # bf16 bit patterns
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
-
-
-def upload(inp, device="cuda") -> dict:
-    return {
-        "logits": to_dev(inp.logits, device),
-        "hidden": to_dev(inp.hidden, device),
-        "prev_token": torch.from_numpy(inp.prev_token.astype(np.int32)).to(device),
-        "A": to_dev(inp.A, device),
-        "B": to_dev(inp.B, device),
-        "W_h": to_dev(inp.W_h, device),
-    }
 
 
 def scores_ok(gpu, ref) -> np.ndarray:

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.dfs_abi_version() == 103
+    assert L.dfs_abi_version() == 104
     for code in range(9):
         s = dfs.status_str(code)
         assert s.startswith("DFS_")
@@ -131,6 +131,39 @@ def test_select_validation(L):
     assert s(sh=ctypes.byref(sh)) == E_UNSUP
     sh = dfs._Shape(2, 4, 1000, 64, 1, 5, 1)
     assert s(sh=ctypes.byref(sh)) == E_UNSUP
+
+
+def test_packed_weight_validation(L):
+    # W_h packed once: bf16 [ceil(d/32)][256][32] (zero-padded), fp32 a plain copy
+    assert L.dfs_gate_pack_bytes(5120, 1) == 160 * 256 * 32 * 2
+    assert L.dfs_gate_pack_bytes(72, 1) == 3 * 256 * 32 * 2
+    assert L.dfs_gate_pack_bytes(1024, 0) == 1024 * 256 * 4
+    assert L.dfs_gate_pack_bytes(60, 1) == 0
+    assert L.dfs_gate_pack_bytes(0, 1) == 0
+    assert L.dfs_gate_pack_bytes(64, 9) == 0
+    nb = L.dfs_gate_pack_bytes(64, 1)
+
+    def pk(W=P, dt=1, d=64, out=P + 0x100000, ob=nb):
+        return L.dfs_gate_pack(W, dt, d, out, ob, None)
+
+    assert pk(W=None) == E_NULL
+    assert pk(out=None) == E_NULL
+    assert pk(dt=5) == E_UNSUP
+    assert pk(d=0) == E_SHAPE
+    assert pk(d=60) == E_UNSUP
+    assert pk(W=P + 8) == E_ALIGN
+    assert pk(ob=nb - 1) == E_WS
+    assert pk(out=P + 0x100) == E_ARG  # overlaps W_h
+    assert L.dfs_gate_packed(None, P, 1, 4, 64, 256, P, P, 1 << 24, None) == E_NULL
+    assert L.dfs_gate_packed(P, P, 1, 4, 60, 256, P, P, 1 << 24, None) == E_UNSUP
+    shape = dfs._Shape(2, 4, 1000, 64, 1, 1, 1)
+    assert L.dfs_select_packed(P, P, P, P, P, None, 16, ctypes.byref(shape), 0, 1.0, 0, P, 1 << 26, P, P,
+                               None) == E_NULL
+    assert L.dfs_select_packed(P, P, P, P, P, P, 16, ctypes.byref(shape), 0, 1.0, 0, P, 16, P, P, None) == E_WS
+    assert L.dfs_select_draft_packed(P, P, P, P, P, P, 16, ctypes.byref(shape), 0, 0.0, 0, P, 1 << 26, P, P,
+                                     P, P, None) == E_ARG
+    assert L.dfs_select_draft_packed(P, P, P, P, P, P, 16, ctypes.byref(shape), 0, 1.0, 0, P, 1 << 26, P, P,
+                                     None, P, None) == E_NULL
 
 
 def test_select_draft_and_verify_validation(L):
