@@ -26,7 +26,8 @@ HBM_PEAK_GBS = 8000.0
 # Sources of the top-16 kernel; HBM traffic figures taken with rocprofv3 counters
 # are reported only while these files hash to the value recorded with them.
 TOPK_SOURCES = ["draft_selection_position_amd/csrc/topk.hip", "draft_selection_position_amd/csrc/dfs_device.h",
-                "draft_selection_position_amd/csrc/gate_pack.h", "draft_selection_position_amd/csrc/topk_merge.h"]
+                "draft_selection_position_amd/csrc/gate_pack.h", "draft_selection_position_amd/csrc/topk_merge.h",
+                "draft_selection_position_amd/csrc/gate_tile.h", "draft_selection_position_amd/csrc/dfs_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_throughput_traffic.txt")
 
 

@@ -92,13 +92,15 @@ int check_walk_mode(int mode, double temperature) {
 struct SelectLayout {
   TopkPlan topk;
   GatePlan gate;
-  size_t cand_idx_off, cand_val_off, gate_off, topk_ws_off, gate_ws_off, total;
+  bool few;  // few rows: per-position pair workgroups (tiles, counters)
+  size_t cand_idx_off, cand_val_off, gate_off, topk_ws_off, gate_ws_off, tiles_off, counters_off, total;
 };
 
 SelectLayout select_layout(const dfs_shape_t& s) {
   SelectLayout l{};
   const int64_t rows = s.batch * s.L;
-  l.topk = plan_topk(rows, s.V, esize(s.logits_dtype));
+  l.few = rows <= kPosMaxRows;
+  l.topk = l.few ? plan_topk_small(rows, s.V, esize(s.logits_dtype)) : plan_topk(rows, s.V, esize(s.logits_dtype));
   l.gate = plan_gate(rows, s.d, s.act_dtype == DFS_BF16);
   size_t off = 0;
   l.cand_idx_off = off;
@@ -111,6 +113,13 @@ SelectLayout select_layout(const dfs_shape_t& s) {
   off += l.topk.ws_bytes;
   l.gate_ws_off = off;
   off += l.gate.ws_bytes;
+  l.tiles_off = off;
+  l.counters_off = off;
+  if (l.few) {
+    off += align_up((size_t)rows * sizeof(PosTile), 256);
+    l.counters_off = off;
+    off += align_up((size_t)s.batch * sizeof(uint32_t), 256);
+  }
   l.total = off;
   return l;
 }
@@ -163,16 +172,20 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   // leave their partial lists for the pair kernel to merge.  With few rows and a gate
   // that needs no repacking (fp32, or W_h packed by the caller) the gate's tiles ride
   // in the same launch; otherwise the W_h packing slabs (when needed) ride in its tail
-  // and (2) the gate GEMM follows.  (3) Pair scores and the walk in one kernel, which
-  // also merges the split rows' lists and adds up the gate's K-split partial sums.
+  // and (2) the gate GEMM follows.  (3) Pair scores and the walk, which also merges the
+  // split rows' lists and adds up the gate's K-split partial sums: one workgroup per
+  // sequence, or with few rows one per position (the last of a sequence walks it; its
+  // counters are zeroed by launch (1)).
+  uint32_t* counters = reinterpret_cast<uint32_t*>(w + l.counters_off);
+  const ZeroJob zj = l.few ? ZeroJob{counters, (int)s.batch} : ZeroJob{};
   hipError_t e;
   if (l.gate.kind == GatePlan::kJobs && (wh_packed || !bf16_act)) {
     const GateJobs gj = gate_jobs(l.gate, hidden, W_h, gate, gws);
-    e = launch_topk_gate(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, gj, bf16_act, stream);
+    e = launch_topk_gate(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, gj, bf16_act, zj, stream);
     if (e != hipSuccess) return DFS_E_HIP;
   } else {
     const PackJob job = bf16_act && !wh_packed ? gate_pack_job(l.gate, W_h, gws) : PackJob{nullptr, 0, nullptr, 0};
-    e = launch_topk(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, stream, &job, false);
+    e = launch_topk(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, stream, &job, false, zj);
     if (e != hipSuccess) return DFS_E_HIP;
     const void* Wg = bf16_act && !wh_packed ? gate_packed_in_ws(l.gate, gws) : W_h;
     if ((e = launch_gate_gemm(l.gate, hidden, Wg, gate, gws, stream)) != hipSuccess) return DFS_E_HIP;
@@ -182,8 +195,13 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   const GateSrc gs = l.gate.splits > 1 ? GateSrc{gate_partials(l.gate, gws), l.gate.splits, s.batch * s.L * DFS_E}
                                        : GateSrc{gate, 1, 0};
   const WalkArgs wa{(int)mode, temperature, seed, out_q, out_cand};
-  e = launch_pair_walk(cs, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V, nullptr, &wa,
-                       out_path, out_scores, stream);
+  if (l.few) {
+    e = launch_pair_pos(cs, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V, wa, out_path,
+                        out_scores, reinterpret_cast<PosTile*>(w + l.tiles_off), counters, stream);
+  } else {
+    e = launch_pair_walk(cs, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V, nullptr, &wa,
+                         out_path, out_scores, stream);
+  }
   return hip_status(e);
 }
 

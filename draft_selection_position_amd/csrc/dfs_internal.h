@@ -32,6 +32,12 @@ struct GateJobs {
   float* partial = nullptr;    // [splits, rows, 256] when splits > 1
   float* out = nullptr;        // [rows, 256] when splits == 1
 };
+// Counters a later launch of the same call needs at zero, cleared by the top-16 launch.
+struct ZeroJob {
+  uint32_t* p = nullptr;
+  int n = 0;
+};
+
 // ---------------------------------------------------------------- top-16
 struct TopkPlan {
   int64_t rows, V;
@@ -41,17 +47,20 @@ struct TopkPlan {
   size_t ws_bytes; // partial lists when parts > 1
 };
 TopkPlan plan_topk(int64_t rows, int64_t V, int esize);
+// Few rows (the fused selector's gate-carrying launch): chunks small enough to be held in
+// registers whole where the vocabulary allows it.
+TopkPlan plan_topk_small(int64_t rows, int64_t V, int esize);
 // `pack` (may be null): W_h packing slabs run as extra workgroups of the same launch.
 // merge false (rows split, parts > 1): the partial lists are left in ws for a merge job
 // placed elsewhere (topk_merge_job), and out_idx / out_val are not written.
 hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
                        float* out_val, void* ws, hipStream_t stream,
-                       const PackJob* pack = nullptr, bool merge = true);
+                       const PackJob* pack = nullptr, bool merge = true, ZeroJob zero = ZeroJob{});
 
 // The top-16 pass (merge false) with the gate's jobs as extra workgroups of the same
 // launch (ahead of the rows), for few rows; gate_bf16 selects the gate tile kind.
 hipError_t launch_topk_gate(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx, float* out_val,
-                            void* ws, const GateJobs& g, bool gate_bf16, hipStream_t stream);
+                            void* ws, const GateJobs& g, bool gate_bf16, ZeroJob zero, hipStream_t stream);
 
 // Merge of per-row partial top-16 lists [rows, parts, 16] (64-bit keys, 0 = empty).
 hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, int32_t* out_idx,
@@ -124,6 +133,20 @@ hipError_t launch_pair_walk(const CandSrc& cand, const int32_t* prev_token, cons
                             const void* A, const void* B, bool bf16_tables, int64_t batch, int64_t L,
                             int64_t V, float* out_pair, const WalkArgs* walk, int32_t* out_path,
                             float* out_scores, hipStream_t stream);
+// Few rows: one workgroup per (sequence, position), the walk by the last position of each
+// sequence to finish (see pair_pos_kernel).  tiles [batch * L]; counters [batch], zero
+// before the launch (the top-16 launch of the same call zeroes them) and zero after it.
+struct PosTile {
+  int32_t next[16];  // successor slot of each predecessor slot
+  float best[16];    // its score
+  int32_t cand[16];  // candidate ids
+  float tile[16][16];
+};
+constexpr int64_t kPosMaxRows = 64;  // dfs_select takes this path up to this many rows
+hipError_t launch_pair_pos(const CandSrc& cand, const int32_t* prev_token, const GateSrc& gate, const void* A,
+                           const void* B, bool bf16_tables, int64_t batch, int64_t L, int64_t V,
+                           const WalkArgs& walk, int32_t* out_path, float* out_scores, PosTile* tiles,
+                           uint32_t* counters, hipStream_t stream);
 hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L,
                        const WalkArgs& walk, int32_t* out_path, float* out_scores,
                        hipStream_t stream);

@@ -246,6 +246,75 @@ __device__ __forceinline__ float4 gate_finish(const float* __restrict__ gate, in
   return make_float4(sigmoidf(z.x), sigmoidf(z.y), sigmoidf(z.z), sigmoidf(z.w));
 }
 
+// The 16 x 16 score tile of one position on the matrix cores, K = 256: lane (q, r) =
+// (lane / 16, lane % 16) feeds predecessor row `pred` (A operand row r) and candidate row
+// `cand` (B operand column r), and gets S(4q + i, r) = u_r + <A(pred_{4q+i}) * g, B(cand_r)>
+// in sc[i], u = this lane's candidate logit (lanes r of every group hold the same u_r).
+// gp: this lane's 16-byte piece [4 lane, + 4) of the gate row; sGr: 256 floats of LDS for
+// that row, read back by other lanes of the wave only.  The gathers are all in flight
+// before the gate row is parked in LDS (scheduling barriers keep that order).  Every
+// kernel that scores pairs calls this, so their scores agree bit for bit.
+template <bool kBf16Tables>
+__device__ __forceinline__ void score_tile(const void* __restrict__ A_, const void* __restrict__ B_, int64_t pred,
+                                           int64_t cand, float u, float4 gp, float* sGr, int lane, float (&sc)[4]) {
+  const int q = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kBf16Tables) {
+    // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
+    const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) +
+                                                       pred * kE + 16 * q);
+    const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
+                                                       cand * kE + 16 * q);
+    bf16x8 av[8], bv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      av[c] = Ap[8 * (c >> 1) + (c & 1)];
+      bv[c] = Bp[8 * (c >> 1) + (c & 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float g[8];
+      const float4 g0 = *reinterpret_cast<const float4*>(&sGr[64 * (c >> 1) + 16 * q + 8 * (c & 1)]);
+      const float4 g1 = *reinterpret_cast<const float4*>(&sGr[64 * (c >> 1) + 16 * q + 8 * (c & 1) + 4]);
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ag = (float)av[c][e] * g[e];
+        hi[e] = (__bf16)ag;
+        lo[e] = (__bf16)(ag - (float)hi[e]);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv[c], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv[c], acc, 0, 0, 0);
+    }
+  } else {
+    // fp32 (one k slot per lane and step): step 4 c + s gives lane group q the value
+    // e = 16 c + 4 q + s, so a lane reads e = 16 c + 4 q + 0..3 as one float4 and
+    // feeds it to four consecutive steps (same mapping for A, gate and B).
+    const float4* Ap = reinterpret_cast<const float4*>(static_cast<const float*>(A_) + pred * kE +
+                                                       4 * q);
+    const float4* Bp = reinterpret_cast<const float4*>(static_cast<const float*>(B_) + cand * kE +
+                                                       4 * q);
+    *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 8
+    for (int c = 0; c < 16; ++c) {  // two rounds of 8 + 8 row loads in flight
+      const float4 a = Ap[4 * c], bb = Bp[4 * c];
+      const float4 g = *reinterpret_cast<const float4*>(&sGr[16 * c + 4 * q]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w * g.w, bb.w, acc, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = acc[i] + u;
+}
+
 // One workgroup of 16 waves per CU is all a launch of <= 256 sequences gives, so
 // registers are not rationed for a second one: every load of a wave can be in
 // flight at once.
@@ -263,7 +332,7 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   __shared__ float sS[kWalk ? kMaxL : 1][kK][kK];                // whole tiles (best-path walk)
   __shared__ int32_t sC[kMaxL][kK];                              // merged candidates: ids
   __shared__ float sU[kMaxL][kK];                                //   and their logits
-  __shared__ uint64_t sMerge[kMaxL][kMergeBatch];                // merge buffers, one per wave
+  __shared__ uint64_t sMerge[kMaxL][kMergeScratch];                // merge buffers, one per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;  // block position of this wave
   const int64_t b = blockIdx.x;
@@ -311,66 +380,13 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   // row is read back by other lanes of the same wave only.
   const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (kBf16Tables) {
-    // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
-    const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) +
-                                                       pred * kE + 16 * q);
-    const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
-                                                       cand * kE + 16 * q);
-    bf16x8 av[8], bv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      av[c] = Ap[8 * (c >> 1) + (c & 1)];
-      bv[c] = Bp[8 * (c >> 1) + (c & 1)];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    *reinterpret_cast<float4*>(&sG[t][4 * lane]) = gp;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float g[8];
-      const float4 g0 = *reinterpret_cast<const float4*>(&sG[t][64 * (c >> 1) + 16 * q + 8 * (c & 1)]);
-      const float4 g1 = *reinterpret_cast<const float4*>(&sG[t][64 * (c >> 1) + 16 * q + 8 * (c & 1) + 4]);
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ag = (float)av[c][e] * g[e];
-        hi[e] = (__bf16)ag;
-        lo[e] = (__bf16)(ag - (float)hi[e]);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv[c], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv[c], acc, 0, 0, 0);
-    }
-  } else {
-    // fp32 (one k slot per lane and step): step 4 c + s gives lane group q the value
-    // e = 16 c + 4 q + s, so a lane reads e = 16 c + 4 q + 0..3 as one float4 and
-    // feeds it to four consecutive steps (same mapping for A, gate and B).
-    const float4* Ap = reinterpret_cast<const float4*>(static_cast<const float*>(A_) + pred * kE +
-                                                       4 * q);
-    const float4* Bp = reinterpret_cast<const float4*>(static_cast<const float*>(B_) + cand * kE +
-                                                       4 * q);
-    *reinterpret_cast<float4*>(&sG[t][4 * lane]) = gp;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll 8
-    for (int c = 0; c < 16; ++c) {  // two rounds of 8 + 8 row loads in flight
-      const float4 a = Ap[4 * c], bb = Bp[4 * c];
-      const float4 g = *reinterpret_cast<const float4*>(&sG[t][16 * c + 4 * q]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w * g.w, bb.w, acc, 0, 0, 0);
-    }
-  }
-  if (kWalk && lane < kK) sW.cand[t][lane] = cand_id;
-  // lane holds D[4q + i][r]: predecessor slot 4q + i, candidate slot r
   float sc[4];
+  score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG[t], lane, sc);
+  if (kWalk && lane < kK) sW.cand[t][lane] = cand_id;
+  // lane holds S_t(predecessor slot 4q + i, candidate slot r) in sc[i]
+  if constexpr (kWritePair) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc[i] = acc[i] + u;
-    if constexpr (kWritePair) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
+    for (int i = 0; i < 4; ++i) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
   }
   if constexpr (kWalk) {
     if (mode == 2 || out_q != nullptr) {  // whole tiles kept for the best path or the draft rows
@@ -389,6 +405,131 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
       __syncthreads();
       draft_q(sS, sW, t, lane, temperature, row, out_q, out_cand);
     }
+  }
+}
+
+// ---------------------------------------------------------------- few rows
+// With few rows one workgroup per sequence would pull every position's gate partial sums
+// and table rows through a single CU; instead each (sequence, position) gets a workgroup
+// of two waves: wave 0 merges position t's split top-16 lists, wave 1 position t - 1's
+// (the predecessors), wave 0 then scores the tile and computes its successor table
+// exactly as pair_walk_kernel does, and leaves them in `tiles`.  The last workgroup of a
+// sequence to finish (an agent-scope release before an atomic count, acquire after it;
+// the count wraps back to zero, and the launch before this one zeroes it as well) reads
+// all L positions back and walks them with the same code.
+constexpr int kPosThreads = 2 * kWave;
+
+template <bool kBf16Tables>
+__global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
+    const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_val,
+    const uint64_t* __restrict__ partial, int parts, const int32_t* __restrict__ prev_token,
+    const float* __restrict__ gate, int gate_splits, int64_t gate_stride, const void* __restrict__ A_,
+    const void* __restrict__ B_, int L, int64_t V, int mode, double temperature, uint64_t seed,
+    int32_t* __restrict__ out_path, float* __restrict__ out_scores, float* __restrict__ out_q,
+    int32_t* __restrict__ out_cand, PosTile* __restrict__ tiles, uint32_t* __restrict__ counters) {
+  __shared__ int32_t sC[2][kK];  // [0]: position t - 1, [1]: position t
+  __shared__ float sU[2][kK];
+  __shared__ uint64_t sMerge[2][kMergeScratch];
+  __shared__ __attribute__((aligned(16))) float sG[kE];
+  __shared__ WalkTables sW;
+  __shared__ float sS[kMaxL][kK][kK];
+  __shared__ int s_last;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int64_t b = blockIdx.x / L;
+  const int t = (int)(blockIdx.x % L);
+  const int64_t row = b * L + t;
+
+  int32_t pred_id = 0, cand_id = 0;
+  float u = 0.0f;
+  GateRegs gr;
+  if (parts <= 1) {
+    if (wave == 0) {
+      const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
+      pred_id = *pred_p;
+      cand_id = cand_idx[row * kK + r];
+      u = cand_val[row * kK + r];
+      gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
+    }
+  } else {
+    const bool live = wave == 0 || t > 0;  // wave-uniform
+    MergeRegs mr;
+    if (live) merge_load(partial + (row - wave) * parts * kK, parts, lane, mr);
+    int32_t prev = 0;
+    if (wave == 0) {
+      prev = prev_token[b];
+      gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
+    }
+    if (live) {
+      const uint64_t key = merge_keys(mr, parts, lane, sMerge[wave]);
+      if (lane < kK) {
+        sC[1 - wave][lane] = (int32_t)key_index(key);
+        sU[1 - wave][lane] = key_value(key);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      pred_id = t == 0 ? prev : sC[0][r];
+      cand_id = sC[1][r];
+      u = sU[1][r];
+    }
+  }
+  PosTile* pt = tiles + row;
+  if (wave == 0) {
+    const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
+    const int64_t cand = cand_id < 0 ? 0 : (cand_id >= V ? V - 1 : cand_id);
+    const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
+    __builtin_amdgcn_sched_barrier(0);
+    float sc[4];
+    score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG, lane, sc);
+    if (mode == 2 || out_q != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pt->tile[4 * q + i][r] = sc[i];
+    }
+    if (mode != 2) {
+      successors(sc, t, lane, mode, temperature, seed, b, sW);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < kK) {
+        pt->next[lane] = sW.next[t][lane];
+        pt->best[lane] = sW.best[t][lane];
+      }
+    }
+    if (lane < kK) pt->cand[lane] = cand_id;
+    // publish this position, then count it; the last of the sequence walks
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) s_last = atomicInc(counters + b, (unsigned)(L - 1)) == (unsigned)(L - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const PosTile* seq = tiles + b * L;
+  const bool need_tiles = mode == 2 || out_q != nullptr;
+  for (int i = threadIdx.x; i < L * kK; i += kPosThreads) {
+    const int tt = i / kK, j = i % kK;
+    sW.cand[tt][j] = seq[tt].cand[j];
+    if (mode != 2) {
+      sW.next[tt][j] = seq[tt].next[j];
+      sW.best[tt][j] = seq[tt].best[j];
+    }
+  }
+  if (need_tiles) {
+    for (int i = threadIdx.x; i < L * kK * kK; i += kPosThreads) {
+      const int tt = i / (kK * kK), e = i % (kK * kK);
+      sS[tt][e / kK][e % kK] = seq[tt].tile[e / kK][e % kK];
+    }
+  }
+  __syncthreads();
+  if (mode == 2) {
+    if (wave == 0) viterbi_walk(sS, sW.next, sW.cand, sW.slot, b, L, lane, out_path, out_scores);
+  } else if (threadIdx.x == 0) {
+    chase(sW, b, L, out_path, out_scores);
+  }
+  if (out_q != nullptr) {
+    __syncthreads();
+    for (int tt = wave; tt < L; tt += kPosThreads / kWave) draft_q(sS, sW, tt, lane, temperature, b * L + tt, out_q, out_cand);
   }
 }
 
@@ -458,6 +599,26 @@ hipError_t launch_pair_walk(const CandSrc& cand, const int32_t* prev_token, cons
     else DFS_PW(false, false, true);
   }
 #undef DFS_PW
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_pos(const CandSrc& c, const int32_t* prev_token, const GateSrc& g, const void* A,
+                           const void* B, bool bf16_tables, int64_t batch, int64_t L, int64_t V, const WalkArgs& w,
+                           int32_t* out_path, float* out_scores, PosTile* tiles, uint32_t* counters,
+                           hipStream_t stream) {
+  if (g.splits < 1) return hipErrorInvalidValue;
+  if (c.parts > kMaxMergeParts || (c.parts > 1 && c.partial == nullptr)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(batch * L));
+#define DFS_PP(BF)                                                                                                  \
+  pair_pos_kernel<BF><<<grid, kPosThreads, 0, stream>>>(c.idx, c.val, c.partial, c.parts, prev_token, g.gate, g.splits, \
+                                                        g.stride, A, B, (int)L, V, w.mode, w.temperature, w.seed,     \
+                                                        out_path, out_scores, w.out_q, w.out_cand, tiles, counters)
+  if (bf16_tables) {
+    DFS_PP(true);
+  } else {
+    DFS_PP(false);
+  }
+#undef DFS_PP
   return hipGetLastError();
 }
 

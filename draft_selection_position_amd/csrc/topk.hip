@@ -58,6 +58,11 @@ constexpr int kUnroll = DFS_TOPK_UNROLL;  // 16-byte vectors per thread per iter
 constexpr int kMergeAt = 64;      // merge once more keys than this are buffered
 constexpr int kCap = kMergeAt + 8 * kWave;  // room for one whole vector per lane on top
 constexpr int kMinChunk = 4096;   // elements; below this a split does not pay
+constexpr int kMinSmallChunk = 1024;  // the same for the few-row plan
+// Few rows: workgroups the split aims for.
+#ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
+#define DFS_TOPK_SMALL_TARGET_BLOCKS 256
+#endif
 
 template <bool kBf16>
 struct Elems;
@@ -70,6 +75,12 @@ template <>
 struct Elems<false> {
   static constexpr int per_vec = 4;
   using T = float;
+};
+
+struct WaveTop {
+  uint64_t list;  // lanes 0..15: best keys so far, descending (0 = empty slot)
+  float thr;      // admission threshold, identical in every lane
+  int cnt;        // keys waiting in the buffer, identical in every lane
 };
 
 // Out-of-line copy of the 64-lane sort for the compact build of the pass (few rows),
@@ -87,13 +98,8 @@ __device__ __forceinline__ uint64_t sort_desc(uint64_t x, int lane) {
   }
 }
 
-struct WaveTop {
-  uint64_t list;  // lanes 0..15: best keys so far, descending (0 = empty slot)
-  float thr;      // admission threshold, identical in every lane
-  int cnt;        // keys waiting in the buffer, identical in every lane
-};
-
-// Merge the buffered keys into the wave's list and raise the threshold.
+// Merge the buffered keys into the wave's list and raise the threshold (kCompact: the
+// out-of-line sort).
 template <bool kCompact>
 __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint32_t* s_thr,
                                            int lane) {
@@ -123,6 +129,7 @@ __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint
     w.thr = uniformf(unmono32(m));
   }
 }
+
 
 // Append this lane's element to the wave buffer when `adm`.
 __device__ __forceinline__ void append(WaveTop& w, bool adm, float v, uint32_t idx,
@@ -204,8 +211,9 @@ static_assert(sizeof(TopkLds::buf) >= kPackLdsBytes, "a packing job reuses the k
 static_assert(sizeof(TopkLds::buf) >= gtile::kF32LdsBytes, "a gate job reuses the key buffers");
 
 // One (row, part) of the pass: workgroup `bid` of the rows.  kCompact: the sorts are
-// out-of-line calls (few rows: each wave runs the code about once).
-template <bool kBf16, bool kCompact>
+// out-of-line calls (few rows: each wave runs the code about once).  kU: 16-byte vectors
+// per thread per iteration (two iterations in flight).
+template <bool kBf16, bool kCompact, int kU = kUnroll>
 __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64_t V, int parts, int64_t chunk,
                                           uint64_t* __restrict__ partial, int32_t* __restrict__ out_idx,
                                           float* __restrict__ out_val, int64_t bid, TopkLds& lds) {
@@ -258,15 +266,15 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
   // back as zeros and are flagged invalid) and the two register buffers alternate
   // (no copies), so the compiler waits for exactly the vectors it is about to scan
   // and leaves the next ones in flight.
-  const int64_t step = (int64_t)kThreads * kUnroll;
+  const int64_t step = (int64_t)kThreads * kU;
   const int64_t niter = (nvec + step - 1) / step;
   if (niter > 0) {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T*>(rowp + vb), (short)0, (int)(nvec * 16), kRawBufferWord3);
-    uint4 bufA[kUnroll], bufB[kUnroll];
+    uint4 bufA[kU], bufB[kU];
     auto load_iter = [&](uint4* dst, int64_t it) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const uint32_t vid = (uint32_t)(it * step) + (uint32_t)(u * kThreads + tid);
         dst[u] = load_vec(rsrc, vid * 16u);  // past the end: zeros, flagged invalid below
       }
@@ -282,7 +290,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int64_t vid = it * step + (int64_t)u * kThreads + tid;
         scan_vec<kBf16, kCompact>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
                         &s_thr, lane, it == 0 && u == 0);
@@ -314,8 +322,104 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
   if (lane < kK) s_list[wave * kK + lane] = w.list;
   __syncthreads();
   if (wave == 0) {
-    uint64_t x = s_list[lane];  // kWaves * kK == 64 keys
-    x = sort_desc<kCompact>(x, lane);
+    const uint64_t x = sort_desc<kCompact>(s_list[lane], lane);  // kWaves * kK == 64 keys
+    if (lane < kK) {
+      if (parts == 1) {
+        out_idx[row * kK + lane] = (int32_t)key_index(x);
+        out_val[row * kK + lane] = key_value(x);
+      } else {
+        partial[(row * parts + part) * kK + lane] = x;
+      }
+    }
+  }
+}
+
+// Few rows: a chunk of at most kSmallVecs vectors per thread is loaded whole before any
+// compare.  Every lane's maximum over its vectors is a distinct element, so the 16th
+// largest lane maximum of any wave bounds the chunk's top 16; the largest such bound over
+// the four waves (shared through LDS) is the admission threshold from the start.  One
+// sort per wave finds it, typically one more merges the admitted keys, and one more
+// merges the four wave lists: the critical path of a workgroup that runs this code once.
+constexpr int kSmallVecs = 6;
+
+template <bool kBf16>
+__device__ __forceinline__ void topk_small_body(const void* __restrict__ logits, int64_t V, int parts, int64_t chunk,
+                                                uint64_t* __restrict__ partial, int32_t* __restrict__ out_idx,
+                                                float* __restrict__ out_val, int64_t bid, TopkLds& lds) {
+  using T = typename Elems<kBf16>::T;
+  constexpr int PV = Elems<kBf16>::per_vec;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t row = bid / parts;
+  const int part = (int)(bid % parts);
+  const T* rowp = static_cast<const T*>(logits) + row * V;
+  const int64_t beg = (int64_t)part * chunk;
+  const int64_t end = beg + chunk < V ? beg + chunk : V;
+  const uintptr_t a_beg = (uintptr_t)(rowp + beg);
+  int64_t vb = beg + (int64_t)(((16u - (a_beg & 15u)) & 15u) / sizeof(T));
+  if (vb > end) vb = end;
+  const int64_t nvec = (end - vb) / PV;
+  const int64_t ve = vb + nvec * PV;
+  if (tid == 0) lds.thr = 0u;
+
+  uint4 d[kSmallVecs];
+  if (nvec > 0) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(rowp + vb), (short)0, (int)(nvec * 16), kRawBufferWord3);
+#pragma unroll
+    for (int u = 0; u < kSmallVecs; ++u) d[u] = load_vec(rsrc, (uint32_t)(u * kThreads + tid) * 16u);
+  }
+  // the head and tail elements outside the aligned middle (at most 14), one per lane of wave 0
+  const int nhead = (int)(vb - beg);
+  const int ntail = (int)(end - ve);
+  int64_t hi = -1;
+  if (wave == 0) {
+    if (lane < nhead) {
+      hi = beg + lane;
+    } else if (lane < nhead + ntail) {
+      hi = ve + (lane - nhead);
+    }
+  }
+  const float hv = hi >= 0 ? load_scalar<kBf16>(rowp, hi) : 0.0f;
+
+  // lane maxima (vectors past the chunk read as NaN, which fmaxf ignores)
+  float m = hi >= 0 ? hv : __int_as_float(0x7fffffff);
+#pragma unroll
+  for (int u = 0; u < kSmallVecs; ++u) {
+    if ((int64_t)(u * kThreads + tid) >= nvec) d[u] = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
+    if constexpr (kBf16) {
+      m = fmaxf(m, fmaxf(fmaxf(fmaxf(bf16_lo(d[u].x), bf16_hi(d[u].x)), fmaxf(bf16_lo(d[u].y), bf16_hi(d[u].y))),
+                         fmaxf(fmaxf(bf16_lo(d[u].z), bf16_hi(d[u].z)), fmaxf(bf16_lo(d[u].w), bf16_hi(d[u].w)))));
+    } else {
+      m = fmaxf(m, fmaxf(fmaxf(__uint_as_float(d[u].x), __uint_as_float(d[u].y)),
+                         fmaxf(__uint_as_float(d[u].z), __uint_as_float(d[u].w))));
+    }
+  }
+  __syncthreads();  // lds.thr cleared
+  {
+    const uint64_t lk = (m == m) ? make_key(m, (uint32_t)lane) : 0ull;
+    const uint64_t k16 = lane_u64(sort_desc<true>(lk, lane), 15);
+    if (k16 != 0 && lane == 0) atomicMax(&lds.thr, (uint32_t)(k16 >> 32));
+  }
+  __syncthreads();
+  uint64_t* buf = lds.buf[wave];
+  WaveTop w;
+  w.list = 0;
+  w.cnt = 0;
+  const uint32_t t0 = lds.thr;
+  w.thr = t0 != 0u ? unmono32(t0) : -INFINITY;
+  append(w, hi >= 0 && hv >= w.thr, hv, (uint32_t)hi, buf);  // at most 14 keys
+#pragma unroll
+  for (int u = 0; u < kSmallVecs; ++u) {
+    const int64_t vid = (int64_t)u * kThreads + tid;
+    scan_vec<kBf16, true>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, &lds.thr, lane, false);
+  }
+  if (w.cnt > 0) wave_merge<true>(w, buf, &lds.thr, lane);
+  if (lane < kK) lds.list[wave * kK + lane] = w.list;
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t x = sort_desc<true>(lds.list[lane], lane);
     if (lane < kK) {
       if (parts == 1) {
         out_idx[row * kK + lane] = (int32_t)key_index(x);
@@ -332,8 +436,10 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TOPK_WAVES_PER_EU))) void topk_chunk_kernel(
     const void* __restrict__ logits, int64_t V, int parts, int64_t chunk, uint64_t* __restrict__ partial,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_val, int64_t ntopk, PackJob pack) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_val, int64_t ntopk, PackJob pack, ZeroJob zero) {
   __shared__ TopkLds lds;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero.n; i += kThreads) zero.p[i] = 0u;
   const int64_t job = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ntopk;
   const int64_t bid = DFS_TOPK_PACK_FIRST ? (int64_t)blockIdx.x - pack.nslabs : (int64_t)blockIdx.x;
   if (DFS_TOPK_PACK_FIRST ? job < pack.nslabs : job >= 0) {
@@ -350,14 +456,22 @@ template <bool kBf16, bool kGateBf16>
 __global__ __launch_bounds__(kThreads) void topk_gate_kernel(const void* __restrict__ logits, int64_t V, int parts,
                                                              int64_t chunk, uint64_t* __restrict__ partial,
                                                              int32_t* __restrict__ out_idx,
-                                                             float* __restrict__ out_val, GateJobs g) {
+                                                             float* __restrict__ out_val, GateJobs g,
+                                                             ZeroJob zero) {
   __shared__ TopkLds lds;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero.n; i += kThreads) zero.p[i] = 0u;
   const int64_t njobs = (int64_t)g.mtiles * g.splits;
   if ((int64_t)blockIdx.x < njobs) {
     run_gate_job(g, kGateBf16, blockIdx.x, threadIdx.x, &lds.buf[0][0]);
     return;
   }
-  topk_body<kBf16, true>(logits, V, parts, chunk, partial, out_idx, out_val, (int64_t)blockIdx.x - njobs, lds);
+  const int64_t bid = (int64_t)blockIdx.x - njobs;
+  if (chunk <= (int64_t)kSmallVecs * kThreads * Elems<kBf16>::per_vec) {
+    topk_small_body<kBf16>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+  } else {
+    topk_body<kBf16, true>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+  }
 }
 
 // Merge `parts` partial top-16 lists per row (one workgroup per row).
@@ -398,8 +512,29 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int esize) {
   return p;
 }
 
+TopkPlan plan_topk_small(int64_t rows, int64_t V, int esize) {
+  TopkPlan p{};
+  p.rows = rows;
+  p.V = V;
+  p.esize = esize;
+  const int64_t pv = 16 / esize;
+  const int64_t cap = (int64_t)kSmallVecs * kThreads * pv;  // elements a chunk may hold in registers
+  int64_t parts = cdiv(DFS_TOPK_SMALL_TARGET_BLOCKS, rows);
+  const int64_t fit = cdiv(V, cap);
+  if (parts < fit) parts = fit;
+  int64_t maxp = V / kMinSmallChunk;
+  if (maxp < 1) maxp = 1;
+  if (parts > maxp) parts = maxp;
+  if (parts > kMaxMergeParts) parts = kMaxMergeParts;
+  const int64_t chunk = (int64_t)align_up((size_t)cdiv(V, parts), (size_t)pv);
+  p.parts = (int)cdiv(V, chunk);
+  p.chunk = chunk;
+  p.ws_bytes = p.parts > 1 ? align_up((size_t)rows * p.parts * kK * sizeof(uint64_t), 256) : 0;
+  return p;
+}
+
 hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx,
-                       float* out_val, void* ws, hipStream_t stream, const PackJob* pack, bool merge) {
+                       float* out_val, void* ws, hipStream_t stream, const PackJob* pack, bool merge, ZeroJob zero) {
   static_assert(kThreads == kPackThreads, "packing jobs run on top-16 workgroups");
   uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
   const int64_t ntopk = p.rows * p.parts;
@@ -407,10 +542,10 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
   const dim3 grid((unsigned)(ntopk + job.nslabs));
   if (bf16) {
     topk_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial,
-                                                           out_idx, out_val, ntopk, job);
+                                                           out_idx, out_val, ntopk, job, zero);
   } else {
     topk_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk,
-                                                            partial, out_idx, out_val, ntopk, job);
+                                                            partial, out_idx, out_val, ntopk, job, zero);
   }
   if (p.parts > 1 && merge) {
     topk_merge_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.parts, out_idx,
@@ -420,11 +555,11 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
 }
 
 hipError_t launch_topk_gate(const TopkPlan& p, const void* logits, bool bf16, int32_t* out_idx, float* out_val,
-                            void* ws, const GateJobs& g, bool gate_bf16, hipStream_t stream) {
+                            void* ws, const GateJobs& g, bool gate_bf16, ZeroJob zero, hipStream_t stream) {
   uint64_t* partial = p.parts > 1 ? static_cast<uint64_t*>(ws) : nullptr;
   const dim3 grid((unsigned)(p.rows * p.parts + (int64_t)g.mtiles * g.splits));
 #define DFS_TG(LB, GB) \
-  topk_gate_kernel<LB, GB><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial, out_idx, out_val, g)
+  topk_gate_kernel<LB, GB><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial, out_idx, out_val, g, zero)
   if (bf16) {
     if (gate_bf16) DFS_TG(true, true); else DFS_TG(true, false);
   } else {

@@ -46,8 +46,10 @@ __device__ __forceinline__ void merge_row_lists(const uint64_t* __restrict__ src
 // ---------------------------------------------------------------- one wave, one row
 // Most lists one wave merges (the top-16 pass splits a row into at most this many).
 constexpr int kMaxMergeParts = 64;
-// Keys buffered per sort: with the running list (16 lanes) they fill the wave.
+// Keys buffered per selection: with the running list they make 64.
 constexpr int kMergeBatch = kWave - kK;
+// LDS keys a merging wave needs: the buffer, the running list, the 16 output slots.
+constexpr int kMergeScratch = kWave + kK;
 
 // One wave merges one row's `parts` (1..64) sorted lists of 16 keys (src [parts, 16])
 // into their top 16: lanes 0..15 of the result hold it, descending; the other lanes 0.
@@ -55,7 +57,7 @@ constexpr int kMergeBatch = kWave - kK;
 // p / 4); merge_keys then needs only the registers, so a caller can put other loads in
 // flight in between.  Pruning: if some list's 16th key is T, that list alone holds 16
 // keys >= T, so no key below T can be in the result; T only rises as the running list
-// fills.  The survivors are appended to `scratch` (kMergeBatch keys of LDS for this
+// fills.  The survivors are appended to `scratch` (kMergeScratch keys of LDS for this
 // wave) and sorted with the running list whenever the buffer would overflow, and once
 // at the end.  Every lane of the wave must call both.
 constexpr int kMergeGroups = kMaxMergeParts / 4;  // 4 lists per 64 lanes
@@ -101,6 +103,7 @@ __device__ __forceinline__ uint64_t merge_keys(MergeRegs& m, int parts, int lane
       const bool keep = v != 0 && v >= t;
       const uint64_t mask = __ballot(keep);
       if ((n == kMergeBatch && mask != 0) || (last && n > 0)) {
+        // the running list (lanes 0..15) and the buffered keys (lanes 16..): one sort
         __builtin_amdgcn_wave_barrier();
         uint64_t y = 0;
         if (lane < kK) {
