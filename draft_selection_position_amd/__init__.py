@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.dfs_select.restype = c_int
         L.dfs_select_packed.argtypes = L.dfs_select.argtypes
         L.dfs_select_packed.restype = c_int
+        L.dfs_select_packed_static.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int,
+                                               c_double, u64, i32p, f32p, vp]
+        L.dfs_select_packed_static.restype = c_int
         L.dfs_select_draft.argtypes = [vp, vp, i32p, vp, vp, vp, c_int, ctypes.POINTER(_Shape), c_int,
                                        c_double, u64, vp, sz, i32p, f32p, f32p, i32p, vp]
         L.dfs_select_draft.restype = c_int

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdfs.so")
-SOURCES = ["topk.hip", "gate.hip", "select.hip", "verify.hip", "conv.hip", "lmhead.hip", "dfs_api.cpp"]
+SOURCES = ["topk.hip", "gate.hip", "select.hip", "verify.hip", "conv.hip", "lmhead.hip", "static_scratch.hip",
+           "dfs_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

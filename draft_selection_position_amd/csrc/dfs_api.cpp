@@ -138,11 +138,10 @@ int check_shape(const dfs_shape_t* s) {
 
 }  // namespace
 
-static int select_impl(const void* logits, const void* hidden, const int32_t* prev_token,
-                       const void* A, const void* B, const void* W_h, bool wh_packed, int k,
-                       const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
-                       uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
-                       float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream) {
+// The host-side checks of a dfs_select call, in order, before any device call.
+static int select_host_checks(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                              const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,
+                              double temperature, int32_t* out_path, float* out_scores) {
   if (!logits || !hidden || !prev_token || !A || !B || !W_h || !out_path || !out_scores)
     return DFS_E_NULL;
   int st = check_shape(shape);
@@ -154,6 +153,18 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
       !aligned(A, 16) || !aligned(B, 16) || !aligned(prev_token, 4) || !aligned(out_path, 4) ||
       !aligned(out_scores, 4))
     return DFS_E_ALIGN;
+  return DFS_OK;
+}
+
+static int select_impl(const void* logits, const void* hidden, const int32_t* prev_token,
+                       const void* A, const void* B, const void* W_h, bool wh_packed, int k,
+                       const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
+                       uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
+                       float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream) {
+  int st = select_host_checks(logits, hidden, prev_token, A, B, W_h, k, shape, mode, temperature, out_path,
+                              out_scores);
+  if (st != DFS_OK) return st;
+  const dfs_shape_t s = *shape;
   const SelectLayout l = select_layout(s);
   if (!ws || ws_bytes < l.total) return DFS_E_WORKSPACE;
   if (!aligned(ws, 256)) return DFS_E_ALIGN;
@@ -205,6 +216,19 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   return hip_status(e);
 }
 
+namespace dfs {
+// dfs_select / dfs_select_packed with a given workspace, and the bytes it needs (0 if the
+// shape is rejected), for the entry points that bring their own scratch.
+int select_with_workspace(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                          const void* B, const void* W_h, bool wh_packed, int k, const dfs_shape_t* shape,
+                          int mode, double temperature, uint64_t seed, void* ws, size_t ws_bytes,
+                          int32_t* out_path, float* out_scores, hipStream_t stream);
+size_t select_workspace_need(const dfs_shape_t* shape);
+int select_static_checks(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                         const void* B, const void* W_h, int k, const dfs_shape_t* shape, int mode,
+                         double temperature, int32_t* out_path, float* out_scores);
+}  // namespace dfs
+
 static int select_entry(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
                         const void* B, const void* W_h, bool wh_packed, int k, const dfs_shape_t* shape,
                         dfs_walk_t mode, double temperature, uint64_t seed, void* ws, size_t ws_bytes,
@@ -235,6 +259,9 @@ const char* dfs_status_str(int status) {
     case DFS_E_ARCH: return "DFS_E_ARCH: the current device is not gfx950";
     case DFS_E_ARG:
       return "DFS_E_ARG: invalid argument (temperature must be finite and > 0; outputs must not overlap inputs)";
+    case DFS_E_TOO_LARGE:
+      return "DFS_E_TOO_LARGE: the call needs more scratch than the library's static buffer holds "
+             "(dfs_select_packed_static; use dfs_select_packed with a workspace)";
     default: return "unknown dfs status";
   }
 }
@@ -346,6 +373,30 @@ size_t dfs_select_workspace_bytes(const dfs_shape_t* shape) {
   if (check_shape(shape) != DFS_OK) return 0;
   return select_layout(*shape).total;
 }
+
+}  // extern "C"
+
+int dfs::select_with_workspace(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                               const void* B, const void* W_h, bool wh_packed, int k, const dfs_shape_t* shape,
+                               int mode, double temperature, uint64_t seed, void* ws, size_t ws_bytes,
+                               int32_t* out_path, float* out_scores, hipStream_t stream) {
+  return select_entry(logits, hidden, prev_token, A, B, W_h, wh_packed, k, shape, (dfs_walk_t)mode, temperature,
+                      seed, ws, ws_bytes, out_path, out_scores, nullptr, nullptr, stream);
+}
+
+int dfs::select_static_checks(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
+                              const void* B, const void* W_h, int k, const dfs_shape_t* shape, int mode,
+                              double temperature, int32_t* out_path, float* out_scores) {
+  return select_host_checks(logits, hidden, prev_token, A, B, W_h, k, shape, (dfs_walk_t)mode, temperature, out_path,
+                            out_scores);
+}
+
+size_t dfs::select_workspace_need(const dfs_shape_t* shape) {
+  if (check_shape(shape) != DFS_OK) return 0;
+  return select_layout(*shape).total;
+}
+
+extern "C" {
 
 int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
                const void* B, const void* W_h, int k, const dfs_shape_t* shape, dfs_walk_t mode,

@@ -67,8 +67,10 @@ typedef enum {
   DFS_E_ALIGN = 5,       /* a pointer is not aligned as documented */
   DFS_E_HIP = 6,         /* no usable HIP device, or a HIP launch error */
   DFS_E_ARCH = 7,        /* the current device is not gfx950 */
-  DFS_E_ARG = 8          /* an argument is invalid (temperature <= 0 for sampling; an output
+  DFS_E_ARG = 8,         /* an argument is invalid (temperature <= 0 for sampling; an output
                             that overlaps an input) */
+  DFS_E_TOO_LARGE = 9    /* dfs_select_packed_static: the call needs more scratch than
+                            DFS_STATIC_SCRATCH_BYTES */
 } dfs_status_t;
 
 typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype_t;
@@ -216,6 +218,22 @@ int dfs_select_draft(const void* logits, const void* hidden, const int32_t* prev
                      const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
                      uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                      float* out_scores, float* out_q, int32_t* out_cand, hipStream_t stream);
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): dfs_select_packed without a workspace.
+ * Its scratch is a device array of DFS_STATIC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends (its device address is looked up on the first call on
+ * each device, which must therefore happen outside graph capture).  It allocates nothing
+ * and gives the same bits as dfs_select_packed.  Calls needing more scratch than the array
+ * holds (dfs_select_workspace_bytes(shape) > DFS_STATIC_SCRATCH_BYTES) return
+ * DFS_E_TOO_LARGE before anything is launched.  Every call on one GPU uses that GPU's one
+ * array: calls that overlap on one GPU (two streams, two host threads) race and must be
+ * ordered by the caller.  The array keeps nothing that a later call relies on. */
+#define DFS_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int dfs_select_packed_static(const void* logits, const void* hidden, const int32_t* prev_token,
+                             const void* A, const void* B, const void* W_packed, int k,
+                             const dfs_shape_t* shape, dfs_walk_t mode, double temperature,
+                             uint64_t seed, int32_t* out_path, float* out_scores, hipStream_t stream);
+
 /* dfs_select_draft with W_h packed by dfs_gate_pack. */
 int dfs_select_draft_packed(const void* logits, const void* hidden, const int32_t* prev_token,
                             const void* A, const void* B, const void* W_packed, int k,
@@ -301,7 +319,7 @@ int dfs_lmhead_logits(const void* hidden, const void* W_lm, dfs_dtype_t dt, int6
 const char* dfs_status_str(int status);
 
 /* ABI version of this header and library (major * 100 + minor). */
-#define DFS_ABI_VERSION 104
+#define DFS_ABI_VERSION 105
 int dfs_abi_version(void);
 
 #ifdef __cplusplus

@@ -10,7 +10,7 @@ import draft_selection_position_amd as dfs
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dfs.h")
 P = 0x10000  # a fake, 256-byte-aligned device address; never dereferenced by these calls
-OK, E_NULL, E_SHAPE, E_UNSUP, E_WS, E_ALIGN, E_HIP, E_ARCH, E_ARG = range(9)
+OK, E_NULL, E_SHAPE, E_UNSUP, E_WS, E_ALIGN, E_HIP, E_ARCH, E_ARG, E_TOO_LARGE = range(10)
 
 
 def _declared():
@@ -34,8 +34,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.dfs_abi_version() == 104
-    for code in range(9):
+    assert L.dfs_abi_version() == 105
+    for code in range(10):
         s = dfs.status_str(code)
         assert s.startswith("DFS_")
     assert dfs.status_str(12345) == "unknown dfs status"
@@ -164,6 +164,28 @@ def test_packed_weight_validation(L):
                                      P, P, None) == E_ARG
     assert L.dfs_select_draft_packed(P, P, P, P, P, P, 16, ctypes.byref(shape), 0, 1.0, 0, P, 1 << 26, P, P,
                                      None, P, None) == E_NULL
+
+
+def test_static_scratch_validation(L):
+    # dfs_select_packed_static: the same checks as dfs_select_packed, plus the size of its
+    # static scratch (32 MiB), all on the host before anything is launched
+    def st(sh, lg=P, W=P, T=1.0, mode=0):
+        return L.dfs_select_packed_static(lg, P, P, P, P, W, 16, ctypes.byref(sh) if sh is not None else None, mode,
+                                          T, 0, P, P, None)
+
+    assert st(None) == E_NULL
+    assert st(dfs._Shape(2, 4, 1000, 64, 1, 1, 1), lg=None) == E_NULL
+    assert st(dfs._Shape(2, 4, 1000, 64, 1, 1, 1), mode=1, T=0.0) == E_ARG
+    assert st(dfs._Shape(0, 4, 1000, 64, 1, 1, 1)) == E_SHAPE
+    big = dfs._Shape(4096, 16, 151936, 5120, 1, 1, 1)  # 65536 rows: 64 MB of gate rows alone
+    assert L.dfs_select_workspace_bytes(ctypes.byref(big)) > 32 << 20
+    assert st(big) == E_TOO_LARGE
+    for name in ("throughput", "sampled", "small_batch", "single_stream", "tiny"):
+        from workloads import config_by_name
+        c = config_by_name(name)
+        dt = 1 if c.dtype == "bf16" else 0
+        sh = dfs._Shape(c.batch, c.L, c.V, c.d, dt, dt, dt)
+        assert L.dfs_select_workspace_bytes(ctypes.byref(sh)) <= 32 << 20, name
 
 
 def test_select_draft_and_verify_validation(L):
