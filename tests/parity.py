@@ -19,6 +19,13 @@ TOL_ABS = 1e-3
 TOL_REL = 2e-3
 NEAR_TIE = 1e-4
 
+# (what, workload) -> (units checked, unit name, note); printed at the end of the run
+FULL_SIZE: dict = {}
+
+
+def record(what: str, workload: str, checked: int, unit: str, note: str = "all exact") -> None:
+    FULL_SIZE[(what, workload)] = (int(checked), unit, note)
+
 
 def scores_ok(gpu, ref) -> np.ndarray:
     gpu = np.asarray(gpu, np.float64)

@@ -6,7 +6,8 @@ import torch
 import oracle
 from workloads import CONFIGS, make, variant
 
-from .parity import assert_scores, check_path, to_dev
+from .oracle_pool import stack
+from .parity import assert_scores, check_path, record, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -32,17 +33,18 @@ GATE_ATOL = 2e-5  # fp32 sums of d bf16 products; sigmoid slope <= 1/4
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
-def test_gate_full_size_configs(cfg, full_workload):
+def test_gate_full_size_configs(cfg, full_workload, full_oracle):
+    # every row of the full-size gate against the oracle's fp64 gate
     inp, dev = full_workload(cfg.name)
-    print(f"gate {cfg.name}: rows {cfg.batch * cfg.L} d {cfg.d}", flush=True)
+    rows = cfg.batch * cfg.L
+    print(f"gate {cfg.name}: rows {rows} d {cfg.d}", flush=True)
     g = dfs_mod().gate(dev["hidden"].view(-1, cfg.d), dev["W_h"])
     torch.cuda.synchronize()
     g = g.cpu().numpy().astype(np.float64)
-    h = oracle.widen(inp.hidden.reshape(-1, cfg.d), cfg.dtype)
-    W = oracle.widen(inp.W_h, cfg.dtype)
-    rows = np.arange(h.shape[0]) if h.shape[0] <= 64 else np.random.default_rng(1).choice(h.shape[0], 64, False)
-    want = oracle.gate(h[rows], W)
-    np.testing.assert_allclose(g[rows], want, rtol=0, atol=GATE_ATOL)
+    want = stack(full_oracle(cfg.name), "gate").reshape(rows, -1)
+    np.testing.assert_allclose(g, want, rtol=0, atol=GATE_ATOL)
+    record("gate", cfg.name, rows, "rows", f"max abs error {np.abs(g - want).max():.2g}")
+    print(f"gate {cfg.name}: max abs error {np.abs(g - want).max():.3g}", flush=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -105,6 +107,30 @@ def test_pair_scores_match_oracle(cfg):
     err = np.abs(got - want).max()
     print(f"pair {cfg.name}: max abs error {err:.3g}", flush=True)
     assert err < 5e-5  # much tighter than the tolerance: hi/lo bf16 split + fp32 sums
+
+
+@pytest.mark.parametrize("name", ["small_batch", "throughput", "sampled"])
+def test_pair_scores_full_size(name, full_workload, full_oracle):
+    # the step chain on a full-size workload: every sequence's 16 x 16 score tiles against the
+    # oracle's, element by element (the GPU's own top-16 and gate feed the pair step; both
+    # were checked bit for bit / to the gate's bar against the same oracle results)
+    dfs = dfs_mod()
+    inp, dev = full_workload(name)
+    cfg = inp.config
+    idx, val = dfs.topk(dev["logits"])
+    g = dfs.gate(dev["hidden"], dev["W_h"])
+    pair = dfs.pair_scores(idx, val, dev["prev_token"], g, dev["A"], dev["B"])
+    torch.cuda.synchronize()
+    want = full_oracle(name)
+    np.testing.assert_array_equal(idx.cpu().numpy().reshape(cfg.batch, cfg.L, 16), stack(want, "cand_idx"))
+    got = pair.cpu().numpy()
+    ref = stack(want, "pair")
+    assert got.shape == ref.shape == (cfg.batch, cfg.L, 16, 16)
+    assert_scores(got, ref, f"pair {name}")
+    err = np.abs(got - ref)
+    print(f"pair {name}: {cfg.batch} sequences, max abs error {err.max():.3g}, "
+          f"max rel error {(err / np.maximum(np.abs(ref), 1e-30)).max():.3g}", flush=True)
+    record("pair", name, cfg.batch * cfg.L * 256, "scores", f"max abs error {err.max():.2g}")
 
 
 @pytest.mark.parametrize("cfg", PAIR_CASES, ids=lambda c: c.name)

@@ -6,7 +6,8 @@ import torch
 import oracle
 from workloads import CONFIGS, make, variant
 
-from .parity import to_dev
+from .oracle_pool import stack
+from .parity import record, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -38,20 +39,23 @@ def _check_rows(rows_np, dtype, idx, val, which):
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
-def test_topk_full_size_configs(cfg, full_workload):
-    # full-size launch; rows checked: all for the small workloads, a sample otherwise
+def test_topk_full_size_configs(cfg, full_workload, full_oracle):
+    # full-size launch; every row against the oracle's stable sort, bit for bit
     import draft_selection_position_amd as dfs
 
     inp, dev = full_workload(cfg.name)
-    print(f"topk {cfg.name}: rows {cfg.batch * cfg.L} V {cfg.V}", flush=True)
+    rows = cfg.batch * cfg.L
+    print(f"topk {cfg.name}: rows {rows} V {cfg.V}", flush=True)
     idx, val = dfs.topk(dev["logits"].view(-1, cfg.V))
     torch.cuda.synchronize()
     idx, val = idx.cpu().numpy(), val.cpu().numpy()
-    rows = inp.logits.reshape(-1, cfg.V)
-    rng = np.random.default_rng(7)
-    which = range(rows.shape[0]) if rows.shape[0] <= 16 else np.unique(
-        np.r_[0, rows.shape[0] - 1, rng.choice(rows.shape[0], 40, replace=False)])
-    _check_rows(rows, cfg.dtype, idx, val, which)
+    want = full_oracle(cfg.name)
+    oi = stack(want, "cand_idx").reshape(rows, 16)
+    ov = stack(want, "cand_val").reshape(rows, 16)
+    bad = np.nonzero((idx != oi).any(1) | (val.astype(np.float64) != ov).any(1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:8].tolist()}"
+    assert not np.signbit(val[val == 0]).any()
+    record("topk", cfg.name, rows, "rows", "bit-exact ids and values")
 
 
 VARIANTS = [
