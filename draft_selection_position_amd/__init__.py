@@ -41,7 +41,9 @@ _lock = threading.Lock()
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libdfs.so")
+    """libdfs.so next to this file, or the build that DFS_LIBRARY names (another build of the
+    same sources, e.g. the host-sanitized one the ABI tests run against)."""
+    return os.environ.get("DFS_LIBRARY") or os.path.join(_HERE, "libdfs.so")
 
 
 class _Shape(ctypes.Structure):

@@ -57,7 +57,16 @@ extern "C" {
 #define DFS_MAX_ROWS (1 << 22)
 #define DFS_CONV_MAX_L 65536 /* longest run of positions dfs_conv2 takes per sequence */
 
-typedef enum {
+/* C++ builds give the enums int as their fixed underlying type, so that every int a caller
+   passes (an unknown dtype or walk mode, say) is a value of the type that the argument
+   checks then reject, as in C; the size and calling convention are those of int either way. */
+#ifdef __cplusplus
+#define DFS_ENUM_BASE : int
+#else
+#define DFS_ENUM_BASE
+#endif
+
+typedef enum DFS_ENUM_BASE {
   DFS_OK = 0,
   DFS_E_NULL = 1,        /* a required pointer is NULL */
   DFS_E_SHAPE = 2,       /* a size is out of range (batch, rows < 1; V < 16; L not in [1,16];
@@ -73,9 +82,9 @@ typedef enum {
                             DFS_STATIC_SCRATCH_BYTES */
 } dfs_status_t;
 
-typedef enum { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype_t;
+typedef enum DFS_ENUM_BASE { DFS_F32 = 0, DFS_BF16 = 1 } dfs_dtype_t;
 
-typedef enum {
+typedef enum DFS_ENUM_BASE {
   DFS_WALK_GREEDY = 0, /* argmax successor at each step, lowest candidate slot on ties */
   DFS_WALK_GUMBEL = 1, /* Gumbel-max draw from softmax(S / temperature) over the 16 candidates */
   DFS_WALK_VITERBI = 2 /* the path of largest summed score (dynamic programming), see dfs_walk */

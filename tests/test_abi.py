@@ -305,3 +305,29 @@ def test_row_limit(L):
     assert L.dfs_lmhead_topk_workspace_bytes(M + 1, 1000, 512) == 0
     assert L.dfs_lmhead_topk_workspace_bytes(1 << 16, 1 << 24, 512) == 0  # 2^9 x 2^17 tiles
     assert L.dfs_lmhead_topk_workspace_bytes(4096, 151936, 5120) > 0
+
+
+EXTREMES = [-1, 0, 1, 2, 7, 8, 15, 16, 17, 31, 32, 33, 255, 256, 257, 4095, 4096, 4097, 151936, 262144,
+            (1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 22) - 1, 1 << 22, (1 << 22) + 1, (1 << 31) - 1, 1 << 31,
+            (1 << 62), -(1 << 62)]
+
+
+def test_planners_over_extreme_sizes(L):
+    # every workspace query plans the launches it would make; none may crash, overflow or
+    # report an absurd size for any int64 it is given (run under the host-sanitized build too)
+    import itertools
+
+    cap = 1 << 46
+    for a, b in itertools.product(EXTREMES, EXTREMES):
+        for dt in (0, 1, 5):
+            for q in (L.dfs_topk_workspace_bytes, L.dfs_gate_workspace_bytes, L.dfs_lmhead_topk_workspace_bytes):
+                args = (a, b, dt) if q is not L.dfs_lmhead_topk_workspace_bytes else (a, b, 4096)
+                assert q(*args) < cap
+        assert L.dfs_gate_pack_bytes(a, b & 1) < cap
+    for bsz, Ln, V, d in itertools.product([-1, 0, 1, 256, 1 << 22, 1 << 40], [0, 1, 16, 17],
+                                           [0, 16, 151936, (1 << 31) - 1, 1 << 31], [0, 8, 5120, 1 << 20, 1 << 21]):
+        for dt in (0, 1, 9):
+            s = dfs._shape(bsz, Ln, V, d, dt, dt, dt)
+            assert L.dfs_select_workspace_bytes(ctypes.byref(s)) < cap
+            assert L.dfs_verify_workspace_bytes(bsz, Ln, V, dt) < cap
+            assert L.dfs_conv2_workspace_bytes(bsz, Ln, d, dt) < cap
