@@ -189,24 +189,46 @@ __global__ __launch_bounds__(kGemmThreads) void gate_mfma_kernel(const uint16_t*
 // 128 x 128 tiles of Z on the LDS-DMA mainloop (mfma_big.h: four waves of 64 x 64,
 // operands straight from memory into an S-stage LDS ring), for row counts that give
 // enough tiles: W_h is read 128 rows at a time instead of 64, and no wave fetches
-// operands another wave also fetches.  The packed W_h is an operand whose row n of
-// k step ks sits at ks * 256 * 64 + n * 64 bytes.  Work items (K split, row tile,
+// operands another wave also fetches.  A ring step covers 64 k: whole 128-byte lines of
+// the H rows, and two packed W_h slabs (row n of slab ks sits at ks * 256 * 64 + n * 64
+// bytes, so the step's second 64 bytes of a row are one slab, 16 KB, further on).  The
+// products are added in the same k order as 32-k steps.  Work items (K split, row tile,
 // column half) are numbered column half fastest and cut into eight contiguous runs,
 // one per XCD: an XCD holds one K slice of W_h in its L2, and the two column halves
-// of a row tile read its H rows back to back (the second from L2).
+// of a row tile read its H rows back to back (the second from L2).  K-split partial
+// sums leave with non-temporal stores: another kernel reads them, mostly from another
+// XCD, and dirty lines left in L2 would be written back at the end of this kernel.
 #ifndef DFS_GATE_STAGES
 #define DFS_GATE_STAGES 4
 #endif
 #ifndef DFS_GATE_DMA_ROWS
 #define DFS_GATE_DMA_ROWS 512
 #endif
-using GC = big::Cfg<4, 4, DFS_GATE_STAGES>;
+#ifndef DFS_GATE_DMA_TM
+#define DFS_GATE_DMA_TM 4  // 16 x 16 tiles per wave along the rows
+#endif
+#ifndef DFS_GATE_DMA_TN
+#define DFS_GATE_DMA_TN 4  // and along the 256 columns
+#endif
+#ifndef DFS_GATE_DMA_WG_PER_CU
+#define DFS_GATE_DMA_WG_PER_CU 1
+#endif
+#ifndef DFS_GATE_NT_PARTIALS
+#define DFS_GATE_NT_PARTIALS 1  // partial sums bypass L2 on the way out (read by another kernel, often on another XCD)
+#endif
+#ifndef DFS_GATE_DMA_KK
+#define DFS_GATE_DMA_KK 64  // k per ring step: two packed slabs, whole 128-byte H lines
+#endif
+using GC = big::Cfg<DFS_GATE_DMA_TM, DFS_GATE_DMA_TN, DFS_GATE_STAGES, DFS_GATE_DMA_KK>;
+constexpr int kDmaSlabs = GC::KK / kKB;        // packed W_h slabs per ring step
 constexpr int kDmaBM = GC::BM;                 // 128 rows
 constexpr int kDmaBN = GC::BN;                 // 128 columns: two halves of the 256
+constexpr int kDmaHalves = kE / kDmaBN;        // column tiles per row tile
+static_assert(kDmaHalves * kDmaBN == kE, "column tiles cover the 256 columns");
 constexpr int kDmaPitch = kDmaBN + 4;          // fp32 per LDS row of the output tile
 constexpr int kDmaLds = GC::kLdsBytes > kDmaBM * kDmaPitch * 4 ? GC::kLdsBytes : kDmaBM * kDmaPitch * 4;
 
-__global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* __restrict__ H,
+__global__ __launch_bounds__(kThreads, DFS_GATE_DMA_WG_PER_CU) void gate_dma_kernel(const uint16_t* __restrict__ H,
                                                                const uint16_t* __restrict__ Wp,
                                                                int64_t rows, int64_t d, int mtiles,
                                                                int splits, int kps, int per_xcd,
@@ -214,18 +236,21 @@ __global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* _
                                                                float* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds[kDmaLds];
   const int64_t t = (int64_t)(blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
-  if (t >= (int64_t)splits * mtiles * 2) return;
-  const int nh = (int)(t & 1);
-  const int mt = (int)((t >> 1) % mtiles);
-  const int s = (int)((t >> 1) / mtiles);
+  if (t >= (int64_t)splits * mtiles * kDmaHalves) return;
+  const int nh = (int)(t % kDmaHalves);
+  const int mt = (int)((t / kDmaHalves) % mtiles);
+  const int s = (int)((t / kDmaHalves) / mtiles);
   const int64_t m0 = (int64_t)mt * kDmaBM;
   const int tile_rows = (int)(rows - m0 < kDmaBM ? rows - m0 : kDmaBM);
-  const int KB = (int)(d / kKB);
+  const int KB = (int)(d / GC::KK);  // ring steps over the whole K
   const int ks0 = s * kps;
   const int ks1 = ks0 + kps < KB ? ks0 + kps : KB;
-  const big::Operand a = big::rows_operand(H + m0 * d, tile_rows, d);
-  const big::Operand b = big::make_operand(Wp + nh * kDmaBN * kKB, (int64_t)KB * kE * kKB * 2 - nh * kDmaBN * kKB * 2,
-                                           (uint32_t)(kKB * 2), (uint32_t)(kE * kKB * 2));
+  const big::Operand a = big::rows_operand(H + m0 * d, tile_rows, d, GC::KK);
+  // row n of ring step ks: slab kDmaSlabs * ks (+ 1 for the second 64 bytes) at n * 64
+  const big::Operand b = big::make_operand(Wp + nh * kDmaBN * kKB,
+                                           (int64_t)(d / kKB) * kE * kKB * 2 - nh * kDmaBN * kKB * 2,
+                                           (uint32_t)(kKB * 2), (uint32_t)(kDmaSlabs * kE * kKB * 2),
+                                           (uint32_t)(kE * kKB * 2));
   GC::Acc acc;
   GC::zero(acc);
   big::mma<GC>(a, b, ks0, ks1, lds, acc);
@@ -243,15 +268,22 @@ __global__ __launch_bounds__(kThreads, 1) void gate_dma_kernel(const uint16_t* _
         sOut[(16 * GC::TM * wm + 16 * mt_ + 4 * q + i) * kDmaPitch + 16 * GC::TN * wn + 16 * nt + r] =
             acc.v[mt_][nt][i];
   __syncthreads();
-  const int c4 = tid & 31;  // 32 float4 per row
-  for (int rr = tid >> 5; rr < tile_rows; rr += kThreads / 32) {
+  constexpr int kRowF4 = kDmaBN / 4;  // float4 per row of the tile
+  const int c4 = tid % kRowF4;
+  for (int rr = tid / kRowF4; rr < tile_rows; rr += kThreads / kRowF4) {
     float4 v = *reinterpret_cast<const float4*>(&sOut[rr * kDmaPitch + 4 * c4]);
     const int64_t col = (int64_t)(m0 + rr) * kE + nh * kDmaBN + 4 * c4;
     if (splits == 1) {
       v = make_float4(sigmoidf(v.x), sigmoidf(v.y), sigmoidf(v.z), sigmoidf(v.w));
       *reinterpret_cast<float4*>(out + col) = v;
     } else {
+#if DFS_GATE_NT_PARTIALS
+      typedef float f32x4_t __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<f32x4_t*>(partial + (int64_t)s * rows * kE + col));
+#else
       *reinterpret_cast<float4*>(partial + (int64_t)s * rows * kE + col) = v;
+#endif
     }
   }
 }
@@ -305,27 +337,39 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
       p.mtiles = (int)cdiv(rows, gtile::kRows16);
       splits = cdiv(DFS_GATE_SMALL_WG, p.mtiles);
       min_steps = DFS_GATE_SMALL_MIN_STEPS;
-    } else if (rows >= DFS_GATE_DMA_ROWS && d % kKB == 0) {
-      // one workgroup per CU; at least eight k steps per split on the DMA ring
+    } else if (rows >= DFS_GATE_DMA_ROWS && d % GC::KK == 0) {
+      // one workgroup per CU; at least 256 k per split on the DMA ring, in whole ring steps
       p.kind = GatePlan::kDma;
       p.mtiles = (int)cdiv(rows, kDmaBM);
-      splits = cdiv(kTargetWG, (int64_t)p.mtiles * 2);
+      splits = cdiv(kTargetWG, (int64_t)p.mtiles * kDmaHalves);
       min_steps = 8;
+      const int64_t KS = d / GC::KK;
+      const int64_t max_splits = KS * kDmaSlabs / min_steps > 1 ? KS * kDmaSlabs / min_steps : 1;
+      if (splits > max_splits) splits = max_splits;
+      if (splits < 1) splits = 1;
+      const int64_t ks_per = cdiv(KS, splits);
+      p.kchunk = ks_per * GC::KK;
+      p.splits = (int)cdiv(KS, ks_per);
+      p.packed_off = 0;
+      p.packed_bytes = gate_packed_bytes(d);
+      off = p.packed_bytes;
     } else {
       p.kind = GatePlan::kTile64;
       p.mtiles = (int)cdiv(rows, kTileM);
       splits = cdiv(kTargetWG, p.mtiles);
       min_steps = 2;
     }
-    const int64_t max_splits = KB / min_steps > 1 ? KB / min_steps : 1;
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
-    const int64_t kb_per = cdiv(KB, splits);
-    p.kchunk = kb_per * kKB;
-    p.splits = (int)cdiv(KB, kb_per);
-    p.packed_off = 0;
-    p.packed_bytes = gate_packed_bytes(d);
-    off = p.packed_bytes;
+    if (p.kind != GatePlan::kDma) {
+      const int64_t max_splits = KB / min_steps > 1 ? KB / min_steps : 1;
+      if (splits > max_splits) splits = max_splits;
+      if (splits < 1) splits = 1;
+      const int64_t kb_per = cdiv(KB, splits);
+      p.kchunk = kb_per * kKB;
+      p.splits = (int)cdiv(KB, kb_per);
+      p.packed_off = 0;
+      p.packed_bytes = gate_packed_bytes(d);
+      off = p.packed_bytes;
+    }
   } else {
     p.kind = GatePlan::kJobs;
     p.mtiles = (int)cdiv(rows, gtile::kF32Rows);
@@ -384,9 +428,9 @@ hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W
     const uint16_t* Wp = static_cast<const uint16_t*>(W);
     const uint16_t* H = static_cast<const uint16_t*>(hidden);
     if (p.kind == GatePlan::kDma) {
-      const int per_xcd = (int)cdiv((int64_t)p.splits * p.mtiles * 2, 8);
+      const int per_xcd = (int)cdiv((int64_t)p.splits * p.mtiles * kDmaHalves, 8);
       gate_dma_kernel<<<dim3((unsigned)(8 * per_xcd)), kThreads, 0, stream>>>(
-          H, Wp, p.rows, p.d, p.mtiles, p.splits, (int)(p.kchunk / kKB), per_xcd, partial, out_gate);
+          H, Wp, p.rows, p.d, p.mtiles, p.splits, (int)(p.kchunk / GC::KK), per_xcd, partial, out_gate);
     } else {
       const dim3 grid((unsigned)((int64_t)p.mtiles * p.splits));
       gate_mfma_kernel<<<grid, kGemmThreads, 0, stream>>>(H, Wp, p.rows, p.d, p.kchunk, p.splits, partial,

@@ -80,14 +80,15 @@ __device__ __forceinline__ rsrc_t span_rsrc(const void* p, int64_t bytes) {
 }
 
 // An operand: its range (reads past it return zeros) and where row `row`'s bytes of
-// k step `ks` start: row * row_bytes + ks * step_bytes.
+// k step `ks` start: row * row_bytes + ks * step_bytes.  A 64-k step's 128 bytes are two
+// 64-byte halves, the second `half_bytes` after the first (64 when the row is contiguous).
 struct Operand {
   rsrc_t rsrc;
-  uint32_t row_bytes, step_bytes;
+  uint32_t row_bytes, step_bytes, half_bytes;
 };
 __device__ __forceinline__ Operand make_operand(const void* p, int64_t bytes, uint32_t row_bytes,
-                                                uint32_t step_bytes) {
-  return Operand{span_rsrc(p, bytes), row_bytes, step_bytes};
+                                                uint32_t step_bytes, uint32_t half_bytes = 64) {
+  return Operand{span_rsrc(p, bytes), row_bytes, step_bytes, half_bytes};
 }
 // Row-major [nrows, K] bf16 starting at p, steps of kk.
 __device__ __forceinline__ Operand rows_operand(const uint16_t* p, int64_t nrows, int64_t K, int kk = kK) {
@@ -134,8 +135,8 @@ __device__ __forceinline__ void load_step(char* stage, const Operand& a, const O
   const int rr = lane / C::kChunks;             // row within the instruction's R
   const int slot = lane % C::kChunks;           // LDS chunk slot
   const int chunk = chunk_slot<C>(slot, rr);    // global chunk stored there (the swizzle is an involution)
-  const uint32_t ka = (uint32_t)ks * a.step_bytes + 16u * chunk;
-  const uint32_t kb = (uint32_t)ks * b.step_bytes + 16u * chunk;
+  const uint32_t ka = (uint32_t)ks * a.step_bytes + 16u * (chunk & 3) + (uint32_t)(chunk >> 2) * a.half_bytes;
+  const uint32_t kb = (uint32_t)ks * b.step_bytes + 16u * (chunk & 3) + (uint32_t)(chunk >> 2) * b.half_bytes;
 #pragma unroll
   for (int i = 0; i < C::kLoadsPerWave; ++i) {
     const int j = wave + 4 * i;
@@ -267,7 +268,9 @@ __device__ __forceinline__ void mma(const Operand& a, const Operand& b, int ks0,
           bar();
           const int nxt = cur + kStages - 1;
           load_step<C>(st[(j + kStages - 1) % kStages], a, b, ks0 + (nxt < n ? nxt : n - 1), wave, lane);
-          if (cur + 1 < n) read_frags<C>(st[(j + 1) % kStages], wm, wn, r, q, f[(j + 1) & 1]);
+          // unconditional (after the last step it reads a stage nobody uses): a branch here
+          // would make the compiler wait for these reads before the MFMAs below
+          read_frags<C>(st[(j + 1) % kStages], wm, wn, r, q, f[(j + 1) & 1]);
           mfma_frags<C>(f[j & 1], acc);
         }
       }
