@@ -46,7 +46,7 @@ constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims fo
 #define DFS_GATE_SMALL_ROWS 64
 #endif
 #ifndef DFS_GATE_SMALL_WG
-#define DFS_GATE_SMALL_WG 32
+#define DFS_GATE_SMALL_WG 16
 #endif
 #ifndef DFS_GATE_SMALL_MIN_STEPS
 #define DFS_GATE_SMALL_MIN_STEPS 4

@@ -61,7 +61,7 @@ constexpr int kMinChunk = 4096;   // elements; below this a split does not pay
 constexpr int kMinSmallChunk = 1024;  // the same for the few-row plan
 // Few rows: workgroups the split aims for.
 #ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
-#define DFS_TOPK_SMALL_TARGET_BLOCKS 256
+#define DFS_TOPK_SMALL_TARGET_BLOCKS 64
 #endif
 
 template <bool kBf16>
@@ -340,7 +340,10 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
 // the four waves (shared through LDS) is the admission threshold from the start.  One
 // sort per wave finds it, typically one more merges the admitted keys, and one more
 // merges the four wave lists: the critical path of a workgroup that runs this code once.
-constexpr int kSmallVecs = 6;
+#ifndef DFS_TOPK_SMALL_VECS
+#define DFS_TOPK_SMALL_VECS 6
+#endif
+constexpr int kSmallVecs = DFS_TOPK_SMALL_VECS;
 
 template <bool kBf16>
 __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits, int64_t V, int parts, int64_t chunk,
