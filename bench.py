@@ -299,16 +299,17 @@ def main() -> int:
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    # Per-call spread first (each call between its own pair of events): it also keeps
-    # the timed figure below from depending on how short the warm-up is.
+    # Per-call spread first (each call between its own pair of events), over at least
+    # 200 calls: the first few dozen calls after start-up run several percent slower, so
+    # this also keeps the timed figure below from depending on how short the warm-up is.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(max(args.steps, 50))]
+           for _ in range(max(args.steps, 200))]
     for i, (a, b) in enumerate(evs):
         a.record()
         call(i)
         b.record()
     torch.cuda.synchronize()
-    per_call = np.array([a.elapsed_time(b) for a, b in evs])
+    per_call = np.array([a.elapsed_time(b) for a, b in evs])[50:]  # past the slow start
     pct = {f"p{q}": float(np.percentile(per_call, q)) for q in (10, 50, 90)}
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
