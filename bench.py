@@ -132,6 +132,68 @@ def traffic_record(fetch_dir: str, write_dir: str, copy_mb: int, workload: str) 
     print(f"algorithmic_bytes_per_launch: {rows * cfg.V * esize}")
 
 
+TABLE_WORKLOADS = ["tiny", "single_stream", "small_batch", "sampled", "throughput"]
+
+
+def _load_json(d, w):
+    with open(os.path.join(d, f"{w}.json")) as f:
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def bench_table(d: str) -> None:
+    """Print the all-workloads tables (markdown) from the JSON lines of
+    `bench.py --workload <w> --no-cpu-baseline --verify --conv --lmhead`, saved as DIR/<w>.json."""
+    from workloads import config_by_name
+
+    out = ["# bench.py on the five workloads, MI355X (one GPU)", "",
+           "Command (repository root), per workload: `python bench.py --workload <name> --no-cpu-baseline "
+           "--verify --conv --lmhead`",
+           "(20 warm-up calls, then per-call timing of at least 200 calls, then 200 timed `dfs_select_packed` calls; "
+           "hipEvents on the launch stream; input sets rotated so that at least 512 MB cycle through; "
+           "`python bench.py --bench-table <dir>` turns the JSON lines into these tables). "
+           "p50 is the median of single calls, each between its own events.", "",
+           "| workload | B x L x V, d | dfs_select us | p50 us | blocks/s | top-16 us | top-16 GB/s | % of 8 TB/s | "
+           "gate us (standalone call) | pair us (standalone call) |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for w in TABLE_WORKLOADS:
+        r = _load_json(d, w)
+        c = config_by_name(w)
+        sm = r["step_ms"]
+        esize = 2 if c.dtype == "bf16" else 4
+        gbs = c.batch * c.L * c.V * esize / (sm["topk"] * 1e-3) / 1e9
+        out.append(f"| {w} | {c.batch}x{c.L}x{c.V}, d {c.d}{', fp32' if esize == 4 else ''} | "
+                   f"{r['ms_per_step'] * 1e3:.1f} | {r['select_ms_per_call']['p50'] * 1e3:.1f} | "
+                   f"{r['value']:,.0f} | {sm['topk'] * 1e3:.1f} | {gbs:.0f} | {gbs / 80:.1f} | "
+                   f"{sm['gate'] * 1e3:.1f} | {sm['pair_scores'] * 1e3:.1f} |")
+    out += ["", "The standalone gate and pair calls are timed through Python one call after another and",
+            "include the host's submission time; inside `dfs_select` the kernel times are those of",
+            "profiles/select_throughput_kernel_trace.md.", "",
+            "Verification (`dfs_select_draft` then `dfs_verify` over target logits [B, L+1, V] of the workload's dtype):",
+            "", "| workload | draft us | verify us | target bytes | verify GB/s | % of 8 TB/s | accepted (mean) |",
+            "|---|---|---|---|---|---|---|"]
+    for w in TABLE_WORKLOADS:
+        v = _load_json(d, w)["verify"]
+        out.append(f"| {w} | {v['draft_ms'] * 1e3:.1f} | {v['verify_ms'] * 1e3:.1f} | {v['target_bytes']:,} | "
+                   f"{v['verify_GBps']:.0f} | {v['verify_frac_of_peak'] * 100:.1f} | {v['accepted_mean']:.2f} |")
+    out += ["", "Two-tap convolution (`dfs_conv2` on x [B, L, d] of the workload's dtype):", "",
+            "| workload | conv us | algorithmic bytes | GB/s | TFLOP/s | % of matrix peak |", "|---|---|---|---|---|---|"]
+    for w in TABLE_WORKLOADS:
+        v = _load_json(d, w)["conv"]
+        out.append(f"| {w} | {v['ms'] * 1e3:.1f} | {v['bytes_per_launch']:,} | {v['GBps']:.0f} | {v['TFLOPs']:.1f} | "
+                   f"{v['mfma_frac'] * 100:.1f} |")
+    out += ["", "Top-16 straight from the hidden states (`dfs_lmhead_topk`, W_lm [V, d] ~ N(0, 0.02); bf16 workloads):",
+            "", "| workload | fused ms | chain ms (logits + top-16) | TFLOP/s | W_lm GB/s | equal to chain |",
+            "|---|---|---|---|---|---|"]
+    for w in TABLE_WORKLOADS:
+        v = _load_json(d, w)["lmhead"]
+        if "skipped" in v:
+            out.append(f"| {w} | — | — | — | — | {v['skipped']} |")
+            continue
+        out.append(f"| {w} | {v['fused_ms']:.3f} | {v['chain_ms']:.3f} ({v['logits_ms']:.3f} + {v['topk_fp32_ms']:.3f}) | "
+                   f"{v['fused_TFLOPs']:.0f} | {v['fused_GBps']:.0f} | {v['fused_equals_chain']} |")
+    print("\n".join(out))
+
+
 def _affinity() -> int:
     try:
         return len(os.sched_getaffinity(0))
@@ -220,6 +282,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run device-to-device copies of this size (counter calibration)")
     ap.add_argument("--summarize-rocprof", metavar="DIR", help="print a summary of rocprofv3 csv output and exit")
+    ap.add_argument("--bench-table", metavar="DIR",
+                    help="print the all-workloads tables from DIR/<workload>.json bench lines and exit")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the top-16 traffic record from FETCH_SIZE / WRITE_SIZE counter runs and exit")
     ap.add_argument("--conv", action="store_true",
@@ -233,6 +297,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time dfs_select replayed from a captured HIP graph (one launch per step)")
     args = ap.parse_args()
+    if args.bench_table:
+        bench_table(args.bench_table)
+        return 0
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
         return 0
@@ -414,7 +481,7 @@ def main() -> int:
         tgt[:, cfg.L] = (1.5 * torch.randn((cfg.batch, cfg.V), generator=gen, device=lg.device)).to(tgt.dtype)
         del lg
         T = cfg.temperature if cfg.walk == "gumbel" else 1.0
-        dargs = (dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], dev["W_h"])
+        dargs = (dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], packed[0])
         sws = torch.empty(dfs.select_workspace_bytes(cfg.batch, cfg.L, cfg.V, cfg.d, dev["logits"].dtype,
                                                      dev["hidden"].dtype, dev["A"].dtype),
                           dtype=torch.uint8, device=logits2d.device)
