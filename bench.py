@@ -375,10 +375,8 @@ def main() -> int:
         a.record()
         call(i)
         b.record()
-    torch.cuda.synchronize()
-    per_call = np.array([a.elapsed_time(b) for a, b in evs])[50:]  # past the slow start
-    pct = {f"p{q}": float(np.percentile(per_call, q)) for q in (10, 50, 90)}
-
+    # (the per-call figures are read back after the timed steps, so that the GPU does not
+    # sit idle for the read-back right before them)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -389,6 +387,8 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    per_call = np.array([a.elapsed_time(b) for a, b in evs])[50:]  # past the slow start
+    pct = {f"p{q}": float(np.percentile(per_call, q)) for q in (10, 50, 90)}
     blocks_per_s = cfg.batch / (ms_per_step * 1e-3)
     path = sel.path.cpu().numpy()  # the last call's (every set holds the same values)
     scores_gpu = sel.scores.cpu().numpy()
