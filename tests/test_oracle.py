@@ -286,7 +286,51 @@ def test_viterbi_is_the_best_total_over_all_paths(L):
                  for js in itertools.product(range(16), repeat=L) if list(js) != list(slots)) \
         if L <= 2 else None
     if second is not None:
-        assert top - second >= margins.min() - 1e-12
+        # the runner-up takes the second-best choice at the closest decision, so the gap
+        # between the two best totals is exactly the smallest margin
+        assert abs((top - second) - margins.min()) < 1e-12
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("gumbel", 1.0), ("gumbel", 0.5)])
+def test_walk_margins_are_the_decision_gaps(mode, T):
+    # margins[t] is how far the chosen successor leads the runner-up at step t: raising the
+    # runner-up's score by a little less than margins[t] * T leaves the whole path alone,
+    # a little more makes step t take the runner-up (and nothing before t changes)
+    L, seed, b = 5, 0xC0FFEE, 3
+    S = RNG.standard_normal((L, 16, 16))
+    S[0] = S[0, 0][None, :]
+    cidx = np.stack([RNG.choice(1000, 16, replace=False) for _ in range(L)])
+    _, _, slots, margins = oracle.walk(S, cidx, mode, T, seed, b)
+    assert (margins > 0).all()
+    for t in range(L):
+        prev = 0 if t == 0 else int(slots[t - 1])
+        key = S[t, prev] / T
+        if mode == "gumbel":
+            key = key + np.array([oracle.gumbel(seed, b, t, j) for j in range(16)])
+        runner = int(np.argsort(-key, kind="stable")[1])
+        for factor, moves in ((0.99, False), (1.01, True)):
+            S2 = S.copy()
+            rows = [prev] if t > 0 else range(16)  # position 0's rows all hold the same row
+            for r in rows:
+                S2[t, r, runner] += margins[t] * T * factor
+            _, _, slots2, _ = oracle.walk(S2, cidx, mode, T, seed, b)
+            np.testing.assert_array_equal(slots2[:t], slots[:t])
+            assert (slots2[t] == runner) == moves, (t, factor)
+            if not moves:
+                np.testing.assert_array_equal(slots2, slots)
+
+
+def test_walk_margins_planted_gaps():
+    # rows with known leads: at step t the best successor leads by 2^-t exactly
+    L = 4
+    S = np.zeros((L, 16, 16))
+    for t in range(L):
+        S[t, :, 3] = 1.0
+        S[t, :, 7] = 1.0 - 2.0 ** -t
+    cidx = np.stack([np.arange(16) + 100 * t for t in range(L)])
+    _, _, slots, margins = oracle.walk(S, cidx)
+    np.testing.assert_array_equal(slots, [3] * L)
+    np.testing.assert_array_equal(margins, [2.0 ** -t for t in range(L)])
 
 
 def test_viterbi_ties_take_lowest_slots():
