@@ -180,17 +180,17 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   const bool bf16_logits = s.logits_dtype == DFS_BF16;
   const bool bf16_act = s.act_dtype == DFS_BF16;
   // Two or three launches on one stream.  (1) The top-16 pass; rows split into parts
-  // leave their partial lists for the pair kernel to merge.  With few rows and a gate
-  // that needs no repacking (fp32, or W_h packed by the caller) the gate's tiles ride
-  // in the same launch; otherwise the W_h packing slabs (when needed) ride in its tail
-  // and (2) the gate GEMM follows.  (3) Pair scores and the walk, which also merges the
+  // leave their partial lists for the pair kernel to merge.  Up to kGateTileRows rows,
+  // with a gate that needs no repacking (fp32, or W_h packed by the caller), the gate's
+  // tiles ride in the same launch; otherwise the W_h packing slabs (when needed) ride
+  // in its tail and (2) the gate GEMM follows.  (3) Pair scores and the walk, which also merges the
   // split rows' lists and adds up the gate's K-split partial sums: one workgroup per
   // sequence, or with few rows one per position (the last of a sequence walks it; its
   // counters are zeroed by launch (1)).
   uint32_t* counters = reinterpret_cast<uint32_t*>(w + l.counters_off);
   const ZeroJob zj = l.few ? ZeroJob{counters, (int)s.batch} : ZeroJob{};
   hipError_t e;
-  if (l.gate.kind == GatePlan::kJobs && (wh_packed || !bf16_act)) {
+  if (l.gate.kind == GatePlan::kJobs && s.batch * s.L <= kGateTileRows && (wh_packed || !bf16_act)) {
     const GateJobs gj = gate_jobs(l.gate, hidden, W_h, gate, gws);
     e = launch_topk_gate(l.topk, logits, bf16_logits, cand_idx, cand_val, tws, gj, bf16_act, zj, stream);
     if (e != hipSuccess) return DFS_E_HIP;

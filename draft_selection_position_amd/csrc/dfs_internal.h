@@ -67,6 +67,11 @@ hipError_t launch_topk_merge(const uint64_t* partial, int64_t rows, int parts, i
                              float* out_val, hipStream_t stream);
 
 // ---------------------------------------------------------------- gate
+// Up to this many rows the bf16 gate runs as 16-row tiles (gate_tile.h), and the fused
+// selector puts those tiles (or the fp32 tiles) into its top-16 launch when W_h needs no
+// repacking: the top-16 pass runs at most two workgroups per CU there and leaves room.
+constexpr int64_t kGateTileRows = 512;
+
 struct GatePlan {
   enum Kind { kJobs = 0, kTile64 = 1, kDma = 2 };
   int64_t rows, d;

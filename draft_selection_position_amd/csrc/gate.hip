@@ -12,11 +12,12 @@
 // (dfs_gate_pack), or per call into the workspace.  Both operands are then read
 // straight from memory with 16-byte loads.  Three tilings, one operand layout (so
 // a K split adds the same products in the same order in each):
-//   - up to 64 rows: 16-row x 256-column tiles of four waves (gate_tile.h), K split
-//     across workgroups; the same tiles ride in the top-16 launch of the fused
-//     selector when W_h comes pre-packed;
-//   - from 512 rows (d a multiple of 32): 128 x 128 LDS-DMA tiles (gate_dma_kernel);
-//   - in between: 64-row x 256-column tiles of eight waves sharing the H tile in LDS.
+//   - up to 512 rows: 16-row x 256-column tiles of four waves (gate_tile.h), K split
+//     across about 16 workgroups (up to 64 rows) or 256 (more); the same tiles ride in
+//     the top-16 launch of the fused selector when W_h comes pre-packed, where that
+//     pass leaves CU slots free (it runs one or two workgroups per CU at these sizes);
+//   - from 512 rows (d a multiple of 64): 128 x 128 LDS-DMA tiles (gate_dma_kernel);
+//   - otherwise: 64-row x 256-column tiles of eight waves sharing the H tile in LDS.
 // Row counts too small to fill the chip split K; the partial sums are added in split
 // order (by the finish kernel here, or by the pair kernel that reads the gate) before
 // the sigmoid.
@@ -40,13 +41,17 @@ static_assert(kKB == kPackK, "the GEMM steps through W_h one packed slab at a ti
 #define DFS_GATE_TARGET_WG 256
 #endif
 constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims for
-// Few rows (16-row tiles): up to this many rows, about this many workgroups, at least
-// this many k steps per split.
+// 16-row tiles up to kGateTileRows rows: about DFS_GATE_SMALL_WG workgroups up to
+// DFS_GATE_SMALL_ROWS rows (their partial sums are added on the critical path of a
+// short call), about DFS_GATE_JOBS_WG beyond; at least this many k steps per split.
 #ifndef DFS_GATE_SMALL_ROWS
 #define DFS_GATE_SMALL_ROWS 64
 #endif
 #ifndef DFS_GATE_SMALL_WG
 #define DFS_GATE_SMALL_WG 16
+#endif
+#ifndef DFS_GATE_JOBS_WG
+#define DFS_GATE_JOBS_WG 256
 #endif
 #ifndef DFS_GATE_SMALL_MIN_STEPS
 #define DFS_GATE_SMALL_MIN_STEPS 4
@@ -330,12 +335,12 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   if (bf16) {
     const int64_t KB = cdiv(d, kKB);
     int64_t splits, min_steps;
-    if (rows <= DFS_GATE_SMALL_ROWS) {
-      // few rows: 16-row tiles, K split over about kSmallWG workgroups (at least
-      // kSmallMinSteps k steps each, so that a tile's loads overlap)
+    if (rows <= kGateTileRows) {
+      // 16-row tiles, K split over about DFS_GATE_SMALL_WG or DFS_GATE_JOBS_WG workgroups
+      // (at least DFS_GATE_SMALL_MIN_STEPS k steps each, so that a tile's loads overlap)
       p.kind = GatePlan::kJobs;
       p.mtiles = (int)cdiv(rows, gtile::kRows16);
-      splits = cdiv(DFS_GATE_SMALL_WG, p.mtiles);
+      splits = cdiv(rows <= DFS_GATE_SMALL_ROWS ? DFS_GATE_SMALL_WG : DFS_GATE_JOBS_WG, p.mtiles);
       min_steps = DFS_GATE_SMALL_MIN_STEPS;
     } else if (rows >= DFS_GATE_DMA_ROWS && d % GC::KK == 0) {
       // one workgroup per CU; at least 256 k per split on the DMA ring, in whole ring steps

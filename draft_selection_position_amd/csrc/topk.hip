@@ -60,6 +60,11 @@ constexpr int kCap = kMergeAt + 8 * kWave;  // room for one whole vector per lan
 constexpr int kMinChunk = 4096;   // elements; below this a split does not pay
 constexpr int kMinSmallChunk = 1024;  // the same for the few-row plan
 // Few rows: workgroups the split aims for.
+// Whole rows in the launch that carries the gate's tiles: sorts inlined (false) or as
+// out-of-line calls (true).
+#ifndef DFS_TOPK_GATE_COMPACT
+#define DFS_TOPK_GATE_COMPACT false
+#endif
 #ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
 #define DFS_TOPK_SMALL_TARGET_BLOCKS 64
 #endif
@@ -452,9 +457,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
   topk_body<kBf16, false>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
 }
 
-// The pass with the gate's jobs (few rows) as the first workgroups of the launch: the
-// gate tiles hold more registers than the pass's 8-waves-per-SIMD budget, which few
-// rows do not need.
+// The pass with the gate's jobs as the first workgroups of the launch, for up to 512
+// rows: the gate tiles hold more registers than the pass's 8-waves-per-SIMD budget,
+// which it does not need at those sizes (one or two of its workgroups per CU), so the
+// tiles run in the CU slots it leaves free.
 template <bool kBf16, bool kGateBf16>
 __global__ __launch_bounds__(kThreads) void topk_gate_kernel(const void* __restrict__ logits, int64_t V, int parts,
                                                              int64_t chunk, uint64_t* __restrict__ partial,
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void topk_gate_kernel(const void* __restr
   if (chunk <= (int64_t)kSmallVecs * kThreads * Elems<kBf16>::per_vec) {
     topk_small_body<kBf16>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
   } else {
-    topk_body<kBf16, true>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+    topk_body<kBf16, DFS_TOPK_GATE_COMPACT>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
   }
 }
 

@@ -208,7 +208,8 @@ int dfs_select(const void* logits, const void* hidden, const int32_t* prev_token
                double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,
                float* out_scores, hipStream_t stream);
 /* dfs_select with W_h already packed by dfs_gate_pack (the same bits).  With few rows
- * (batch * L <= 64) the gate then runs inside the top-16 launch: two kernels per call. */
+ * (batch * L <= 512) the gate then runs inside the top-16 launch; up to 64 rows a call
+ * is two kernels. */
 int dfs_select_packed(const void* logits, const void* hidden, const int32_t* prev_token, const void* A,
                       const void* B, const void* W_packed, int k, const dfs_shape_t* shape, dfs_walk_t mode,
                       double temperature, uint64_t seed, void* ws, size_t ws_bytes, int32_t* out_path,

@@ -29,14 +29,18 @@ def dfs_mod():
 
 
 # rows = batch * L: 8 and 16 (the gate's tiles ride in the top-16 launch when W_h is
-# packed), 80 (64-row gate tiles), 1 (one row split 64 ways), 600 (LDS-DMA gate);
-# fp32 (tiny); d not a multiple of 32
+# packed, per-position pair workgroups), 80, 195, 320 and 512 (the gate's tiles still in
+# the top-16 launch, 256-way K split, one pair workgroup per sequence), 1 (one row split
+# 64 ways), 600 (LDS-DMA gate); fp32 (tiny); d not a multiple of 32
 SHAPES = [
     variant("tiny", emb_std=0.3),
     variant("single_stream", emb_std=0.3, V=151936, d=5120),
     variant("single_stream", emb_std=0.3, batch=5, V=20000, d=256),
     variant("single_stream", emb_std=0.3, batch=1, L=1, V=262144, d=512),
     variant("single_stream", emb_std=0.3, batch=3, L=7, V=32001, d=72),
+    variant("small_batch", emb_std=0.3, batch=13, L=15, V=32001, d=72),
+    variant("small_batch", emb_std=0.3, batch=20, L=16, V=20000, d=1024),
+    variant("small_batch", emb_std=0.3, batch=32, L=16, V=20000, d=5120),
     variant("small_batch", emb_std=0.3, batch=40, L=15, V=20000, d=1024),
 ]
 
