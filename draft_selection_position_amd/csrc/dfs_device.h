@@ -100,6 +100,43 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
   return x;
 }
 
+// The wave sorted descending when it holds four descending runs of 16 keys (lanes
+// 16 r .. 16 r + 15): the odd runs are reversed (DPP row mirror), which leaves the
+// alternating runs that the first four phases of the bitonic sort would have made, and
+// only its last two phases run (11 exchange steps instead of 21).
+__device__ __forceinline__ uint64_t wave_merge_runs16(uint64_t x, int lane) {
+  const uint32_t mlo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, 0x140, 0xF, 0xF, false);
+  const uint32_t mhi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), 0x140, 0xF, 0xF, false);
+  if (lane & 16) x = ((uint64_t)mhi << 32) | mlo;
+#pragma unroll
+  for (int k = 32; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = shfl_xor_u64(x, j, lane);
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;
+      const bool take_max = (lower == desc);
+      const uint64_t mx = x > y ? x : y;
+      const uint64_t mn = x > y ? y : x;
+      x = take_max ? mx : mn;
+    }
+  }
+  return x;
+}
+
+// The 16th largest of one 32-bit key per lane (0 when fewer than 16 lanes hold a key
+// above 0), found bit by bit from the top: a prefix stays when at least 16 lanes are
+// at or above it.  Wave-uniform.
+__device__ __forceinline__ uint32_t wave_16th_largest(uint32_t key) {
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    if (__popcll(__ballot(key >= cand)) >= 16) prefix = cand;
+  }
+  return prefix;
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -194,10 +194,9 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
 #pragma unroll
   for (int e = 1; e < PV; ++e) m = fmaxf(m, v[e]);
   if (seed) {
-    const uint64_t lk = (m == m) ? make_key(m, (uint32_t)lane) : 0ull;
-    const uint64_t k16 = lane_u64(sort_desc<kCompact>(lk, lane), 15);
-    if (k16 != 0) {
-      const float t = key_value(k16);
+    const uint32_t k16 = wave_16th_largest(m == m ? mono32(m) : 0u);
+    if (k16 != 0u) {
+      const float t = unmono32(k16);
       if (t > w.thr) w.thr = uniformf(t);
     }
   }
@@ -327,7 +326,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
   if (lane < kK) s_list[wave * kK + lane] = w.list;
   __syncthreads();
   if (wave == 0) {
-    const uint64_t x = sort_desc<kCompact>(s_list[lane], lane);  // kWaves * kK == 64 keys
+    const uint64_t x = wave_merge_runs16(s_list[lane], lane);  // the four waves' sorted lists
     if (lane < kK) {
       if (parts == 1) {
         out_idx[row * kK + lane] = (int32_t)key_index(x);
@@ -342,9 +341,10 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
 // Few rows: a chunk of at most kSmallVecs vectors per thread is loaded whole before any
 // compare.  Every lane's maximum over its vectors is a distinct element, so the 16th
 // largest lane maximum of any wave bounds the chunk's top 16; the largest such bound over
-// the four waves (shared through LDS) is the admission threshold from the start.  One
-// sort per wave finds it, typically one more merges the admitted keys, and one more
-// merges the four wave lists: the critical path of a workgroup that runs this code once.
+// the four waves (shared through LDS) is the admission threshold from the start.  A
+// bitwise search over ballots finds it, typically one sort merges the admitted keys, and
+// a merge of four sorted runs joins the wave lists: the critical path of a workgroup that
+// runs this code once.
 #ifndef DFS_TOPK_SMALL_VECS
 #define DFS_TOPK_SMALL_VECS 6
 #endif
@@ -406,9 +406,8 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
   }
   __syncthreads();  // lds.thr cleared
   {
-    const uint64_t lk = (m == m) ? make_key(m, (uint32_t)lane) : 0ull;
-    const uint64_t k16 = lane_u64(sort_desc<true>(lk, lane), 15);
-    if (k16 != 0 && lane == 0) atomicMax(&lds.thr, (uint32_t)(k16 >> 32));
+    const uint32_t k16 = wave_16th_largest(m == m ? mono32(m) : 0u);
+    if (k16 != 0u && lane == 0) atomicMax(&lds.thr, k16);
   }
   __syncthreads();
   uint64_t* buf = lds.buf[wave];
@@ -427,7 +426,7 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
   if (lane < kK) lds.list[wave * kK + lane] = w.list;
   __syncthreads();
   if (wave == 0) {
-    const uint64_t x = sort_desc<true>(lds.list[lane], lane);
+    const uint64_t x = wave_merge_runs16(lds.list[lane], lane);  // the four waves' sorted lists
     if (lane < kK) {
       if (parts == 1) {
         out_idx[row * kK + lane] = (int32_t)key_index(x);

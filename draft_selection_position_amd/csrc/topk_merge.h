@@ -1,8 +1,8 @@
 // Merge of one row's partial top-16 lists (64-bit keys, 0 = empty; key order is value
 // descending, then the lower token id) by four waves: each wave folds its share of the
-// lists into its own top-16 with 64-lane sorts (its list plus three more per sort),
-// then one wave sorts the four lists.  Used by the merge pass of the top-16 kernel
-// and by merge jobs that ride along in another launch.
+// lists into its own top-16 with 64-lane merges of four sorted runs (its list plus
+// three more per merge), then one wave merges the four lists.  Used by the merge pass
+// of the top-16 kernel and by merge jobs that ride along in another launch.
 #pragma once
 
 #include "dfs_device.h"
@@ -28,14 +28,14 @@ __device__ __forceinline__ void merge_row_lists(const uint64_t* __restrict__ src
         const int p = p0 + (lane - kK) / kK;
         if (p < parts) x = src[(int64_t)p * kK + (lane & (kK - 1))];
       }
-      x = wave_sort_desc(x, lane);
+      x = wave_merge_runs16(x, lane);  // the list and up to three partial lists, each sorted
       list = lane < kK ? x : 0;
     }
   }
   if (lane < kK) s_list[wave * kK + lane] = list;
   __syncthreads();
   if (live && wave == 0) {
-    const uint64_t x = wave_sort_desc(s_list[lane], lane);
+    const uint64_t x = wave_merge_runs16(s_list[lane], lane);
     if (lane < kK) {
       out_idx[lane] = (int32_t)key_index(x);
       out_val[lane] = key_value(x);
