@@ -68,11 +68,13 @@ VARIANTS = [
     variant("sampled", emb_std=0.3, batch=6, V=50000, d=256, temperature=0.7, walk_seed=12345),
     variant("sampled", emb_std=0.3, batch=3, V=50000, d=256, L=5, temperature=2.0, walk_seed=2**63 + 5),
     variant("throughput", emb_std=0.3, batch=3, V=40000, d=1024),
-    # 256 rows: the gate's K split is 4, 2 and 1 wide for d = 256, 128, 64, so the
-    # pair kernel adds the partial sums itself (or the GEMM finishes the gate)
+    # 256 rows: 16-row gate tiles with a K split 2, 1 and 1 wide for d = 256, 128, 64, so
+    # the pair kernel adds the partial sums itself (or the tiles finish the gate)
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=256),
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=128),
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=64),
+    # 600 rows, d = 16384: the LDS-DMA gate over 20 K splits, all added by the pair kernel
+    variant("small_batch", emb_std=0.3, batch=40, L=15, V=20000, d=16384),
     # the best-total-path walk
     variant("tiny", emb_std=0.3, walk="viterbi"),
     variant("tiny", emb_std=0.3, L=1, walk="viterbi"),
