@@ -20,7 +20,10 @@
 // embedding A(a) * g (fp32) is split as hi + lo in bf16 and fed to two MFMAs, so
 // the products are exact to ~2^-17 before fp32 accumulation.  Each wave reduces
 // its tile to the successor of every predecessor slot; one lane then follows the
-// chain through LDS.
+// chain through LDS.  With few rows (one or a few sequences) a workgroup per sequence
+// would put all the gathers behind a handful of CUs, so pair_pos_kernel gives each
+// position a workgroup of its own and lets the last of a sequence's workgroups (an
+// atomic ticket after a device-wide release) run the walk.
 #include "dfs_device.h"
 #include "dfs_internal.h"
 #include "philox.h"
