@@ -65,6 +65,12 @@ constexpr int kMinSmallChunk = 1024;  // the same for the few-row plan
 #ifndef DFS_TOPK_GATE_COMPACT
 #define DFS_TOPK_GATE_COMPACT false
 #endif
+// The pass seeds each workgroup's threshold from its waves' whole first iteration (one
+// barrier) when all its workgroups fit one round on the chip (256 CUs x 8 workgroups at
+// 8 waves per SIMD): then every workgroup starts at once and an early threshold saves
+// admissions (1024 rows x 262144: -1.8 us, 512 rows x 151936: -0.8 us); with two rounds
+// (4096 rows) the barrier costs more than it saves (+1.8 us).
+constexpr int64_t kWideSeedMaxBlocks = 2048;
 #ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
 #define DFS_TOPK_SMALL_TARGET_BLOCKS 64
 #endif
@@ -168,6 +174,18 @@ __device__ __forceinline__ float load_scalar(const typename Elems<kBf16>::T* p, 
   }
 }
 
+// The largest of one 16-byte vector's elements (NaN, which fmaxf ignores, when invalid).
+template <bool kBf16>
+__device__ __forceinline__ float vec_max(uint4 d, bool valid) {
+  if (!valid) return __int_as_float(0x7fffffff);
+  if constexpr (kBf16) {
+    return fmaxf(fmaxf(fmaxf(bf16_lo(d.x), bf16_hi(d.x)), fmaxf(bf16_lo(d.y), bf16_hi(d.y))),
+                 fmaxf(fmaxf(bf16_lo(d.z), bf16_hi(d.z)), fmaxf(bf16_lo(d.w), bf16_hi(d.w))));
+  } else {
+    return fmaxf(fmaxf(__uint_as_float(d.x), __uint_as_float(d.y)), fmaxf(__uint_as_float(d.z), __uint_as_float(d.w)));
+  }
+}
+
 // Admission test and append for one 16-byte vector (8 bf16 or 4 fp32 values),
 // then a merge if the buffer has filled past kMergeAt.  A vector past the end of
 // the chunk (`valid` false) is replaced by NaNs, which never pass.  On a wave's
@@ -217,7 +235,7 @@ static_assert(sizeof(TopkLds::buf) >= gtile::kF32LdsBytes, "a gate job reuses th
 // One (row, part) of the pass: workgroup `bid` of the rows.  kCompact: the sorts are
 // out-of-line calls (few rows: each wave runs the code about once).  kU: 16-byte vectors
 // per thread per iteration (two iterations in flight).
-template <bool kBf16, bool kCompact, int kU = kUnroll>
+template <bool kBf16, bool kCompact, bool kWide, int kU = kUnroll>
 __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64_t V, int parts, int64_t chunk,
                                           uint64_t* __restrict__ partial, int32_t* __restrict__ out_idx,
                                           float* __restrict__ out_val, int64_t bid, TopkLds& lds) {
@@ -297,13 +315,24 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
       for (int u = 0; u < kU; ++u) {
         const int64_t vid = it * step + (int64_t)u * kThreads + tid;
         scan_vec<kBf16, kCompact>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
-                        &s_thr, lane, it == 0 && u == 0);
+                        &s_thr, lane, !kWide && it == 0 && u == 0);
       }
     };
     constexpr std::false_type kInside{};
     constexpr std::true_type kEdge{};
     const int64_t nfull = nvec / step;  // iterations with every vector inside the chunk
     load_iter(bufA, 0);
+    if constexpr (kWide) {
+      // The 16th-largest lane maximum over a wave's first iteration bounds the chunk's top
+      // 16 (every lane maximum is a distinct element); the largest such bound over the
+      // waves is where every wave's threshold starts (scan_iter reads it back).
+      float m = __int_as_float(0x7fffffff);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) m = fmaxf(m, vec_max<kBf16>(bufA[u], (int64_t)u * kThreads + tid < nvec));
+      const uint32_t k16 = wave_16th_largest(m == m ? mono32(m) : 0u);
+      if (k16 != 0u && lane == 0) atomicMax(&s_thr, k16);
+      __syncthreads();
+    }
     int64_t it = 0;
     // bufA holds iteration `it` at the top of each loop; no exit in the middle of an
     // iteration pair, so the compiler's load waits stay exact
@@ -440,7 +469,7 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
 
 // The pass over `ntopk` = rows * parts workgroups; W_h packing slabs (the fused
 // selector) ride as extra workgroups after or before the rows.
-template <bool kBf16>
+template <bool kBf16, bool kWide>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TOPK_WAVES_PER_EU))) void topk_chunk_kernel(
     const void* __restrict__ logits, int64_t V, int parts, int64_t chunk, uint64_t* __restrict__ partial,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, int64_t ntopk, PackJob pack, ZeroJob zero) {
@@ -453,7 +482,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
     pack_w_slab(pack.W, pack.d, pack.Wp, job, threadIdx.x, reinterpret_cast<uint16_t(*)[kPackPitch]>(&lds.buf[0][0]));
     return;
   }
-  topk_body<kBf16, false>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+  topk_body<kBf16, false, kWide>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
 }
 
 // The pass with the gate's jobs as the first workgroups of the launch, for up to 512
@@ -478,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void topk_gate_kernel(const void* __restr
   if (chunk <= (int64_t)kSmallVecs * kThreads * Elems<kBf16>::per_vec) {
     topk_small_body<kBf16>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
   } else {
-    topk_body<kBf16, DFS_TOPK_GATE_COMPACT>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+    topk_body<kBf16, DFS_TOPK_GATE_COMPACT, true>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
   }
 }
 
@@ -548,13 +577,15 @@ hipError_t launch_topk(const TopkPlan& p, const void* logits, bool bf16, int32_t
   const int64_t ntopk = p.rows * p.parts;
   const PackJob job = pack ? *pack : PackJob{nullptr, 0, nullptr, 0};
   const dim3 grid((unsigned)(ntopk + job.nslabs));
+  const bool wide = ntopk <= kWideSeedMaxBlocks;
+#define DFS_TK(LB, WS) \
+  topk_chunk_kernel<LB, WS><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial, out_idx, out_val, ntopk, job, zero)
   if (bf16) {
-    topk_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk, partial,
-                                                           out_idx, out_val, ntopk, job, zero);
+    if (wide) DFS_TK(true, true); else DFS_TK(true, false);
   } else {
-    topk_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(logits, p.V, p.parts, p.chunk,
-                                                            partial, out_idx, out_val, ntopk, job, zero);
+    if (wide) DFS_TK(false, true); else DFS_TK(false, false);
   }
+#undef DFS_TK
   if (p.parts > 1 && merge) {
     topk_merge_kernel<<<dim3((unsigned)p.rows), kThreads, 0, stream>>>(partial, p.parts, out_idx,
                                                                         out_val);
