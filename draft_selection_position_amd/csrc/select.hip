@@ -165,16 +165,34 @@ __device__ __forceinline__ void viterbi_walk(const float (*sS)[kK][kK], int32_t 
   }
 }
 
-__device__ __forceinline__ void chase(WalkTables& w, int64_t b, int L,
+// The chain, run by one whole wave: lanes 0..15 hold the successor column of their
+// slot for every position (independent LDS reads), and each step picks the next slot
+// with a lane read indexed by the current one, so the L dependent steps cost a few
+// cycles each instead of an LDS round trip.  Lane t keeps position t's slot and
+// predecessor slot and writes that position's outputs.
+__device__ __forceinline__ void chase(WalkTables& w, int64_t b, int L, int lane,
                                       int32_t* __restrict__ out_path,
                                       float* __restrict__ out_scores) {
-  int a = 0;
-  for (int t = 0; t < L; ++t) {
-    const int j = w.next[t][a];
-    w.slot[t] = j;
-    out_path[b * L + t] = w.cand[t][j];
-    out_scores[b * L + t] = w.best[t][a];
-    a = j;
+  const int l = lane & (kK - 1);
+  int nx[kMaxL];
+#pragma unroll
+  for (int t = 0; t < kMaxL; ++t) nx[t] = t < L ? w.next[t][l] : 0;
+  int a = 0, slot = 0, pred = 0;
+#pragma unroll
+  for (int t = 0; t < kMaxL; ++t) {
+    if (t < L) {
+      const int j = __builtin_amdgcn_readlane(nx[t], a);
+      if (lane == t) {
+        pred = a;
+        slot = j;
+      }
+      a = j;
+    }
+  }
+  if (lane < L) {
+    w.slot[lane] = slot;
+    out_path[b * L + lane] = w.cand[lane][slot];
+    out_scores[b * L + lane] = w.best[lane][pred];
   }
 }
 
@@ -402,7 +420,7 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
     } else {
       successors(sc, t, lane, mode, temperature, seed, b, sW);
       __syncthreads();
-      if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+      if (t == 0) chase(sW, b, L, lane, out_path, out_scores);
     }
     if (out_q != nullptr) {
       __syncthreads();
@@ -414,13 +432,14 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
 // ---------------------------------------------------------------- few rows
 // With few rows one workgroup per sequence would pull every position's gate partial sums
 // and table rows through a single CU; instead each (sequence, position) gets a workgroup
-// of two waves: wave 0 merges position t's split top-16 lists, wave 1 position t - 1's
-// (the predecessors), wave 0 then scores the tile and computes its successor table
-// exactly as pair_walk_kernel does, and leaves them in `tiles`.  The last workgroup of a
-// sequence to finish (an agent-scope release before an atomic count, acquire after it;
-// the count wraps back to zero, and the launch before this one zeroes it as well) reads
-// all L positions back and walks them with the same code.
-constexpr int kPosThreads = 2 * kWave;
+// of eight waves: waves 0-3 merge position t's split top-16 lists, waves 4-7 position
+// t - 1's (the predecessors), four lists per wave and then the four waves' lists, each
+// a merge of four sorted runs; wave 0 then scores the tile and computes its successor
+// table exactly as pair_walk_kernel does, and leaves them in `tiles`.  The last
+// workgroup of a sequence to finish (an agent-scope release before an atomic count,
+// acquire after it; the count wraps back to zero, and the launch before this one zeroes
+// it as well) reads all L positions back and walks them with the same code.
+constexpr int kPosThreads = 8 * kWave;
 
 template <bool kBf16Tables>
 __global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
@@ -432,7 +451,7 @@ __global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
     int32_t* __restrict__ out_cand, PosTile* __restrict__ tiles, uint32_t* __restrict__ counters) {
   __shared__ int32_t sC[2][kK];  // [0]: position t - 1, [1]: position t
   __shared__ float sU[2][kK];
-  __shared__ uint64_t sMerge[2][kMergeScratch];
+  __shared__ uint64_t sLists[2][4 * kK];  // the four waves' lists of each row
   __shared__ __attribute__((aligned(16))) float sG[kE];
   __shared__ WalkTables sW;
   __shared__ float sS[kMaxL][kK][kK];
@@ -457,19 +476,23 @@ __global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
       gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
     }
   } else {
-    const bool live = wave == 0 || t > 0;  // wave-uniform
-    MergeRegs mr;
-    if (live) merge_load(partial + (row - wave) * parts * kK, parts, lane, mr);
+    const int group = wave / 4, w4 = wave % 4;  // group 0: position t, 1: position t - 1
+    const bool live = group == 0 || t > 0;       // wave-uniform
+    Merge4Regs mr;
+    if (live) merge4_load(partial + (row - group) * parts * kK, parts, w4, lane, mr);
     int32_t prev = 0;
     if (wave == 0) {
       prev = prev_token[b];
       gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
     }
-    if (live) {
-      const uint64_t key = merge_keys(mr, parts, lane, sMerge[wave]);
+    const uint64_t list = live ? merge4_wave(mr, parts, w4, lane) : 0;
+    if (lane < kK) sLists[group][w4 * kK + lane] = list;
+    __syncthreads();
+    if (live && w4 == 0) {
+      const uint64_t key = wave_merge_runs16(sLists[group][lane], lane);
       if (lane < kK) {
-        sC[1 - wave][lane] = (int32_t)key_index(key);
-        sU[1 - wave][lane] = key_value(key);
+        sC[1 - group][lane] = (int32_t)key_index(key);
+        sU[1 - group][lane] = key_value(key);
       }
     }
     __syncthreads();
@@ -527,8 +550,8 @@ __global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
   __syncthreads();
   if (mode == 2) {
     if (wave == 0) viterbi_walk(sS, sW.next, sW.cand, sW.slot, b, L, lane, out_path, out_scores);
-  } else if (threadIdx.x == 0) {
-    chase(sW, b, L, out_path, out_scores);
+  } else if (wave == 0) {
+    chase(sW, b, L, lane, out_path, out_scores);
   }
   if (out_q != nullptr) {
     __syncthreads();
@@ -565,7 +588,7 @@ __global__ __launch_bounds__(kWave * kMaxL) void walk_kernel(const float* __rest
   } else {
     successors(sc, t, lane, mode, temperature, seed, b, sW);
     __syncthreads();
-    if (threadIdx.x == 0) chase(sW, b, L, out_path, out_scores);
+    if (t == 0) chase(sW, b, L, lane, out_path, out_scores);
   }
 }
 

@@ -133,4 +133,41 @@ __device__ __forceinline__ uint64_t merge_keys(MergeRegs& m, int parts, int lane
   return list;
 }
 
+// ---------------------------------------------------------------- four waves, one row
+// Four waves (w4 = 0..3) of a workgroup share one row's `parts` (1..64) sorted lists:
+// in round 0 wave w4 takes lists 4 w4 .. 4 w4 + 3 as its four 16-lane runs, in round
+// k >= 1 its running list (lanes 0..15) and lists 16 + 12 (k - 1) + 3 w4 .. + 2; each
+// round is one merge of four sorted runs.  merge4_load issues every load up front;
+// merge4_wave leaves the wave's top 16 in lanes 0..15 (the others 0), and a merge of
+// the four waves' lists gives the row's.  Up to 16 lists this is one merge per wave.
+constexpr int kMerge4Rounds = 1 + (kMaxMergeParts - 16 + 11) / 12;
+struct Merge4Regs {
+  uint64_t x[kMerge4Rounds];
+};
+
+__device__ __forceinline__ void merge4_load(const uint64_t* __restrict__ src, int parts, int w4, int lane,
+                                            Merge4Regs& m) {
+  const int j = lane & (kK - 1);
+  const int p0 = 4 * w4 + (lane >> 4);
+  m.x[0] = p0 < parts ? src[(int64_t)p0 * kK + j] : 0;
+#pragma unroll
+  for (int k = 1; k < kMerge4Rounds; ++k) {
+    const int p = 16 + 12 * (k - 1) + 3 * w4 + (lane >> 4) - 1;
+    m.x[k] = (lane >= kK && p < parts) ? src[(int64_t)p * kK + j] : 0;
+  }
+}
+
+__device__ __forceinline__ uint64_t merge4_wave(const Merge4Regs& m, int parts, int w4, int lane) {
+  uint64_t x = wave_merge_runs16(m.x[0], lane);
+  uint64_t list = lane < kK ? x : 0;
+#pragma unroll
+  for (int k = 1; k < kMerge4Rounds; ++k) {
+    if (16 + 12 * (k - 1) + 3 * w4 < parts) {  // wave-uniform: this wave has lists in round k
+      x = wave_merge_runs16(lane < kK ? list : m.x[k], lane);
+      list = lane < kK ? x : 0;
+    }
+  }
+  return list;
+}
+
 }  // namespace dfs
