@@ -91,10 +91,9 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
       const uint64_t y = shfl_xor_u64(x, j, lane);
       const bool lower = (lane & j) == 0;
       const bool desc = (lane & k) == 0;
-      const bool take_max = (lower == desc);
-      const uint64_t mx = x > y ? x : y;
-      const uint64_t mn = x > y ? y : x;
-      x = take_max ? mx : mn;
+      // the lane keeps the larger key where lower == desc, else the smaller: one
+      // compare and one select (equal keys are the same either way)
+      x = ((x > y) == (lower == desc)) ? x : y;
     }
   }
   return x;
@@ -115,10 +114,9 @@ __device__ __forceinline__ uint64_t wave_merge_runs16(uint64_t x, int lane) {
       const uint64_t y = shfl_xor_u64(x, j, lane);
       const bool lower = (lane & j) == 0;
       const bool desc = (lane & k) == 0;
-      const bool take_max = (lower == desc);
-      const uint64_t mx = x > y ? x : y;
-      const uint64_t mn = x > y ? y : x;
-      x = take_max ? mx : mn;
+      // the lane keeps the larger key where lower == desc, else the smaller: one
+      // compare and one select (equal keys are the same either way)
+      x = ((x > y) == (lower == desc)) ? x : y;
     }
   }
   return x;

@@ -7,8 +7,9 @@
 //
 // Design (gfx950): the pass is HBM-bound, so each workgroup (4 waves) streams a
 // row chunk with 16-byte coalesced non-temporal loads, the next iteration's
-// vectors in flight while the current ones are scanned.  An element is only looked at further when it reaches
-// the wave's admission threshold; admitted elements are appended to a per-wave
+// vectors in flight while the current ones are scanned.  An element is only looked at
+// further when it reaches the wave's admission threshold (which starts at a bound taken
+// over the wave's first iteration); admitted elements are appended to a per-wave
 // LDS buffer as exact 64-bit (value, index) keys with one ballot per element
 // slot, and the buffer is merged into the wave's sorted top-16 (held in lanes
 // 0..15) by a 64-lane bitonic sort.  The 16th best key of any wave is a valid
@@ -76,11 +77,12 @@ constexpr int kMinSmallChunk = 1024;  // the same for the few-row plan
 #ifndef DFS_TOPK_GATE_COMPACT
 #define DFS_TOPK_GATE_COMPACT true
 #endif
-// The pass seeds each workgroup's threshold from its waves' whole first iteration (one
-// barrier) when all its workgroups fit one round on the chip (256 CUs x 8 workgroups at
-// 8 waves per SIMD): then every workgroup starts at once and an early threshold saves
-// admissions (1024 rows x 262144: -1.8 us, 512 rows x 151936: -0.8 us); with two rounds
-// (4096 rows) the barrier costs more than it saves (+1.8 us).
+// Each wave's threshold starts from a bound taken over its whole first iteration.  When
+// all the pass's workgroups fit one round on the chip (256 CUs x 8 workgroups at 8 waves
+// per SIMD), a barrier then lets every wave start from the best bound of its workgroup:
+// every workgroup starts at once and the early threshold saves admissions (1024 rows x
+// 262144: -1.8 us, 512 rows x 151936: -0.8 us); with two rounds (4096 rows) the barrier
+// costs more than it saves (+1.8 us).
 constexpr int64_t kWideSeedMaxBlocks = 2048;
 // Few rows: workgroups the split aims for.
 #ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
@@ -106,9 +108,9 @@ struct WaveTop {
   int cnt;        // keys waiting in the buffer, identical in every lane
 };
 
-// Out-of-line copy of the 64-lane sort for the compact build of the pass (few rows),
-// where each wave runs the code about once per launch and every inlined copy would be
-// fetched cold: one copy, called from every merge and seed.
+// Out-of-line copy of the 64-lane sort for the compact build of the pass: merges are
+// rare next to the scan, so one copy called from every merge keeps the scan's code
+// small.
 __device__ __attribute__((noinline)) uint64_t wave_sort_desc_call(uint64_t x, int lane) {
   return wave_sort_desc(x, lane);
 }
@@ -200,13 +202,10 @@ __device__ __forceinline__ float vec_max(uint4 d, bool valid) {
 
 // Admission test and append for one 16-byte vector (8 bf16 or 4 fp32 values),
 // then a merge if the buffer has filled past kMergeAt.  A vector past the end of
-// the chunk (`valid` false) is replaced by NaNs, which never pass.  On a wave's
-// first vector (`seed`), the threshold is first raised to the 16th largest lane
-// maximum: those 16 maxima are distinct elements, so nothing below it can make
-// the top 16.
+// the chunk (`valid` false) is replaced by NaNs, which never pass.
 template <bool kBf16, bool kCompact>
 __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, WaveTop& w,
-                                         uint64_t* buf, uint32_t* s_thr, int lane, bool seed) {
+                                         uint64_t* buf, uint32_t* s_thr, int lane) {
   constexpr int PV = Elems<kBf16>::per_vec;
   if (!valid) d = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
   float v[PV];
@@ -223,13 +222,6 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
   float m = v[0];
 #pragma unroll
   for (int e = 1; e < PV; ++e) m = fmaxf(m, v[e]);
-  if (seed) {
-    const uint32_t k16 = wave_16th_largest(m == m ? mono32(m) : 0u);
-    if (k16 != 0u) {
-      const float t = unmono32(k16);
-      if (t > w.thr) w.thr = uniformf(t);
-    }
-  }
   if (__ballot(m >= w.thr) == 0) return;
 #pragma unroll
   for (int e = 0; e < PV; ++e) append(w, v[e] >= w.thr, v[e], idx0 + e, buf);
@@ -327,23 +319,28 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
       for (int u = 0; u < kU; ++u) {
         const int64_t vid = it * step + (int64_t)u * kThreads + tid;
         scan_vec<kBf16, kCompact>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
-                        &s_thr, lane, !kWide && it == 0 && u == 0);
+                        &s_thr, lane);
       }
     };
     constexpr std::false_type kInside{};
     constexpr std::true_type kEdge{};
     const int64_t nfull = nvec / step;  // iterations with every vector inside the chunk
     load_iter(bufA, 0);
-    if constexpr (kWide) {
-      // The 16th-largest lane maximum over a wave's first iteration bounds the chunk's top
-      // 16 (every lane maximum is a distinct element); the largest such bound over the
-      // waves is where every wave's threshold starts (scan_iter reads it back).
+    {
+      // The 16th-largest lane maximum over the wave's first iteration bounds the chunk's
+      // top 16 (every lane maximum is a distinct element): the wave's threshold starts
+      // there, and the largest such bound of the four waves is shared through LDS (with
+      // a barrier when every wave should start from it, see kWideSeedMaxBlocks).
       float m = __int_as_float(0x7fffffff);
 #pragma unroll
       for (int u = 0; u < kU; ++u) m = fmaxf(m, vec_max<kBf16>(bufA[u], (int64_t)u * kThreads + tid < nvec));
       const uint32_t k16 = wave_16th_largest(m == m ? mono32(m) : 0u);
-      if (k16 != 0u && lane == 0) atomicMax(&s_thr, k16);
-      __syncthreads();
+      if (k16 != 0u) {
+        const float t = unmono32(k16);
+        if (t > w.thr) w.thr = uniformf(t);
+        if (lane == 0) atomicMax(&s_thr, k16);
+      }
+      if constexpr (kWide) __syncthreads();
     }
     int64_t it = 0;
     // bufA holds iteration `it` at the top of each loop; no exit in the middle of an
@@ -461,7 +458,7 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
 #pragma unroll
   for (int u = 0; u < kSmallVecs; ++u) {
     const int64_t vid = (int64_t)u * kThreads + tid;
-    scan_vec<kBf16, true>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, &lds.thr, lane, false);
+    scan_vec<kBf16, true>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, &lds.thr, lane);
   }
   if (w.cnt > 0) wave_merge<true>(w, buf, &lds.thr, lane);
   if (lane < kK) lds.list[wave * kK + lane] = w.list;
