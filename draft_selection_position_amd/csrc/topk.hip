@@ -84,6 +84,11 @@ constexpr int kMinSmallChunk = 1024;  // the same for the few-row plan
 // 262144: -1.8 us, 512 rows x 151936: -0.8 us); with two rounds (4096 rows) the barrier
 // costs more than it saves (+1.8 us).
 constexpr int64_t kWideSeedMaxBlocks = 2048;
+// Launches of more than one round also raise the shared threshold to the bound over all
+// four waves' lists at every merge (wave_merge): fewer admissions where the VALU is busy.
+#ifndef DFS_TOPK_UNION
+#define DFS_TOPK_UNION 1
+#endif
 // Few rows: workgroups the split aims for.
 #ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
 #define DFS_TOPK_SMALL_TARGET_BLOCKS 64
@@ -123,9 +128,26 @@ __device__ __forceinline__ uint64_t sort_desc(uint64_t x, int lane) {
   }
 }
 
+// The workgroup's shared words: s_thr[0] is the chunk's admission threshold key (0: none
+// yet), s_thr[1 + 16 w + j] the value key of slot j of wave w's list as of its last merge.
+// A slot's value never falls (each merge keeps the top 16 of a larger set), so from any
+// mix of old and new words wave w holds at least j + 1 elements at or above word j; the
+// waves see disjoint elements, so the 16th largest of the 64 words has 16 distinct
+// elements of the chunk at or above it, whatever the other waves are doing meanwhile.
+constexpr int kThrWords = 1 + kWaves * kK;
+
+// That 16th largest word (lane l reads word 1 + l): one out-of-line copy, as merges are
+// rare and the search is long.
+__device__ __attribute__((noinline)) uint32_t union_bound(uint32_t* s_thr, int lane) {
+  return wave_16th_largest(
+      __hip_atomic_load(&s_thr[1 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+
 // Merge the buffered keys into the wave's list and raise the threshold (kCompact: the
-// out-of-line sort).
-template <bool kCompact>
+// out-of-line sort; kUnion: also publish the list's values and raise the threshold to the
+// bound over all four waves' lists, which pays where the pass is short of issue slots,
+// with eight waves per SIMD, and not where a wave's merges are on its own critical path).
+template <bool kCompact, bool kUnion>
 __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint32_t* s_thr,
                                            int lane) {
   __builtin_amdgcn_wave_barrier();
@@ -145,8 +167,14 @@ __device__ __forceinline__ void wave_merge(WaveTop& w, const uint64_t* buf, uint
   w.cnt = 0;
   __builtin_amdgcn_wave_barrier();
   const uint64_t k16 = lane_u64(w.list, 15);
-  if (k16 != 0) {
-    uint32_t m = (uint32_t)(k16 >> 32);
+  uint32_t bound = (uint32_t)(k16 >> 32);
+  if constexpr (kUnion) {
+    if (lane < kK) s_thr[1 + (threadIdx.x / kWave) * kK + lane] = (uint32_t)(w.list >> 32);
+    const uint32_t u = (uint32_t)uniform((int)union_bound(s_thr, lane));
+    bound = u > bound ? u : bound;
+  }
+  if (bound != 0) {
+    uint32_t m = bound;
     uint32_t old = 0;
     if (lane == 0) old = atomicMax(s_thr, m);
     old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
@@ -203,7 +231,7 @@ __device__ __forceinline__ float vec_max(uint4 d, bool valid) {
 // Admission test and append for one 16-byte vector (8 bf16 or 4 fp32 values),
 // then a merge if the buffer has filled past kMergeAt.  A vector past the end of
 // the chunk (`valid` false) is replaced by NaNs, which never pass.
-template <bool kBf16, bool kCompact>
+template <bool kBf16, bool kCompact, bool kUnion>
 __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, WaveTop& w,
                                          uint64_t* buf, uint32_t* s_thr, int lane) {
   constexpr int PV = Elems<kBf16>::per_vec;
@@ -225,13 +253,13 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
   if (__ballot(m >= w.thr) == 0) return;
 #pragma unroll
   for (int e = 0; e < PV; ++e) append(w, v[e] >= w.thr, v[e], idx0 + e, buf);
-  if (w.cnt > kMergeAt) wave_merge<kCompact>(w, buf, s_thr, lane);
+  if (w.cnt > kMergeAt) wave_merge<kCompact, kUnion>(w, buf, s_thr, lane);
 }
 
 struct TopkLds {
   uint64_t buf[kWaves][kCap];  // per-wave key buffers
   uint64_t list[kWaves * kK];
-  uint32_t thr;
+  uint32_t thr[kThrWords];     // the chunk's threshold and the waves' published list values
 };
 static_assert(sizeof(TopkLds::buf) >= kPackLdsBytes, "a packing job reuses the key buffers");
 static_assert(sizeof(TopkLds::buf) >= gtile::kF32LdsBytes, "a gate job reuses the key buffers");
@@ -239,7 +267,7 @@ static_assert(sizeof(TopkLds::buf) >= gtile::kF32LdsBytes, "a gate job reuses th
 // One (row, part) of the pass: workgroup `bid` of the rows.  kCompact: the sorts are
 // out-of-line calls (few rows: each wave runs the code about once).  kU: 16-byte vectors
 // per thread per iteration (two iterations in flight).
-template <bool kBf16, bool kCompact, bool kWide, int kU = kUnroll>
+template <bool kBf16, bool kCompact, bool kWide, bool kUnion, int kU = kUnroll>
 __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64_t V, int parts, int64_t chunk,
                                           uint64_t* __restrict__ partial, int32_t* __restrict__ out_idx,
                                           float* __restrict__ out_val, int64_t bid, TopkLds& lds) {
@@ -247,7 +275,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
   constexpr int PV = Elems<kBf16>::per_vec;
   auto& s_buf = lds.buf;
   auto& s_list = lds.list;
-  auto& s_thr = lds.thr;
+  uint32_t* s_thr = lds.thr;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -257,7 +285,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
   const int64_t beg = (int64_t)part * chunk;
   const int64_t end = beg + chunk < V ? beg + chunk : V;
 
-  if (tid == 0) s_thr = 0u;
+  if (tid < kThrWords) s_thr[tid] = 0u;
   __syncthreads();
 
   uint64_t* buf = s_buf[wave];
@@ -309,7 +337,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
     auto scan_iter = [&](const uint4* src, int64_t it, auto kCheck) {
       {  // other waves may have raised the chunk's threshold
         const uint32_t m = uniform(
-            (int)__hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            (int)__hip_atomic_load(s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (m != 0u) {
           const float t = unmono32(m);
           if (t > w.thr) w.thr = uniformf(t);
@@ -318,8 +346,8 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t vid = it * step + (int64_t)u * kThreads + tid;
-        scan_vec<kBf16, kCompact>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV), w, buf,
-                        &s_thr, lane);
+        scan_vec<kBf16, kCompact, kUnion>(src[u], !decltype(kCheck)::value || vid < nvec, (uint32_t)(vb + vid * PV),
+                                          w, buf, s_thr, lane);
       }
     };
     constexpr std::false_type kInside{};
@@ -338,7 +366,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
       if (k16 != 0u) {
         const float t = unmono32(k16);
         if (t > w.thr) w.thr = uniformf(t);
-        if (lane == 0) atomicMax(&s_thr, k16);
+        if (lane == 0) atomicMax(s_thr, k16);
       }
       if constexpr (kWide) __syncthreads();
     }
@@ -360,7 +388,7 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
     if (it < niter) scan_iter(bufA, it, kEdge);  // odd count: bufA holds the last iteration
   }
 
-  if (w.cnt > 0) wave_merge<kCompact>(w, buf, &s_thr, lane);
+  if (w.cnt > 0) wave_merge<kCompact, false>(w, buf, s_thr, lane);
   if (lane < kK) s_list[wave * kK + lane] = w.list;
   __syncthreads();
   if (wave == 0) {
@@ -407,7 +435,7 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
   if (vb > end) vb = end;
   const int64_t nvec = (end - vb) / PV;
   const int64_t ve = vb + nvec * PV;
-  if (tid == 0) lds.thr = 0u;
+  if (tid == 0) lds.thr[0] = 0u;
 
   uint4 d[kSmallVecs];
   if (nvec > 0) {
@@ -442,25 +470,25 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
                          fmaxf(__uint_as_float(d[u].z), __uint_as_float(d[u].w))));
     }
   }
-  __syncthreads();  // lds.thr cleared
+  __syncthreads();  // threshold cleared
   {
     const uint32_t k16 = wave_16th_largest(m == m ? mono32(m) : 0u);
-    if (k16 != 0u && lane == 0) atomicMax(&lds.thr, k16);
+    if (k16 != 0u && lane == 0) atomicMax(lds.thr, k16);
   }
   __syncthreads();
   uint64_t* buf = lds.buf[wave];
   WaveTop w;
   w.list = 0;
   w.cnt = 0;
-  const uint32_t t0 = lds.thr;
+  const uint32_t t0 = lds.thr[0];
   w.thr = t0 != 0u ? unmono32(t0) : -INFINITY;
   append(w, hi >= 0 && hv >= w.thr, hv, (uint32_t)hi, buf);  // at most 14 keys
 #pragma unroll
   for (int u = 0; u < kSmallVecs; ++u) {
     const int64_t vid = (int64_t)u * kThreads + tid;
-    scan_vec<kBf16, true>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, &lds.thr, lane);
+    scan_vec<kBf16, true, false>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, lds.thr, lane);
   }
-  if (w.cnt > 0) wave_merge<true>(w, buf, &lds.thr, lane);
+  if (w.cnt > 0) wave_merge<true, false>(w, buf, lds.thr, lane);
   if (lane < kK) lds.list[wave * kK + lane] = w.list;
   __syncthreads();
   if (wave == 0) {
@@ -491,7 +519,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DFS_TO
     pack_w_slab(pack.W, pack.d, pack.Wp, job, threadIdx.x, reinterpret_cast<uint16_t(*)[kPackPitch]>(&lds.buf[0][0]));
     return;
   }
-  topk_body<kBf16, DFS_TOPK_CHUNK_COMPACT, kWide>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+  topk_body<kBf16, DFS_TOPK_CHUNK_COMPACT, kWide, !kWide && DFS_TOPK_UNION>(logits, V, parts, chunk, partial, out_idx,
+                                                                          out_val, bid, lds);
 }
 
 // The pass with the gate's jobs as the first workgroups of the launch, for up to 512
@@ -516,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void topk_gate_kernel(const void* __restr
   if (chunk <= (int64_t)kSmallVecs * kThreads * Elems<kBf16>::per_vec) {
     topk_small_body<kBf16>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
   } else {
-    topk_body<kBf16, DFS_TOPK_GATE_COMPACT, true>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
+    topk_body<kBf16, DFS_TOPK_GATE_COMPACT, true, false>(logits, V, parts, chunk, partial, out_idx, out_val, bid, lds);
   }
 }
 
