@@ -103,6 +103,35 @@ def test_topk_adversarial_rows(dtype):
     _check_rows(rows, dtype, idx, val, range(rows.shape[0]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_adversarial_rows_two_rounds(dtype):
+    """More rows than one round of workgroups holds (2304 > 2048 workgroups): there the pass
+    raises its shared threshold from all four waves' published list values at every merge.
+    Rows that admit every element, rows of ties at one or a few levels, signed zeros, -inf,
+    and unaligned rows (V = 6001)."""
+    V = 6001
+    rng = np.random.default_rng(5)
+    base = [
+        np.arange(V, dtype=np.float32),  # ascending: every element beats the running threshold
+        np.arange(V, dtype=np.float32)[::-1].copy(),
+        rng.permutation(V).astype(np.float32),
+        np.zeros(V, np.float32),  # all tied: ids 0..15
+        rng.choice(np.array([0.0, -0.0, 1.0], np.float32), V),
+        np.full(V, -np.inf, np.float32),
+        np.where(rng.random(V) < 0.5, np.float32(-np.inf), np.float32(2.5)),
+        np.round(rng.standard_normal(V) * 2).astype(np.float32),  # a few levels, heavy ties
+        rng.standard_normal(V).astype(np.float32),
+    ]
+    rows = np.stack([base[i % len(base)] for i in range(2304)])
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+
+        rows = f32_to_bf16_bits(rows)
+    print(f"topk adversarial rows 2304 x {V} {dtype}", flush=True)
+    idx, val = _run(rows, dtype)
+    _check_rows(rows, dtype, idx, val, range(rows.shape[0]))
+
+
 def test_topk_repeatable():
     cfg = variant("small_batch", d=64, batch=8)
     x = to_dev(make(cfg).logits.reshape(-1, cfg.V))
