@@ -414,6 +414,9 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
 #ifndef DFS_TOPK_SMALL_VECS
 #define DFS_TOPK_SMALL_VECS 6
 #endif
+#ifndef DFS_TOPK_SMALL_BATCHED
+#define DFS_TOPK_SMALL_BATCHED 1
+#endif
 constexpr int kSmallVecs = DFS_TOPK_SMALL_VECS;
 
 template <bool kBf16>
@@ -483,10 +486,57 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
   const uint32_t t0 = lds.thr[0];
   w.thr = t0 != 0u ? unmono32(t0) : -INFINITY;
   append(w, hi >= 0 && hv >= w.thr, hv, (uint32_t)hi, buf);  // at most 14 keys
+  // Every element of the lane's vectors at or above the threshold goes to the buffer in one
+  // pass: a lane's count is summed over the lanes below it with one ballot per count bit,
+  // which places its keys (vectors past the chunk hold NaNs and never pass).  Inputs that
+  // pass more keys than the buffer holds take the vector-by-vector scan instead.
+  bool scanned = false;
+#if DFS_TOPK_SMALL_BATCHED
+  {
+    auto elem = [&](int u, int e) -> float {
+      if constexpr (kBf16) {
+        const uint32_t word = (e >> 1) == 0 ? d[u].x : (e >> 1) == 1 ? d[u].y : (e >> 1) == 2 ? d[u].z : d[u].w;
+        return (e & 1) ? bf16_hi(word) : bf16_lo(word);
+      } else {
+        return __uint_as_float(e == 0 ? d[u].x : e == 1 ? d[u].y : e == 2 ? d[u].z : d[u].w);
+      }
+    };
+    uint32_t bits[kSmallVecs];
+    int c = 0;
 #pragma unroll
-  for (int u = 0; u < kSmallVecs; ++u) {
-    const int64_t vid = (int64_t)u * kThreads + tid;
-    scan_vec<kBf16, true, false>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, lds.thr, lane);
+    for (int u = 0; u < kSmallVecs; ++u) {
+      bits[u] = 0;
+#pragma unroll
+      for (int e = 0; e < PV; ++e) bits[u] |= (elem(u, e) >= w.thr ? 1u : 0u) << e;
+      c += __popc(bits[u]);
+    }
+    int pos = w.cnt, tot = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) <= kSmallVecs * PV; ++b) {
+      const uint64_t mb = __ballot((c >> b) & 1);
+      pos += lanes_below(mb) << b;
+      tot += __popcll(mb) << b;
+    }
+    if (w.cnt + tot <= kCap) {
+#pragma unroll
+      for (int u = 0; u < kSmallVecs; ++u) {
+        if (__ballot(bits[u] != 0u) == 0) continue;
+        const uint32_t base = (uint32_t)(vb + ((int64_t)u * kThreads + tid) * PV);
+#pragma unroll
+        for (int e = 0; e < PV; ++e)
+          if ((bits[u] >> e) & 1u) buf[pos++] = make_key(elem(u, e), base + (uint32_t)e);
+      }
+      w.cnt = uniform(w.cnt + tot);
+      scanned = true;
+    }
+  }
+#endif
+  if (!scanned) {
+#pragma unroll
+    for (int u = 0; u < kSmallVecs; ++u) {
+      const int64_t vid = (int64_t)u * kThreads + tid;
+      scan_vec<kBf16, true, false>(d[u], vid < nvec, (uint32_t)(vb + vid * PV), w, buf, lds.thr, lane);
+    }
   }
   if (w.cnt > 0) wave_merge<true, false>(w, buf, lds.thr, lane);
   if (lane < kK) lds.list[wave * kK + lane] = w.list;

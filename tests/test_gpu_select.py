@@ -219,3 +219,40 @@ def test_select_ragged_rows_each_gate_split(batch, d, splits):
     assert np.array_equal(scores, s2.cpu().numpy())
     seqs = np.unique(np.r_[0, cfg.batch - 1, np.random.default_rng(6).choice(cfg.batch, 8, replace=False)])
     _check(inp, path, scores, seqs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_few_rows_adversarial_logits(dtype):
+    """One sequence of 16 x 151936 (the fused launch whose chunks are held in registers):
+    rows where every element reaches the threshold (all equal: more keys than a wave's
+    buffer holds), ascending and descending rows, signed zeros, -inf and a few tied
+    levels.  The drafted candidates equal the oracle's top-16 of every row."""
+    import draft_selection_position_amd as dfs
+    from workloads import f32_to_bf16_bits
+
+    from .parity import to_dev
+
+    cfg = variant("single_stream", emb_std=0.3, dtype=dtype, d=256)
+    V = cfg.V
+    rng = np.random.default_rng(11)
+    patterns = [
+        np.zeros(V, np.float32),
+        np.arange(V, dtype=np.float32),
+        np.arange(V, dtype=np.float32)[::-1].copy(),
+        rng.choice(np.array([0.0, -0.0, 1.0], np.float32), V),
+        np.where(rng.random(V) < 0.5, np.float32(-np.inf), np.float32(2.5)),
+        np.round(rng.standard_normal(V)).astype(np.float32),
+    ]
+    rows = np.stack([patterns[i % len(patterns)] for i in range(cfg.L)])
+    if dtype == "bf16":
+        rows = f32_to_bf16_bits(rows)
+    dev = upload(make(cfg))
+    dev["logits"] = to_dev(rows.reshape(1, cfg.L, V))
+    W = dfs.gate_pack(dev["W_h"]) if dtype == "bf16" else dev["W_h"]
+    print(f"select few rows adversarial {dtype}", flush=True)
+    _, _, _, cand = dfs.select(dev["logits"], dev["hidden"], dev["prev_token"], dev["A"], dev["B"], W, draft=True)
+    torch.cuda.synchronize()
+    cand = cand.cpu().numpy().reshape(cfg.L, 16)
+    for r in range(cfg.L):
+        oi, _ = oracle.top16(oracle.widen(rows[r], dtype))
+        np.testing.assert_array_equal(cand[r], oi, err_msg=f"row {r}")
