@@ -366,12 +366,16 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   GateRegs gr;
   if (parts <= 1) {
     // The candidates are final lists (cand_idx / cand_val).  The gate row does not
-    // depend on them: its loads go out with the id loads (a pointer select, not a
+    // depend on them: its loads go out right after the id loads (a pointer select, not a
     // branch: no load has to wait for another).
     const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
     pred_id = *pred_p;
     cand_id = cand_idx[row * kK + r];
     u = cand_val[row * kK + r];
+    // Every wave's id loads go out before any wave's gate loads: the ids gate the table
+    // gathers, and behind the workgroup's 64 KB of gate partial sums the last wave's ids
+    // took 3.5 us to arrive (a bare barrier: it orders the issue, it waits for no load).
+    __builtin_amdgcn_s_barrier();
     gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
   } else {
     // The top-16 pass left `parts` sorted partial lists per row: each wave merges its
