@@ -11,12 +11,14 @@
 // further when it reaches the wave's admission threshold (which starts at a bound taken
 // over the wave's first iteration); admitted elements are appended to a per-wave
 // LDS buffer as exact 64-bit (value, index) keys with one ballot per element
-// slot, and the buffer is merged into the wave's sorted top-16 (held in lanes
-// 0..15) by a 64-lane bitonic sort.  The 16th best key of any wave is a valid
-// threshold for the whole chunk and is shared through LDS.  The four wave lists
-// are merged at the end; rows split over several workgroups are merged by a
-// second kernel.  Every comparison is on exact integer keys, so the result does
-// not depend on the order in which elements are seen.
+// slot (chunks held whole in registers: one prefix count for all of a lane's elements),
+// and the buffer is merged into the wave's sorted top-16 (held in lanes 0..15) by a
+// 64-lane bitonic sort.  The 16th best key of any wave is a valid threshold for the
+// whole chunk and is shared through LDS (in launches of two rounds, the bound over all
+// four waves' lists).  The four wave lists are merged at the end; rows split over
+// several workgroups are merged by a second kernel or by the kernel that reads them.
+// Every comparison is on exact integer keys, so the result does not depend on the order
+// in which elements are seen.
 #include <type_traits>
 
 #include "dfs_device.h"
