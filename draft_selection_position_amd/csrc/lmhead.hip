@@ -12,10 +12,12 @@
 // The same product can be written out (lmhead_logits*_kernel): the fused result
 // equals the top-16 pass run on those logits, bit for bit.
 //
-// Tiles (LDS-DMA mainloop of mfma_big.h): 128 x 128 (four waves of 64 x 64, two
-// workgroups per CU, a double buffer of 64 k per step: whole 128-byte lines) below
-// 2048 rows, 256 x 256 (four waves of 128 x 128, one per CU, a four-stage ring of
-// 32 k per step: a double buffer of 64 k leaves too little in flight) from there.
+// Tiles (LDS-DMA mainloop of mfma_big.h): the fused kernel uses 128 x 128 (four waves of
+// 64 x 64, two workgroups per CU, a double buffer of 64 k per step: whole 128-byte lines)
+// at every size, so that one workgroup's fold overlaps the other's products; the
+// written-out product switches to 256 x 256 (four waves of 128 x 128, one per CU, a
+// four-stage ring of 32 k per step: a double buffer of 64 k leaves too little in flight)
+// from 2048 rows.
 // For at most 32 rows the product (16-row register-staged tiles, mfma_tile.h, runs of
 // column tiles per workgroup: the pass streams W_lm and the matrix cores idle) is
 // written to the workspace and the top-16 pass runs over it, which is faster there.
@@ -101,9 +103,15 @@ constexpr int kMergeAt = 32;
 // wave row % 4 and lanes 0-15, so that each list slot is read back by the lane that
 // wrote it.  A stale threshold only lets more candidates through; every value that
 // can be in the top-16 is offered.
+//
+// 128 x 128 tiles (whose registers allow it) test a row's values against its threshold
+// as floats first, a wave at a time (keys above the threshold have values at or above
+// its value), and on a stripe's first tile raise each row's threshold to the smallest of
+// its 16 lanes' largest values (16 distinct elements of the row are at or above it), so
+// that the first tile offers tens of candidates per row instead of all of them.
 template <int TM, int TN, int WNW, class CandRow>
 __device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int tile_rows, int64_t n0,
-                                          int64_t ncols, bool last, uint64_t* s_thr, int* s_cnt,
+                                          int64_t ncols, bool first, bool last, uint64_t* s_thr, int* s_cnt,
                                           int* s_has, CandRow cand_row, uint64_t* plist, int64_t m0,
                                           int64_t row_stride) {
   const int tid = threadIdx.x;
@@ -115,14 +123,42 @@ __device__ __forceinline__ void fold_tile(const tile::f32x4 (&v)[TM][TN], int ti
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int lr = 16 * TM * wm + 16 * a + 4 * q + i;
-      if (lr >= tile_rows) continue;
-      const uint64_t thr = s_thr[lr];
+      if constexpr (TM * TN <= 16) {
+        // row lr is held by the 16 lanes of one DPP row (r = 0..15), TN values each
+        const bool row_ok = lr < tile_rows;
+        uint64_t thr = row_ok ? s_thr[lr] : ~0ull;
+        float m = -INFINITY;  // this lane's largest value of the row (NaN never counts)
 #pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int lc = 16 * TN * wn + 16 * b + r;
-        if (lc >= ncols) continue;
-        const uint64_t key = make_key(v[a][b][i], (uint32_t)(n0 + lc));
-        if (key > thr) cand_row(lr)[atomicAdd(&s_cnt[lr], 1)] = key;
+        for (int b = 0; b < TN; ++b)
+          if (16 * TN * wn + 16 * b + r < ncols) m = fmaxf(m, v[a][b][i]);
+        if (first) {
+          float bm = m;
+#pragma unroll
+          for (int j = 1; j < 16; j <<= 1) bm = fminf(bm, __uint_as_float(xor_lanes(__float_as_uint(bm), j, lane)));
+          const uint64_t bkey = (uint64_t)mono32(bm) << 32;  // below every key of value bm
+          thr = bkey > thr ? bkey : thr;
+        }
+        const float thrf = thr == 0 ? -INFINITY : unmono32((uint32_t)(thr >> 32));
+        if (__ballot(row_ok && m >= thrf) == 0) continue;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int lc = 16 * TN * wn + 16 * b + r;
+          const float x = v[a][b][i];
+          if (row_ok && lc < ncols && x >= thrf) {
+            const uint64_t key = make_key(x, (uint32_t)(n0 + lc));
+            if (key > thr) cand_row(lr)[atomicAdd(&s_cnt[lr], 1)] = key;
+          }
+        }
+      } else {
+        if (lr >= tile_rows) continue;
+        const uint64_t thr = s_thr[lr];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int lc = 16 * TN * wn + 16 * b + r;
+          if (lc >= ncols) continue;
+          const uint64_t key = make_key(v[a][b][i], (uint32_t)(n0 + lc));
+          if (key > thr) cand_row(lr)[atomicAdd(&s_cnt[lr], 1)] = key;
+        }
       }
     }
     // a row block at a time: keeps the scheduler from hoisting every key of the
@@ -201,7 +237,7 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_topk_dma_kernel(const
     typename C::Acc acc;
     C::zero(acc);
     big::mma<C>(ra, big::rows_operand(W + n0 * g.d, ncols, g.d, C::KK), 0, KS, lds, acc);
-    fold_tile<TM, TN, 2>(acc.v, tile_rows, n0, ncols, nt_ + 1 == t1, s_thr, s_cnt, s_has, cand_row, plist,
+    fold_tile<TM, TN, 2>(acc.v, tile_rows, n0, ncols, nt_ == t0, nt_ + 1 == t1, s_thr, s_cnt, s_has, cand_row, plist,
                          m0, row_stride);
   }
 }
@@ -283,21 +319,32 @@ __global__ __launch_bounds__(kThreads, kMinWG) void lmhead_logits_dma_kernel(con
     }
 }
 
-// Tile shapes: few rows -> 16 x 256 (W_lm streamed once); below DFS_LM_BIG_ROWS ->
-// 128 x 128; from there 256 x 256 (one workgroup per CU; measured faster from 4096
-// rows, slower at 1024).
+// Tile shapes of the written-out product: few rows -> 16 x 256 (W_lm streamed once);
+// below DFS_LM_BIG_ROWS -> 128 x 128; from there 256 x 256 (one workgroup per CU;
+// measured faster from 4096 rows, slower at 1024).  The fused kernel keeps 128 x 128
+// tiles at every size (below DFS_LM_FUSED_BIG_ROWS): with two workgroups per CU one
+// folds its tile while the other keeps the matrix cores busy, where a lone 256 x 256
+// workgroup stalls them for its whole fold (4096 x 151936 x 5120: 7.55-7.67 ms against
+// 7.99 ms).
 constexpr int64_t kSmallRows = 32;
 enum TileKind { kSmallTile = 0, kMidTile = 1, kBigTile = 2 };
 TileKind tile_kind(int64_t rows) {
   return rows <= kSmallRows ? kSmallTile : rows < DFS_LM_BIG_ROWS ? kMidTile : kBigTile;
 }
+#ifndef DFS_LM_FUSED_BIG_ROWS
+#define DFS_LM_FUSED_BIG_ROWS INT64_MAX
+#endif
+TileKind fused_tile_kind(int64_t rows) {
+  return rows <= kSmallRows ? kSmallTile : rows < (int64_t)DFS_LM_FUSED_BIG_ROWS ? kMidTile : kBigTile;
+}
 
+// The fused kernel's grid.
 Grid make_grid(int64_t rows, int64_t V, int64_t d) {
   Grid g{};
   g.rows = rows;
   g.V = V;
   g.d = d;
-  const TileKind kind = tile_kind(rows);
+  const TileKind kind = fused_tile_kind(rows);
   const bool big = kind == kBigTile && DFS_LM_BIG_TILE;
   const int BM = kind == kSmallTile ? 16 : big ? 256 : 128;
   const int BN = kind == kSmallTile || big ? 256 : 128;
@@ -360,7 +407,7 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* W_lm, int64_t rows
   const dim3 grid((unsigned)(8 * g.group * cdiv(g.groups, 8)));
   const uint16_t* hp = static_cast<const uint16_t*>(hidden);
   const uint16_t* wp = static_cast<const uint16_t*>(W_lm);
-  switch (tile_kind(rows)) {  // (few rows took the two-pass way above)
+  switch (fused_tile_kind(rows)) {  // (few rows took the two-pass way above)
     case kMidTile:
       lmhead_topk_dma_kernel<MidCfg, kMidWG><<<grid, kThreads, 0, stream>>>(hp, wp, g, partial, cand);
       break;
