@@ -22,13 +22,14 @@ struct PackJob {
 };
 
 // A gate GEMM for few rows, as a list of independent 256-thread jobs (gate_tile.h):
-// bf16 (pre-packed W_h) 16-row tiles or fp32 8-row tiles; job j = row tile j % mtiles of
-// K split j / mtiles.  kchunk: k per split (a multiple of 32 for bf16).
+// bf16 (pre-packed W_h) tiles of 16 rgroups rows or fp32 8-row tiles; job j = row tile
+// j % mtiles of K split j / mtiles.  kchunk: k per split (a multiple of 32 for bf16).
 struct GateJobs {
   const void* H = nullptr;
   const void* W = nullptr;  // packed (bf16) or as stored (fp32)
   int64_t rows = 0, d = 0, kchunk = 0;
   int mtiles = 0, splits = 0;  // mtiles * splits jobs (0: none)
+  int rgroups = 1;             // bf16: 16-row groups per tile (1 or gtile::kTallGroups)
   float* partial = nullptr;    // [splits, rows, 256] when splits > 1
   float* out = nullptr;        // [rows, 256] when splits == 1
 };
@@ -79,6 +80,7 @@ struct GatePlan {
   int kind;            // kJobs: independent 256-thread tiles (bf16 16 rows, fp32 8 rows);
                        // kTile64: 64-row tiles of eight waves; kDma: 128 x 128 LDS-DMA tiles
   int mtiles;          // row tiles
+  int rgroups;         // kJobs, bf16: 16-row groups per tile
   int splits;          // K splits (partial sums added in split order before the sigmoid)
   int64_t kchunk;      // hidden elements per split
   size_t packed_off, packed_bytes;    // W_h packed for the matrix cores (bf16 path)

@@ -41,9 +41,10 @@ static_assert(kKB == kPackK, "the GEMM steps through W_h one packed slab at a ti
 #define DFS_GATE_TARGET_WG 256
 #endif
 constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims for
-// 16-row tiles up to kGateTileRows rows: about DFS_GATE_SMALL_WG workgroups up to
-// DFS_GATE_SMALL_ROWS rows (their partial sums are added on the critical path of a
-// short call), about DFS_GATE_JOBS_WG beyond; at least this many k steps per split.
+// Independent tiles up to kGateTileRows rows: 16-row tiles over about DFS_GATE_SMALL_WG
+// workgroups up to DFS_GATE_SMALL_ROWS rows (their partial sums are added on the
+// critical path of a short call), tiles of 16 kTallGroups rows over about
+// DFS_GATE_JOBS_WG beyond; at least this many k steps per split.
 #ifndef DFS_GATE_SMALL_ROWS
 #define DFS_GATE_SMALL_ROWS 64
 #endif
@@ -51,7 +52,7 @@ constexpr int kTargetWG = DFS_GATE_TARGET_WG;  // workgroups the K split aims fo
 #define DFS_GATE_SMALL_WG 16
 #endif
 #ifndef DFS_GATE_JOBS_WG
-#define DFS_GATE_JOBS_WG 256
+#define DFS_GATE_JOBS_WG 128
 #endif
 #ifndef DFS_GATE_SMALL_MIN_STEPS
 #define DFS_GATE_SMALL_MIN_STEPS 4
@@ -331,6 +332,7 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
   p.rows = rows;
   p.d = d;
   p.bf16 = bf16;
+  p.rgroups = 1;
   size_t off = 0;
   if (bf16) {
     const int64_t KB = cdiv(d, kKB);
@@ -339,7 +341,8 @@ GatePlan plan_gate(int64_t rows, int64_t d, bool bf16) {
       // 16-row tiles, K split over about DFS_GATE_SMALL_WG or DFS_GATE_JOBS_WG workgroups
       // (at least DFS_GATE_SMALL_MIN_STEPS k steps each, so that a tile's loads overlap)
       p.kind = GatePlan::kJobs;
-      p.mtiles = (int)cdiv(rows, gtile::kRows16);
+      p.rgroups = rows <= DFS_GATE_SMALL_ROWS ? 1 : gtile::kTallGroups;
+      p.mtiles = (int)cdiv(rows, (int64_t)gtile::kRows16 * p.rgroups);
       splits = cdiv(rows <= DFS_GATE_SMALL_ROWS ? DFS_GATE_SMALL_WG : DFS_GATE_JOBS_WG, p.mtiles);
       min_steps = DFS_GATE_SMALL_MIN_STEPS;
     } else if (rows >= DFS_GATE_DMA_ROWS && d % GC::KK == 0) {
@@ -414,7 +417,7 @@ const float* gate_partials(const GatePlan& p, const void* ws) {
 GateJobs gate_jobs(const GatePlan& p, const void* hidden, const void* W, float* out_gate, void* ws) {
   if (p.kind != GatePlan::kJobs) return GateJobs{};
   float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.partial_off) : nullptr;
-  return GateJobs{hidden, W, p.rows, p.d, p.kchunk, p.mtiles, p.splits, partial, out_gate};
+  return GateJobs{hidden, W, p.rows, p.d, p.kchunk, p.mtiles, p.splits, p.rgroups, partial, out_gate};
 }
 
 hipError_t launch_gate_gemm(const GatePlan& p, const void* hidden, const void* W, float* out_gate, void* ws,

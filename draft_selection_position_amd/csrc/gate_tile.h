@@ -21,7 +21,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kKB = 32;                      // k per MFMA step (one packed slab)
-constexpr int kRows16 = 16;                  // rows per bf16 tile
+constexpr int kRows16 = 16;                  // rows per row group of a bf16 tile
+// Tiles for more than 64 rows: 32 rows, one k step in flight.  Riding in the top-16
+// launch of the selector at 512 x 5120, 128 such tiles (8 K splits) took a call from
+// 52.1 to 48.1 us against 256 tiles of 16 rows; 256 tall tiles, 64, 96, 112, 144 or 192, and
+// 2 or 3 steps in flight were slower, and 64-row tiles hold too many registers for the
+// launch's three waves per SIMD.
+#ifndef DFS_GATE_TALL_GROUPS
+#define DFS_GATE_TALL_GROUPS 2
+#endif
+constexpr int kTallGroups = DFS_GATE_TALL_GROUPS;  // 16-row groups of a tall tile
+#ifndef DFS_GATE_TALL_DEPTH
+#define DFS_GATE_TALL_DEPTH 1
+#endif
+constexpr int kTallDepth = DFS_GATE_TALL_DEPTH;  // its k steps in flight per lane
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer
 #ifndef DFS_GATE_TILE16_DEPTH
 #define DFS_GATE_TILE16_DEPTH 4
@@ -33,48 +46,61 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rsrc, uint32_t vof
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Rows [m0, m0 + 16) x all 256 columns of Z over k steps [kb0, kb1) (bf16 H [rows, d],
-// W_h packed [ceil(d/32)][256][32], zero past d).  Wave w owns columns [64 w, + 64): four
-// V_MFMA_F32_16X16X32_BF16 tiles.  Lane (r, q) feeds H row m0 + r, k 8q .. 8q + 7 of
-// each step (zero past the last row: buffer range check; zero past d) and the packed
-// column 64 w + 16 nt + r at the same k: the operand layout of every other gate GEMM
-// here, so a K split adds up the same products in the same order, bit for bit.  Both
-// operands go straight from memory into a register ring kDepth steps deep.  Results:
-// the K split's partial sums [splits, rows, 256] (splits > 1) or the sigmoid (splits 1).
-__device__ __forceinline__ void tile16(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wp,
-                                       int64_t rows, int64_t d, int64_t m0, int kb0, int kb1, int split,
-                                       int splits, float* __restrict__ partial, float* __restrict__ out,
-                                       int tid) {
+// Rows [m0, m0 + 16 RG) x all 256 columns of Z over k steps [kb0, kb1) (bf16 H [rows, d],
+// W_h packed [ceil(d/32)][256][32], zero past d).  Wave w owns columns [64 w, + 64) of
+// every row: RG x 4 V_MFMA_F32_16X16X32_BF16 tiles.  Lane (r, q) feeds H rows
+// m0 + 16 g + r (g < RG), k 8q .. 8q + 7 of each step (zero past the last row: buffer
+// range check; zero past d) and the packed column 64 w + 16 nt + r at the same k: the
+// operand layout of every other gate GEMM here, so a K split adds up the same products
+// in the same order, bit for bit, whatever RG is.  Both operands go straight from memory
+// into a register ring kDepth steps deep; a taller tile (RG > 1) reads each W_h fragment
+// once for more rows.  Results: the K split's partial sums [splits, rows, 256]
+// (splits > 1) or the sigmoid (splits 1).
+template <int RG, int kDepth>
+__device__ __forceinline__ void tile_rows(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wp,
+                                          int64_t rows, int64_t d, int64_t m0, int kb0, int kb1, int split,
+                                          int splits, float* __restrict__ partial, float* __restrict__ out,
+                                          int tid) {
+  constexpr int TR = kRows16 * RG;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int r = lane & 15;
   const int q = lane >> 4;
   const int KB = (int)((d + kKB - 1) / kKB);
-  const int64_t trows = rows - m0 < kRows16 ? rows - m0 : kRows16;
+  const int64_t trows = rows - m0 < TR ? rows - m0 : TR;
   const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(H + m0 * d), (short)0, (int)(trows * d * 2), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Wp), (short)0, (int)((int64_t)KB * kE * kKB * 2), kRawBufferWord3);
-  const uint32_t hvoff = (uint32_t)(((int64_t)r * d + 8 * q) * 2);
+  uint32_t hvoff[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) hvoff[g] = (uint32_t)(((int64_t)(16 * g + r) * d + 8 * q) * 2);
   uint32_t wvoff[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) wvoff[nt] = (uint32_t)(((64 * wave + 16 * nt + r) * kKB + 8 * q) * 2);
 
-  f32x4 acc[4];
+  f32x4 acc[RG][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 ra[kDepth], rb[kDepth][4];
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[g][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 ra[kDepth][RG], rb[kDepth][4];
   auto fill = [&](int j, int kb) {
-    ra[j] = bload(hrs, hvoff, (uint32_t)kb * kKB * 2);
+#pragma unroll
+    for (int g = 0; g < RG; ++g) ra[j][g] = bload(hrs, hvoff[g], (uint32_t)kb * kKB * 2);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) rb[j][nt] = bload(wrs, wvoff[nt], (uint32_t)kb * kE * kKB * 2);
   };
-  auto step = [&](int kb, uint4 a, const uint4 (&b)[4]) {
+  auto step = [&](int kb, const uint4 (&a)[RG], const uint4 (&b)[4]) {
     const uint32_t keep = (int64_t)kb * kKB + 8 * q < d ? 0xffffffffu : 0u;  // H past d is another row
-    const bf16x8 af = __builtin_bit_cast(bf16x8, make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep));
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, b[nt]), acc[nt], 0, 0, 0);
+    for (int g = 0; g < RG; ++g) {
+      const bf16x8 af =
+          __builtin_bit_cast(bf16x8, make_uint4(a[g].x & keep, a[g].y & keep, a[g].z & keep, a[g].w & keep));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[g][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, b[nt]), acc[g][nt], 0, 0, 0);
+    }
   };
 #pragma unroll
   for (int j = 0; j < kDepth; ++j) fill(j, kb0 + j < kb1 ? kb0 + j : kb1 - 1);
@@ -90,22 +116,24 @@ __device__ __forceinline__ void tile16(const uint16_t* __restrict__ H, const uin
   for (int j = 0; j < kDepth; ++j)
     if (base + j < kb1) step(base + j, ra[j], rb[j]);
 
-  // lane (r, q) holds Z[m0 + 4q + i][64 w + 16 nt + r] in acc[nt][i]
+  // lane (r, q) holds Z[m0 + 16 g + 4q + i][64 w + 16 nt + r] in acc[g][nt][i]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + 4 * q + i;
-    if (m < rows) {
+  for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = 64 * wave + 16 * nt + r;
-        if (splits == 1) {
-          out[m * kE + col] = sigmoidf(acc[nt][i]);
-        } else {
-          partial[((int64_t)split * rows + m) * kE + col] = acc[nt][i];
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 16 * g + 4 * q + i;
+      if (m < rows) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int col = 64 * wave + 16 * nt + r;
+          if (splits == 1) {
+            out[m * kE + col] = sigmoidf(acc[g][nt][i]);
+          } else {
+            partial[((int64_t)split * rows + m) * kE + col] = acc[g][nt][i];
+          }
         }
       }
     }
-  }
 }
 
 // ---------------------------------------------------------------- fp32
@@ -177,8 +205,14 @@ __device__ __forceinline__ void run_gate_job(const GateJobs& g, bool bf16, int64
     const int KB = (int)((g.d + gtile::kKB - 1) / gtile::kKB);
     const int kb0 = s * kps;
     const int kb1 = kb0 + kps < KB ? kb0 + kps : KB;
-    gtile::tile16(static_cast<const uint16_t*>(g.H), static_cast<const uint16_t*>(g.W), g.rows, g.d,
-                  (int64_t)mt * gtile::kRows16, kb0, kb1, s, g.splits, g.partial, g.out, tid);
+    const uint16_t* H = static_cast<const uint16_t*>(g.H);
+    const uint16_t* W = static_cast<const uint16_t*>(g.W);
+    const int64_t m0 = (int64_t)mt * gtile::kRows16 * g.rgroups;
+    if (g.rgroups == 1) {
+      gtile::tile_rows<1, gtile::kDepth>(H, W, g.rows, g.d, m0, kb0, kb1, s, g.splits, g.partial, g.out, tid);
+    } else {
+      gtile::tile_rows<gtile::kTallGroups, gtile::kTallDepth>(H, W, g.rows, g.d, m0, kb0, kb1, s, g.splits, g.partial, g.out, tid);
+    }
   } else {
     const int64_t k0 = (int64_t)s * g.kchunk;
     const int64_t k1 = k0 + g.kchunk < g.d ? k0 + g.kchunk : g.d;

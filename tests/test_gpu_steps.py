@@ -48,14 +48,15 @@ def test_gate_full_size_configs(cfg, full_workload, full_oracle):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-# up to 512 rows the bf16 gate runs as 16-row tiles (1 x 8, 37 x 72, 16 x 5120, 300 x 1000,
-# 16 x 65536 with K split 16 ways, 512 x 96); from 512 rows with d a multiple of 64 on
+# up to 512 rows the bf16 gate runs as independent tiles: 16 rows up to 64 rows (1 x 8,
+# 37 x 72, 16 x 5120, 16 x 65536 with K split 16 ways), 32 rows beyond (300 x 1000 and
+# 113 x 4096: ragged last tiles of 12 and 17 rows, 512 x 96); from 512 rows with d a multiple of 64 on
 # 128 x 128 LDS-DMA tiles of 64-k steps: four ring steps unsplit (2049 x 256), one (4100 x 64),
 # ragged rows over 8 splits (2100 x 5120, finished by its own kernel), 4 splits (4096 x 2048),
 # 20 splits (600 x 16384); otherwise the 64-row tiles (3000 x 1000 and 1024 x 96: d not a
 # multiple of 64).  W_h ~ N(0, 0.05^2), scaled down beyond d = 5120 so that h W_h keeps the
 # scale it has there.
-@pytest.mark.parametrize("rows,d", [(1, 8), (37, 72), (16, 5120), (300, 1000), (16, 65536), (512, 96),
+@pytest.mark.parametrize("rows,d", [(1, 8), (37, 72), (16, 5120), (300, 1000), (113, 4096), (16, 65536), (512, 96),
                                     (2049, 256), (4100, 64), (2100, 5120), (4096, 2048), (600, 16384),
                                     (3000, 1000), (1024, 96)])
 def test_gate_shapes(rows, d, dtype):
