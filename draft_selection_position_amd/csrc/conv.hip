@@ -176,7 +176,9 @@ __global__ __launch_bounds__(kThreads, DFS_CONV_WAVES_PER_EU) void conv2_bf16_ke
 // sequence: each position's x piece is read once and serves as the next position's
 // predecessor from registers (with kR = 1 the predecessor is read again), and the
 // base kernel's two pieces are read once.  Per position, the group's two correction
-// columns are read for every split and added in split order.
+// columns are read for every split and added in split order.  Every load of a run
+// (its x pieces and, up to kSplitRegs splits, all its correction columns) is issued
+// before the first sum, so a thread waits for memory once, not once per position.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split_sum(const float* pc, int64_t sstride, int splits, float& c0, float& c1) {
   c0 = 0.0f;
@@ -187,6 +189,17 @@ __device__ __forceinline__ void split_sum(const float* pc, int64_t sstride, int 
     c1 += v.y;
   }
 }
+
+#ifndef DFS_CONV_EPI_SPLIT_REGS
+#define DFS_CONV_EPI_SPLIT_REGS 4
+#endif
+constexpr int kSplitRegs = DFS_CONV_EPI_SPLIT_REGS;  // splits whose columns are loaded up front
+// The output leaves with non-temporal stores (nothing here reads it back): at 4096 x 5120
+// with three splits the epilogue's loads issued up front and these stores took a call
+// from 66.4 to 65.0 us.
+#ifndef DFS_CONV_EPI_NT
+#define DFS_CONV_EPI_NT 1
+#endif
 
 template <typename Idx, int kR>
 __global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
   const int64_t ch = 8 * (int64_t)(j - run * P);
   const Idx b = run / runs;
   const int t0 = (int)(run - b * runs) * kR;
-  const int t1 = t0 + kR < L ? t0 + kR : L;
+  const int n = (t0 + kR < L ? t0 + kR : L) - t0;  // positions of this run, 1..kR
   const int64_t rows = batch * (int64_t)L;
   const int64_t nvec = D / 8;
   const int64_t sstride = rows * nvec;
@@ -210,13 +223,48 @@ __global__ __launch_bounds__(kThreads) void conv2_split_epilogue_kernel(
   const int64_t m0 = (int64_t)b * L + t0;
   uint4 pv = t0 > 0 ? *reinterpret_cast<const uint4*>(x + (m0 - 1) * D + ch)
                     : *reinterpret_cast<const uint4*>(xprev + (int64_t)b * D + ch);
-  for (int t = t0; t < t1; ++t) {
-    const int64_t m = (int64_t)b * L + t;
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + m * D + ch);
-    float c0, c1;
-    split_sum(partial + m * nvec + 2 * (ch / 16), sstride, splits, c0, c1);
-    *reinterpret_cast<uint4*>(y + m * D + ch) = conv8(xv, pv, b0, b1, c0, c1);
-    pv = xv;
+  uint4 xs[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i)
+    xs[i] = i < n ? *reinterpret_cast<const uint4*>(x + (m0 + i) * D + ch) : make_uint4(0u, 0u, 0u, 0u);
+  const float* pc = partial + m0 * nvec + 2 * (ch / 16);
+  float c0[kR], c1[kR];
+  if (splits <= kSplitRegs) {
+    f32x2 v[kR][kSplitRegs];
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+#pragma unroll
+      for (int s = 0; s < kSplitRegs; ++s)
+        v[i][s] = (i < n && s < splits) ? *reinterpret_cast<const f32x2*>(pc + i * nvec + s * sstride)
+                                        : f32x2{0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      c0[i] = 0.0f;
+      c1[i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kSplitRegs; ++s)
+        if (s < splits) {
+          c0[i] += v[i][s].x;
+          c1[i] += v[i][s].y;
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+      if (i < n) split_sum(pc + i * nvec, sstride, splits, c0[i], c1[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    if (i < n) {
+      const uint4 o = conv8(xs[i], pv, b0, b1, c0[i], c1[i]);
+#if DFS_CONV_EPI_NT
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4_t{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4_t*>(y + (m0 + i) * D + ch));
+#else
+      *reinterpret_cast<uint4*>(y + (m0 + i) * D + ch) = o;
+#endif
+      pv = xs[i];
+    }
   }
 }
 
