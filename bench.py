@@ -142,12 +142,12 @@ def _load_json(d, w):
 
 def bench_table(d: str) -> None:
     """Print the all-workloads tables (markdown) from the JSON lines of
-    `bench.py --workload <w> --no-cpu-baseline --verify --conv --lmhead`, saved as DIR/<w>.json."""
+    `bench.py --workload <w> --no-cpu-baseline --verify --conv --lmhead [--library]`, saved as DIR/<w>.json."""
     from workloads import config_by_name
 
     out = ["# bench.py on the five workloads, MI355X (one GPU)", "",
            "Command (repository root), per workload: `python bench.py --workload <name> --no-cpu-baseline "
-           "--verify --conv --lmhead`",
+           "--verify --conv --lmhead --library`",
            "(20 warm-up calls, then per-call timing of at least 200 calls, then 200 timed `dfs_select_packed` calls; "
            "hipEvents on the launch stream; input sets rotated so that at least 512 MB cycle through; "
            "`python bench.py --bench-table <dir>` turns the JSON lines into these tables). "
@@ -191,6 +191,20 @@ def bench_table(d: str) -> None:
             continue
         out.append(f"| {w} | {v['fused_ms']:.3f} | {v['chain_ms']:.3f} ({v['logits_ms']:.3f} + {v['topk_fp32_ms']:.3f}) | "
                    f"{v['fused_TFLOPs']:.0f} | {v['fused_GBps']:.0f} | {v['fused_equals_chain']} |")
+    if all("library" in _load_json(d, w) for w in TABLE_WORKLOADS):
+        out += ["", "For scale, the vendor library (`--library`: torch.matmul, hipBLASLt) on the bare products, timed",
+                "the same way (the gate without its sigmoid, the convolution's correction without the convolution,",
+                "the LM head's logits in bf16):", "",
+                "| workload | gate us (dfs_gate) | gate product us (library) | conv us (dfs_conv2) | "
+                "correction product us (library) | LM head ms (dfs_lmhead_topk) | logits product ms (library) |",
+                "|---|---|---|---|---|---|---|"]
+        for w in TABLE_WORKLOADS:
+            r = _load_json(d, w)
+            lib_, lm = r["library"], r["lmhead"]
+            lm_ours = "—" if "skipped" in lm else f"{lm['fused_ms']:.3f}"
+            lm_lib = f"{lib_['lmhead_product_ms']:.3f}" if "lmhead_product_ms" in lib_ else "—"
+            out.append(f"| {w} | {r['step_ms']['gate'] * 1e3:.1f} | {lib_['gate_ms'] * 1e3:.1f} | "
+                       f"{r['conv']['ms'] * 1e3:.1f} | {lib_['conv_product_ms'] * 1e3:.1f} | {lm_ours} | {lm_lib} |")
     print("\n".join(out))
 
 
@@ -291,6 +305,9 @@ def main() -> int:
     ap.add_argument("--lmhead", action="store_true",
                     help="also time dfs_lmhead_topk (top-16 straight from the hidden states through a "
                          "synthetic [V, d] LM head) against the unfused dfs_lmhead_logits + dfs_topk")
+    ap.add_argument("--library", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the products of the gate, and of the convolution "
+                         "and the LM head when those legs run, for scale")
     ap.add_argument("--verify", action="store_true",
                     help="also time dfs_select_draft + dfs_verify against synthetic target logits "
                          "[batch, L + 1, V] (the drafter's logits plus noise, one more random row)")
@@ -438,6 +455,12 @@ def main() -> int:
 
     hidden2d = dev["hidden"].view(-1, cfg.d)
     gate_ms = timed(lambda: dfs.gate(hidden2d, packed[0]))
+    library = {} if args.library else None
+    if args.library:
+        # the gate's product alone (no sigmoid) through the vendor library, same operands
+        zlib = torch.empty((hidden2d.shape[0], 256), dtype=hidden2d.dtype, device=hidden2d.device)
+        library["gate_ms"] = timed(lambda: torch.matmul(hidden2d, dev["W_h"], out=zlib))
+        del zlib
     idx, val = dfs.topk(logits2d, workspace=ws)
     g = dfs.gate(hidden2d, dev["W_h"])
     idx3, val3 = idx.view(cfg.batch, cfg.L, 16), val.view(cfg.batch, cfg.L, 16)
@@ -515,6 +538,13 @@ def main() -> int:
         conv = dfs.Conv2(cfg.batch, cfg.L, cfg.d, dtype=cx[0].dtype)
         it = iter(range(1 << 30))
         conv_ms = timed(lambda: conv(cx[next(it) % ncs], *cargs), n=max(50, args.steps))
+        if args.library:
+            # the correction product x W_c^T alone through the vendor library, same rotation
+            Wct = cargs[2].reshape(-1, cfg.d).t().contiguous()
+            clib = torch.empty((cfg.batch * cfg.L, Wct.shape[1]), dtype=Wct.dtype, device=Wct.device)
+            library["conv_product_ms"] = timed(
+                lambda: torch.matmul(cx[next(it) % ncs].view(-1, cfg.d), Wct, out=clib), n=max(50, args.steps))
+            del Wct, clib
         es = cx[0].element_size()
         D, rows = cfg.d, cfg.batch * cfg.L
         cbytes = 2 * rows * D * es + cfg.batch * D * es + 2 * D * es + (D // 8) * D * es
@@ -548,6 +578,11 @@ def main() -> int:
                           device=W_lm.device)
         topk32_ms = timed(lambda: dfs.topk(U, workspace=uws), n=n_lm)
         i2, v2 = dfs.topk(U, workspace=uws)
+        if args.library:
+            # the product alone through the vendor library, bf16 out (half of U's bytes)
+            ulib = torch.empty((rows, cfg.V), dtype=W_lm.dtype, device=W_lm.device)
+            library["lmhead_product_ms"] = timed(lambda: torch.matmul(hidden2d, W_lm.t(), out=ulib), n=n_lm)
+            del ulib
         flops = 2 * rows * cfg.V * cfg.d
         wbytes = cfg.V * cfg.d * 2 + rows * cfg.d * 2
         lm_out = {"fused_ms": fused_ms, "logits_ms": logits_ms, "topk_fp32_ms": topk32_ms,
@@ -598,6 +633,8 @@ def main() -> int:
         out["verify"] = verify_out
     if conv_out is not None:
         out["conv"] = conv_out
+    if library is not None:
+        out["library"] = library
     if lm_out is not None:
         out["lmhead"] = lm_out
     if graph_ms is not None:
