@@ -191,6 +191,8 @@ def bench_table(d: str) -> None:
             continue
         out.append(f"| {w} | {v['fused_ms']:.3f} | {v['chain_ms']:.3f} ({v['logits_ms']:.3f} + {v['topk_fp32_ms']:.3f}) | "
                    f"{v['fused_TFLOPs']:.0f} | {v['fused_GBps']:.0f} | {v['fused_equals_chain']} |")
+    out += ["", "Up to 32 rows `dfs_lmhead_topk` runs the same two kernels as the chain (the product written out,",
+            "then the top-16 pass over it), so there the two differ only by the run-to-run spread."]
     if all("library" in _load_json(d, w) for w in TABLE_WORKLOADS):
         out += ["", "For scale, the vendor library (`--library`: torch.matmul, hipBLASLt) on the bare products, timed",
                 "the same way (the gate without its sigmoid, the convolution's correction without the convolution,",
