@@ -10,8 +10,9 @@
 // vectors in flight while the current ones are scanned.  An element is only looked at
 // further when it reaches the wave's admission threshold (which starts at a bound taken
 // over the wave's first iteration); admitted elements are appended to a per-wave
-// LDS buffer as exact 64-bit (value, index) keys with one ballot per element
-// slot (chunks held whole in registers: one prefix count for all of a lane's elements),
+// LDS buffer as exact 64-bit (value, index) keys, placed by one ballot when no lane holds
+// more than one of a vector's admitted elements, else by a prefix count of every lane's
+// admissions (chunks held whole in registers: one prefix count for all of a lane's elements),
 // and the buffer is merged into the wave's sorted top-16 (held in lanes 0..15) by a
 // 64-lane bitonic sort.  The 16th best key of any wave is a valid threshold for the
 // whole chunk and is shared through LDS (in launches of two rounds, the bound over all
@@ -90,6 +91,11 @@ constexpr int64_t kWideSeedMaxBlocks = 2048;
 // four waves' lists at every merge (wave_merge): fewer admissions where the VALU is busy.
 #ifndef DFS_TOPK_UNION
 #define DFS_TOPK_UNION 1
+#endif
+// Admissions of one vector step: a bit mask per lane and one ballot for the usual case of
+// at most one passing element per lane (1), or one ballot per element slot (0).
+#ifndef DFS_TOPK_APPEND_BATCHED
+#define DFS_TOPK_APPEND_BATCHED 1
 #endif
 // Few rows: workgroups the split aims for.
 #ifndef DFS_TOPK_SMALL_TARGET_BLOCKS
@@ -253,8 +259,36 @@ __device__ __forceinline__ void scan_vec(uint4 d, bool valid, uint32_t idx0, Wav
 #pragma unroll
   for (int e = 1; e < PV; ++e) m = fmaxf(m, v[e]);
   if (__ballot(m >= w.thr) == 0) return;
+#if DFS_TOPK_APPEND_BATCHED
+  // Each lane's passing elements as a bit mask.  Typically every lane that passes holds
+  // one passing element, which is then its maximum m: one ballot places all of them.
+  // Otherwise a lane's count is summed over the lanes below it with one ballot per count
+  // bit, and each lane appends its elements in order.
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < PV; ++e) bits |= (v[e] >= w.thr ? 1u : 0u) << e;
+  if (__ballot(bits & (bits - 1u)) == 0) {
+    const uint64_t mask = __ballot(bits != 0u);
+    if (bits != 0u) buf[w.cnt + lanes_below(mask)] = make_key(m, idx0 + (uint32_t)__builtin_ctz(bits));
+    w.cnt = uniform(w.cnt + __popcll(mask));
+  } else {
+    const int c = __popc(bits);
+    int pos = w.cnt, tot = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) <= PV; ++b) {
+      const uint64_t mb = __ballot((c >> b) & 1);
+      pos += lanes_below(mb) << b;
+      tot += __popcll(mb) << b;
+    }
+#pragma unroll
+    for (int e = 0; e < PV; ++e)
+      if ((bits >> e) & 1u) buf[pos++] = make_key(v[e], idx0 + e);
+    w.cnt = uniform(w.cnt + tot);
+  }
+#else
 #pragma unroll
   for (int e = 0; e < PV; ++e) append(w, v[e] >= w.thr, v[e], idx0 + e, buf);
+#endif
   if (w.cnt > kMergeAt) wave_merge<kCompact, kUnion>(w, buf, s_thr, lane);
 }
 
