@@ -92,9 +92,21 @@ int check_walk_mode(int mode, double temperature) {
 struct SelectLayout {
   TopkPlan topk;
   GatePlan gate;
-  bool few;  // few rows: per-position pair workgroups (tiles, counters)
-  size_t cand_idx_off, cand_val_off, gate_off, topk_ws_off, gate_ws_off, tiles_off, counters_off, total;
+  bool few;    // few rows: per-position pair workgroups (tiles, counters)
+  bool tiled;  // mid-size batches: the pair tensor by position, then the walk by sequence
+  size_t cand_idx_off, cand_val_off, gate_off, topk_ws_off, gate_ws_off, tiles_off, counters_off, pair_off, total;
 };
+
+// Batches up to this many sequences (beyond the few-row path, rows not split by the
+// top-16 pass) score their pairs a wave per position and walk them in a second launch: a
+// workgroup per sequence would leave most CUs without gathers (32 x 16 x 151936: 47.2 ->
+// 44.4 us per call; 64 x 16 x 262144: 110.9 -> 107.2 us).  At 256 sequences, a workgroup
+// per CU, the extra launch and the pair tensor's round trip cost more (219.7 -> 223.7 us);
+// 128 lies between the sizes measured.
+#ifndef DFS_TILED_MAX_BATCH
+#define DFS_TILED_MAX_BATCH 128
+#endif
+constexpr int64_t kTiledMaxBatch = DFS_TILED_MAX_BATCH;
 
 SelectLayout select_layout(const dfs_shape_t& s) {
   SelectLayout l{};
@@ -120,6 +132,9 @@ SelectLayout select_layout(const dfs_shape_t& s) {
     l.counters_off = off;
     off += align_up((size_t)s.batch * sizeof(uint32_t), 256);
   }
+  l.tiled = !l.few && l.topk.parts <= 1 && s.batch <= kTiledMaxBatch;
+  l.pair_off = off;
+  if (l.tiled) off += align_up((size_t)rows * DFS_K * DFS_K * sizeof(float), 256);
   l.total = off;
   return l;
 }
@@ -209,6 +224,12 @@ static int select_impl(const void* logits, const void* hidden, const int32_t* pr
   if (l.few) {
     e = launch_pair_pos(cs, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V, wa, out_path,
                         out_scores, reinterpret_cast<PosTile*>(w + l.tiles_off), counters, stream);
+  } else if (l.tiled && out_q == nullptr) {
+    float* pair = reinterpret_cast<float*>(w + l.pair_off);
+    e = launch_pair_tiles(cand_idx, cand_val, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V,
+                          pair, stream);
+    if (e != hipSuccess) return DFS_E_HIP;
+    e = launch_walk(pair, cand_idx, s.batch, s.L, wa, out_path, out_scores, stream);
   } else {
     e = launch_pair_walk(cs, prev_token, gs, A, B, s.table_dtype == DFS_BF16, s.batch, s.L, s.V, nullptr, &wa,
                          out_path, out_scores, stream);

@@ -154,6 +154,11 @@ hipError_t launch_pair_pos(const CandSrc& cand, const int32_t* prev_token, const
                            const void* B, bool bf16_tables, int64_t batch, int64_t L, int64_t V,
                            const WalkArgs& walk, int32_t* out_path, float* out_scores, PosTile* tiles,
                            uint32_t* counters, hipStream_t stream);
+// Mid-size batches: the [rows, 16, 16] pair tensor from final candidate lists, one wave
+// per (sequence, position); launch_walk then walks it.
+hipError_t launch_pair_tiles(const int32_t* cand_idx, const float* cand_val, const int32_t* prev_token,
+                             const GateSrc& gate, const void* A, const void* B, bool bf16_tables, int64_t batch,
+                             int64_t L, int64_t V, float* out_pair, hipStream_t stream);
 hipError_t launch_walk(const float* pair, const int32_t* cand_idx, int64_t batch, int64_t L,
                        const WalkArgs& walk, int32_t* out_path, float* out_scores,
                        hipStream_t stream);

@@ -433,6 +433,46 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   }
 }
 
+// ---------------------------------------------------------------- mid-size batches
+// A workgroup per sequence puts the gathers of a batch of a few dozen sequences on as
+// many CUs.  Here each (sequence, position) is one wave, four to a workgroup, that scores
+// its 16 x 16 tile with score_tile into a pair tensor [rows, 16, 16]; walk_kernel then
+// walks every sequence over it.  The tile and the walk are the fused kernel's own
+// functions, so the path and the scores are the same bits.  Final candidate lists only
+// (rows not split by the top-16 pass).
+constexpr int kTileWaves = 4;
+
+template <bool kBf16Tables>
+__global__ __launch_bounds__(kWave * kTileWaves) void pair_tile_kernel(
+    const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_val, const int32_t* __restrict__ prev_token,
+    const float* __restrict__ gate, int gate_splits, int64_t gate_stride, const void* __restrict__ A_,
+    const void* __restrict__ B_, int L, int64_t V, int64_t rows, float* __restrict__ out_pair) {
+  __shared__ __attribute__((aligned(16))) float sG[kTileWaves][kE];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int64_t row = (int64_t)blockIdx.x * kTileWaves + w;
+  if (row >= rows) return;  // wave-uniform; only wave-level barriers follow
+  const int64_t b = row / L;
+  const int t = (int)(row % L);
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
+  const int32_t pred_id = *pred_p;
+  const int32_t cand_id = cand_idx[row * kK + r];
+  const float u = cand_val[row * kK + r];
+  GateRegs gr;
+  gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
+  // ids outside [0, V) break the caller's contract; clamped so no gather leaves the tables
+  const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
+  const int64_t cand = cand_id < 0 ? 0 : (cand_id >= V ? V - 1 : cand_id);
+  const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
+  __builtin_amdgcn_sched_barrier(0);
+  float sc[4];
+  score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG[w], lane, sc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
+}
+
 // ---------------------------------------------------------------- few rows
 // With few rows one workgroup per sequence would pull every position's gate partial sums
 // and table rows through a single CU; instead each (sequence, position) gets a workgroup
@@ -649,6 +689,22 @@ hipError_t launch_pair_pos(const CandSrc& c, const int32_t* prev_token, const Ga
     DFS_PP(false);
   }
 #undef DFS_PP
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_tiles(const int32_t* cand_idx, const float* cand_val, const int32_t* prev_token,
+                             const GateSrc& g, const void* A, const void* B, bool bf16_tables, int64_t batch,
+                             int64_t L, int64_t V, float* out_pair, hipStream_t stream) {
+  if (g.splits < 1) return hipErrorInvalidValue;
+  const int64_t rows = batch * L;
+  const dim3 grid((unsigned)((rows + kTileWaves - 1) / kTileWaves));
+  if (bf16_tables) {
+    pair_tile_kernel<true><<<grid, kWave * kTileWaves, 0, stream>>>(cand_idx, cand_val, prev_token, g.gate, g.splits,
+                                                                     g.stride, A, B, (int)L, V, rows, out_pair);
+  } else {
+    pair_tile_kernel<false><<<grid, kWave * kTileWaves, 0, stream>>>(cand_idx, cand_val, prev_token, g.gate, g.splits,
+                                                                      g.stride, A, B, (int)L, V, rows, out_pair);
+  }
   return hipGetLastError();
 }
 
