@@ -36,6 +36,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxL = 16;
+// The pair kernels issue a position's 16 + 16 table-row gathers before they wait for its
+// gate row (1) or after (0): the per-sequence kernel and the per-position tile kernel (1:
+// 512 rows 43.9 -> 43.3 us per dfs_select, 1024 x 262144 107.5 -> 106.6).
+#ifndef DFS_PW_GATHER_FIRST
+#define DFS_PW_GATHER_FIRST 0  // 1 spills (the gate sum's 16 registers sets and the gathers live at once, 128 VGPRs)
+#endif
+#ifndef DFS_TILE_GATHER_FIRST
+#define DFS_TILE_GATHER_FIRST 1
+#endif
 
 // Standard Gumbel noise for (sequence b, position t, slot j), fp64:
 // u = ((x >> 9) + 1/2) 2^-23 in (0, 1), g = -log(-log u).
@@ -275,43 +284,61 @@ __device__ __forceinline__ float4 gate_finish(const float* __restrict__ gate, in
 // that row, read back by other lanes of the wave only.  The gathers are all in flight
 // before the gate row is parked in LDS (scheduling barriers keep that order).  Every
 // kernel that scores pairs calls this, so their scores agree bit for bit.
+// The bf16 tables' fragments of one tile, loaded by tile_rows_issue and consumed by
+// score_tile_rows: a caller may issue them before it waits for the gate row.
+struct TileRows {
+  bf16x8 av[8], bv[8];
+};
+__device__ __forceinline__ void tile_rows_issue(const void* __restrict__ A_, const void* __restrict__ B_, int64_t pred,
+                                                int64_t cand, int lane, TileRows& tr) {
+  const int q = lane >> 4;
+  // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
+  const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) + pred * kE + 16 * q);
+  const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) + cand * kE + 16 * q);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    tr.av[c] = Ap[8 * (c >> 1) + (c & 1)];
+    tr.bv[c] = Bp[8 * (c >> 1) + (c & 1)];
+  }
+}
+__device__ __forceinline__ void score_tile_rows(const TileRows& tr, float u, float4 gp, float* sGr, int lane,
+                                                float (&sc)[4]) {
+  const int q = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float g[8];
+    const float4 g0 = *reinterpret_cast<const float4*>(&sGr[64 * (c >> 1) + 16 * q + 8 * (c & 1)]);
+    const float4 g1 = *reinterpret_cast<const float4*>(&sGr[64 * (c >> 1) + 16 * q + 8 * (c & 1) + 4]);
+    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+    g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ag = (float)tr.av[c][e] * g[e];
+      hi[e] = (__bf16)ag;
+      lo[e] = (__bf16)(ag - (float)hi[e]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, tr.bv[c], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, tr.bv[c], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = acc[i] + u;
+}
+
 template <bool kBf16Tables>
 __device__ __forceinline__ void score_tile(const void* __restrict__ A_, const void* __restrict__ B_, int64_t pred,
                                            int64_t cand, float u, float4 gp, float* sGr, int lane, float (&sc)[4]) {
   const int q = lane >> 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kBf16Tables) {
-    // fragment c of this lane: elements [64 (c / 2) + 16 q + 8 (c % 2), + 8)
-    const bf16x8* Ap = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(A_) +
-                                                       pred * kE + 16 * q);
-    const bf16x8* Bp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(B_) +
-                                                       cand * kE + 16 * q);
-    bf16x8 av[8], bv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      av[c] = Ap[8 * (c >> 1) + (c & 1)];
-      bv[c] = Bp[8 * (c >> 1) + (c & 1)];
-    }
+    TileRows tr;
+    tile_rows_issue(A_, B_, pred, cand, lane, tr);
     __builtin_amdgcn_sched_barrier(0);
-    *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float g[8];
-      const float4 g0 = *reinterpret_cast<const float4*>(&sGr[64 * (c >> 1) + 16 * q + 8 * (c & 1)]);
-      const float4 g1 = *reinterpret_cast<const float4*>(&sGr[64 * (c >> 1) + 16 * q + 8 * (c & 1) + 4]);
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ag = (float)av[c][e] * g[e];
-        hi[e] = (__bf16)ag;
-        lo[e] = (__bf16)(ag - (float)hi[e]);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv[c], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv[c], acc, 0, 0, 0);
-    }
+    score_tile_rows(tr, u, gp, sGr, lane, sc);
+    return;
   } else {
     // fp32 (one k slot per lane and step): step 4 c + s gives lane group q the value
     // e = 16 c + 4 q + s, so a lane reads e = 16 c + 4 q + 0..3 as one float4 and
@@ -403,10 +430,18 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
   // The gate row is parked in LDS before the table-row fragments are loaded, so that
   // all of them can be in flight at once; the scheduling barriers keep that order.  The
   // row is read back by other lanes of the same wave only.
-  const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
-  __builtin_amdgcn_sched_barrier(0);
   float sc[4];
-  score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG[t], lane, sc);
+  if constexpr (kBf16Tables && DFS_PW_GATHER_FIRST) {
+    TileRows tr;
+    tile_rows_issue(A_, B_, pred, cand, lane, tr);
+    const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile_rows(tr, u, gp, sG[t], lane, sc);
+  } else {
+    const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG[t], lane, sc);
+  }
   if (kWalk && lane < kK) sW.cand[t][lane] = cand_id;
   // lane holds S_t(predecessor slot 4q + i, candidate slot r) in sc[i]
   if constexpr (kWritePair) {
@@ -465,10 +500,18 @@ __global__ __launch_bounds__(kWave * kTileWaves) void pair_tile_kernel(
   // ids outside [0, V) break the caller's contract; clamped so no gather leaves the tables
   const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
   const int64_t cand = cand_id < 0 ? 0 : (cand_id >= V ? V - 1 : cand_id);
-  const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
-  __builtin_amdgcn_sched_barrier(0);
   float sc[4];
-  score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG[w], lane, sc);
+  if constexpr (kBf16Tables && DFS_TILE_GATHER_FIRST) {
+    TileRows tr;
+    tile_rows_issue(A_, B_, pred, cand, lane, tr);
+    const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile_rows(tr, u, gp, sG[w], lane, sc);
+  } else {
+    const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG[w], lane, sc);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) out_pair[(row * kK + 4 * q + i) * kK + r] = sc[i];
 }
