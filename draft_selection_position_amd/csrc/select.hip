@@ -37,10 +37,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxL = 16;
 // The pair kernels issue a position's 16 + 16 table-row gathers before they wait for its
-// gate row (1) or after (0): the per-sequence kernel and the per-position tile kernel (1:
-// 512 rows 43.9 -> 43.3 us per dfs_select, 1024 x 262144 107.5 -> 106.6).
+// gate row (1) or after (0): the per-sequence kernel (1: 4096 rows 220.3 -> 219.9 us per
+// dfs_select; it then sums the gate in rounds of four splits, to stay within its registers)
+// and the per-position tile kernel (1: 512 rows 43.9 -> 43.3 us, 1024 x 262144 107.5 -> 106.6).
 #ifndef DFS_PW_GATHER_FIRST
-#define DFS_PW_GATHER_FIRST 0  // 1 spills (the gate sum's 16 registers sets and the gathers live at once, 128 VGPRs)
+#define DFS_PW_GATHER_FIRST 1
 #endif
 #ifndef DFS_TILE_GATHER_FIRST
 #define DFS_TILE_GATHER_FIRST 1
@@ -241,30 +242,35 @@ __device__ __forceinline__ void draft_q(const float (*sS)[kK][kK], const WalkTab
 // up, loading any further rounds.  The guards are wave-uniform branches, not predicated
 // loads.
 constexpr int kGateRound = 16;
+template <int N = kGateRound>
 struct GateRegs {
-  float4 v[kGateRound];
+  float4 v[N];
 };
 
-__device__ __forceinline__ void gate_load_round(const float* p, int s0, int splits, int64_t stride, GateRegs& g) {
+template <int N>
+__device__ __forceinline__ void gate_load_round(const float* p, int s0, int splits, int64_t stride, GateRegs<N>& g) {
 #pragma unroll
-  for (int u = 0; u < kGateRound; ++u)
+  for (int u = 0; u < N; ++u)
     if (s0 + u < splits) g.v[u] = *reinterpret_cast<const float4*>(p + (int64_t)(s0 + u) * stride);
 }
 
+template <int N>
 __device__ __forceinline__ void gate_issue(const float* __restrict__ gate, int splits, int64_t stride,
-                                           int64_t row, int lane, GateRegs& g) {
+                                           int64_t row, int lane, GateRegs<N>& g) {
   gate_load_round(gate + row * kE + 4 * lane, 0, splits, stride, g);
 }
 
+// Rounds of N splits; the sums run in split order whatever N is, so every N gives the same bits.
+template <int N>
 __device__ __forceinline__ float4 gate_finish(const float* __restrict__ gate, int splits, int64_t stride,
-                                              int64_t row, int lane, GateRegs& g) {
+                                              int64_t row, int lane, GateRegs<N>& g) {
   if (splits == 1) return g.v[0];
   float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const float* p = gate + row * kE + 4 * lane;
-  for (int s0 = 0; s0 < splits; s0 += kGateRound) {
+  for (int s0 = 0; s0 < splits; s0 += N) {
     if (s0 > 0) gate_load_round(p, s0, splits, stride, g);
 #pragma unroll
-    for (int u = 0; u < kGateRound; ++u) {
+    for (int u = 0; u < N; ++u) {
       if (s0 + u < splits) {
         z.x += g.v[u].x;
         z.y += g.v[u].y;
@@ -390,7 +396,9 @@ __global__ __launch_bounds__(kWave * kMaxL) __attribute__((amdgpu_waves_per_eu(4
 
   int32_t pred_id, cand_id;
   float u;
-  GateRegs gr;
+  // with the gathers issued first, rounds of four gate splits keep both within the
+  // 128 registers of a 16-wave workgroup
+  GateRegs<DFS_PW_GATHER_FIRST ? 4 : kGateRound> gr;
   if (parts <= 1) {
     // The candidates are final lists (cand_idx / cand_val).  The gate row does not
     // depend on them: its loads go out right after the id loads (a pointer select, not a
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(kWave * kTileWaves) void pair_tile_kernel(
   const int32_t pred_id = *pred_p;
   const int32_t cand_id = cand_idx[row * kK + r];
   const float u = cand_val[row * kK + r];
-  GateRegs gr;
+  GateRegs<> gr;
   gate_issue(gate, gate_splits, gate_stride, row, lane, gr);
   // ids outside [0, V) break the caller's contract; clamped so no gather leaves the tables
   const int64_t pred = pred_id < 0 ? 0 : (pred_id >= V ? V - 1 : pred_id);
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
 
   int32_t pred_id = 0, cand_id = 0;
   float u = 0.0f;
-  GateRegs gr;
+  GateRegs<> gr;
   if (parts <= 1) {
     if (wave == 0) {
       const int32_t* pred_p = t == 0 ? prev_token + b : cand_idx + (row - 1) * kK + r;
