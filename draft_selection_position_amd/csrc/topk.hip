@@ -453,6 +453,11 @@ __device__ __forceinline__ void topk_body(const void* __restrict__ logits, int64
 #ifndef DFS_TOPK_SMALL_BATCHED
 #define DFS_TOPK_SMALL_BATCHED 1
 #endif
+// The batched append walks each lane's set bits only (1) or every element slot (0):
+// 16 x 151936 16.4 -> 15.7 us per dfs_select.
+#ifndef DFS_TOPK_SMALL_BITLOOP
+#define DFS_TOPK_SMALL_BITLOOP 1
+#endif
 constexpr int kSmallVecs = DFS_TOPK_SMALL_VECS;
 
 template <bool kBf16>
@@ -558,9 +563,25 @@ __device__ __forceinline__ void topk_small_body(const void* __restrict__ logits,
       for (int u = 0; u < kSmallVecs; ++u) {
         if (__ballot(bits[u] != 0u) == 0) continue;
         const uint32_t base = (uint32_t)(vb + ((int64_t)u * kThreads + tid) * PV);
+#if DFS_TOPK_SMALL_BITLOOP
+        // only the lane's set bits, lowest first (the wave loops as often as its busiest lane)
+        for (uint32_t m = bits[u]; m != 0u; m &= m - 1u) {
+          const int e = __builtin_ctz(m);
+          float v;
+          if constexpr (kBf16) {
+            const int wi = e >> 1;
+            const uint32_t word = wi == 0 ? d[u].x : wi == 1 ? d[u].y : wi == 2 ? d[u].z : d[u].w;
+            v = (e & 1) ? bf16_hi(word) : bf16_lo(word);
+          } else {
+            v = __uint_as_float(e == 0 ? d[u].x : e == 1 ? d[u].y : e == 2 ? d[u].z : d[u].w);
+          }
+          buf[pos++] = make_key(v, base + (uint32_t)e);
+        }
+#else
 #pragma unroll
         for (int e = 0; e < PV; ++e)
           if ((bits[u] >> e) & 1u) buf[pos++] = make_key(elem(u, e), base + (uint32_t)e);
+#endif
       }
       w.cnt = uniform(w.cnt + tot);
       scanned = true;
