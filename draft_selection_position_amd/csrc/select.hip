@@ -47,6 +47,11 @@ constexpr int kMaxL = 16;
 #define DFS_TILE_GATHER_FIRST 1
 #endif
 // The same for the few-row kernel's wave 0 (1: 16 x 151936 16.9 -> 16.6 us per dfs_select).
+// fp32 tables, few-row kernel: a tile's 32 row loads of a lane in one round (1) or two (0):
+// 8 x 32000 fp32 15.5 -> 15.35 us per dfs_select.
+#ifndef DFS_F32_TILE_ONE_ROUND
+#define DFS_F32_TILE_ONE_ROUND 1
+#endif
 #ifndef DFS_POS_GATHER_FIRST
 #define DFS_POS_GATHER_FIRST 1
 #endif
@@ -338,7 +343,9 @@ __device__ __forceinline__ void score_tile_rows(const TileRows& tr, float u, flo
   for (int i = 0; i < 4; ++i) sc[i] = acc[i] + u;
 }
 
-template <bool kBf16Tables>
+// kOneRound (fp32 tables): every row piece of the lane in flight before the first product
+// (32 float4 registers: for kernels with the registers to spare).
+template <bool kBf16Tables, bool kOneRound = false>
 __device__ __forceinline__ void score_tile(const void* __restrict__ A_, const void* __restrict__ B_, int64_t pred,
                                            int64_t cand, float u, float4 gp, float* sGr, int lane, float (&sc)[4]) {
   const int q = lane >> 4;
@@ -357,16 +364,36 @@ __device__ __forceinline__ void score_tile(const void* __restrict__ A_, const vo
                                                        4 * q);
     const float4* Bp = reinterpret_cast<const float4*>(static_cast<const float*>(B_) + cand * kE +
                                                        4 * q);
-    *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
-    __builtin_amdgcn_wave_barrier();
+    if constexpr (kOneRound) {
+      float4 a[16], bb[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        a[c] = Ap[4 * c];
+        bb[c] = Bp[4 * c];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const float4 g = *reinterpret_cast<const float4*>(&sGr[16 * c + 4 * q]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].x * g.x, bb[c].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].y * g.y, bb[c].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].z * g.z, bb[c].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].w * g.w, bb[c].w, acc, 0, 0, 0);
+      }
+    } else {
+      *reinterpret_cast<float4*>(&sGr[4 * lane]) = gp;
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll 8
-    for (int c = 0; c < 16; ++c) {  // two rounds of 8 + 8 row loads in flight
-      const float4 a = Ap[4 * c], bb = Bp[4 * c];
-      const float4 g = *reinterpret_cast<const float4*>(&sGr[16 * c + 4 * q]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w * g.w, bb.w, acc, 0, 0, 0);
+      for (int c = 0; c < 16; ++c) {  // two rounds of 8 + 8 row loads in flight
+        const float4 a = Ap[4 * c], bb = Bp[4 * c];
+        const float4 g = *reinterpret_cast<const float4*>(&sGr[16 * c + 4 * q]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w * g.w, bb.w, acc, 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -615,7 +642,7 @@ __global__ __launch_bounds__(kPosThreads) void pair_pos_kernel(
     } else {
       const float4 gp = gate_finish(gate, gate_splits, gate_stride, row, lane, gr);
       __builtin_amdgcn_sched_barrier(0);
-      score_tile<kBf16Tables>(A_, B_, pred, cand, u, gp, sG, lane, sc);
+      score_tile<kBf16Tables, DFS_F32_TILE_ONE_ROUND>(A_, B_, pred, cand, u, gp, sG, lane, sc);
     }
     if (mode == 2 || out_q != nullptr) {
 #pragma unroll
