@@ -47,13 +47,13 @@ constexpr int kMaxL = 16;
 #define DFS_TILE_GATHER_FIRST 1
 #endif
 // The same for the few-row kernel's wave 0 (1: 16 x 151936 16.9 -> 16.6 us per dfs_select).
+#ifndef DFS_POS_GATHER_FIRST
+#define DFS_POS_GATHER_FIRST 1
+#endif
 // fp32 tables, few-row kernel: a tile's 32 row loads of a lane in one round (1) or two (0):
 // 8 x 32000 fp32 15.5 -> 15.35 us per dfs_select.
 #ifndef DFS_F32_TILE_ONE_ROUND
 #define DFS_F32_TILE_ONE_ROUND 1
-#endif
-#ifndef DFS_POS_GATHER_FIRST
-#define DFS_POS_GATHER_FIRST 1
 #endif
 
 // Standard Gumbel noise for (sequence b, position t, slot j), fp64:
