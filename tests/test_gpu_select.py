@@ -75,6 +75,11 @@ VARIANTS = [
     variant("small_batch", emb_std=0.3, batch=16, V=20000, d=64),
     # 600 rows, d = 16384: the LDS-DMA gate over 20 K splits, all added by the pair kernel
     variant("small_batch", emb_std=0.3, batch=40, L=15, V=20000, d=16384),
+    # either side of the batch size where the pair scores change path: up to 128 sequences a
+    # wave per position writes the pair tensor and a second launch walks it, beyond that one
+    # workgroup per sequence scores and walks
+    variant("sampled", emb_std=0.3, batch=128, V=4096, d=256, temperature=0.9, walk_seed=99),
+    variant("sampled", emb_std=0.3, batch=129, V=4096, d=256, temperature=0.9, walk_seed=99),
     # the best-total-path walk
     variant("tiny", emb_std=0.3, walk="viterbi"),
     variant("tiny", emb_std=0.3, L=1, walk="viterbi"),
@@ -101,7 +106,9 @@ def test_select_variants(cfg):
 @pytest.mark.parametrize("cfg", [variant("single_stream", emb_std=0.3, batch=5, V=20000, d=256),
                                  variant("small_batch", emb_std=0.3, batch=16, V=20000, d=256),
                                  variant("small_batch", emb_std=0.3, batch=16, V=20000, d=128),
-                                 variant("small_batch", emb_std=0.3, batch=16, V=20000, d=64)],
+                                 variant("small_batch", emb_std=0.3, batch=16, V=20000, d=64),
+                                 variant("throughput", emb_std=0.3, batch=128, V=4096, d=256),
+                                 variant("throughput", emb_std=0.3, batch=129, V=4096, d=256)],
                          ids=lambda c: f"{c.batch}x{c.L}x{c.V}_d{c.d}")
 def test_select_equals_step_chain(cfg):
     import draft_selection_position_amd as dfs
